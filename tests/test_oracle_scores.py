@@ -1,0 +1,138 @@
+"""Pins for the oracle's scores and top-k: hand-worked values, the full 4-bit
+dense dot product (B = 4d), the all-midpoint case (B = 0), agreement of the
+code form with the bit-plane form, reconstruction straight from the t-bit
+quantizer, and brute-force / library selection."""
+
+import numpy as np
+import pytest
+
+import oracle as O
+from sparse_kv_cache_amd import synth
+
+
+def test_hand_worked_one_channel(golden):
+    g = golden["one_channel"]
+    keys = np.array(g["keys"], np.float32)[:, None]
+    planes, lo, step, var, codes = O.pack_head(keys)
+    q = np.array(g["q"], np.float32)
+    for b, expect in g["scores_by_b"].items():
+        if b == "why":
+            continue
+        bb = np.array([int(b)])
+        assert O.scores_from_codes(codes, lo, step, q, bb).tolist() == expect
+        assert O.scores_from_planes(planes, 5, lo, step, q, bb).tolist() == expect
+    s2 = O.scores_from_codes(codes, lo, step, q, np.array([2]))
+    assert O.topk(s2, 2)[0].tolist() == g["topk"]["b2_k2"]
+    assert O.topk(s2, 3)[0].tolist() == g["topk"]["b2_k3"]
+    s0 = O.scores_from_codes(codes, lo, step, q, np.array([0]))
+    assert O.topk(s0, 2)[0].tolist() == g["topk"]["b0_k2"]
+    s1 = O.scores_from_codes(codes, lo, step, q, np.array([1]))
+    assert O.topk(s1, 4)[0].tolist() == g["topk"]["b1_k4"]
+
+
+def test_hand_worked_two_channels(golden):
+    g = golden["two_channels"]
+    keys = np.array(g["keys"], np.float32)
+    planes, lo, step, var, codes = O.pack_head(keys)
+    q = np.array(g["q"], np.float32)
+    b = O.allocate(q, var, 3)
+    s = O.scores_from_codes(codes, lo, step, q, b)
+    assert s.tolist() == g["scores_b30"]["value"]
+    assert O.topk(s, 2)[0].tolist() == g["scores_b30"]["top2"]
+    assert O.scores_from_planes(planes, 4, lo, step, q, b).tolist() == g["scores_b30"]["value"]
+
+
+@pytest.fixture(scope="module")
+def head():
+    keys, q = synth.make_inputs(4, 1, 3000, 6)
+    return keys[0], q
+
+
+def test_full_budget_is_dense_4bit_dot(head):
+    keys, qs = head
+    _, lo, step, var, codes = O.pack_head(keys)
+    recon = lo.astype(np.float64)[None, :] + (codes + 0.5) * step.astype(np.float64)[None, :]
+    for q in qs:
+        b = O.allocate(q, var, 512)
+        s = O.scores_from_codes(codes, lo, step, q, b)
+        dense = np.dot(recon, q.astype(np.float64))
+        assert np.allclose(s, dense, rtol=1e-12, atol=1e-12)
+
+
+def test_zero_budget_is_midpoint(head):
+    keys, qs = head
+    _, lo, step, var, codes = O.pack_head(keys)
+    lo_, hi_ = O.key_range(keys)
+    r32 = (hi_ - lo_).astype(np.float32)       # the range as the fp32 quantizer holds it
+    mid = lo_.astype(np.float64) + r32.astype(np.float64) / 2
+    true_mid = (lo_.astype(np.float64) + hi_.astype(np.float64)) / 2
+    for q in qs:
+        b = O.allocate(q, var, 0)
+        s = O.scores_from_codes(codes, lo, step, q, b)
+        assert np.allclose(s, np.dot(mid, q.astype(np.float64)), rtol=1e-12)
+        assert np.allclose(s, np.dot(true_mid, q.astype(np.float64)), rtol=1e-5)
+        assert np.all(s == s[0])
+        assert O.topk(s, 10)[0].tolist() == list(range(10))
+
+
+@pytest.mark.parametrize("B", [1, 5, 68, 92, 136, 300, 512])
+def test_code_form_equals_plane_form(head, B):
+    keys, qs = head
+    planes, lo, step, var, codes = O.pack_head(keys)
+    for q in qs[:3]:
+        b = O.allocate(q, var, B)
+        a = O.scores_from_codes(codes, lo, step, q, b)
+        p = O.scores_from_planes(planes, keys.shape[0], lo, step, q, b)
+        scale = np.abs(a).max()
+        assert np.max(np.abs(a - p)) <= 1e-12 * scale
+
+
+@pytest.mark.parametrize("B", [7, 92, 200])
+def test_scores_from_direct_tbit_quantizer(head, B):
+    """Reconstructing each channel from its own b_c-bit floor quantizer of
+    the raw keys (bin width r / 2^b_c) gives the same scores."""
+    keys, qs = head
+    _, lo, step, var, codes = O.pack_head(keys)
+    lo_, hi_ = O.key_range(keys)
+    r = (hi_ - lo_).astype(np.float32)
+    for q in qs[:2]:
+        b = O.allocate(q, var, B)
+        khat = np.empty(keys.shape, np.float64)
+        for c in range(keys.shape[1]):
+            t = int(b[c])
+            inv_t = np.float32(2 ** t) / r[c] if r[c] > 0 else np.float32(0)
+            u = ((keys[:, c] - lo_[c]).astype(np.float32) * inv_t).astype(np.float32)
+            code_t = np.minimum(np.floor(u), 2 ** t - 1).astype(np.float64)
+            khat[:, c] = float(lo_[c]) + (code_t + 0.5) * float(r[c]) / 2 ** t
+        ref = khat @ q.astype(np.float64)
+        s = O.scores_from_codes(codes, lo, step, q, b)
+        assert np.allclose(s, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+
+
+def test_topk_brute_force_and_library():
+    rng = np.random.default_rng(8)
+    for n, k in ((50, 7), (300, 300), (1000, 64)):
+        s = np.round(rng.standard_normal(n) * 4) / 4   # many exact ties
+        idx, val = O.topk(s, k)
+        brute = sorted(range(n), key=lambda i: (-s[i], i))[:k]
+        assert idx.tolist() == brute
+        assert np.array_equal(val, s[brute].astype(np.float32))
+    s = rng.standard_normal(5000)                      # no ties: same set as argpartition
+    idx, _ = O.topk(s, 100)
+    assert set(idx.tolist()) == set(np.argpartition(-s, 100)[:100].tolist())
+    with pytest.raises(ValueError):
+        O.topk(s, 0)
+    with pytest.raises(ValueError):
+        O.topk(s, 5001)
+
+
+def test_decode_step_gqa_mapping():
+    keys, q = synth.make_inputs(0, 2, 700, 4)
+    res = O.decode_step(keys, q, 2, 40, 16)
+    for i in range(4):
+        h = i // 2
+        b = O.allocate(q[i], res["var"][h], 40)
+        assert np.array_equal(res["alloc"][i], b)
+        s = O.scores_from_codes(res["codes"][h], res["lo"][h], res["step"][h], q[i], b)
+        assert np.array_equal(res["scores"][i], s)
+        assert res["alloc"][i].sum() == 40
