@@ -1,0 +1,241 @@
+"""Benchmark of the Fathom decode-step hot path on one MI355X.
+
+One step = per-query allocation (fathom_allocate) + plane-prefix scan with
+fused top-k (fathom_scan_topk) over every KV head of the workload, inputs
+resident in HBM.  The default workload is the 1M-token Qwen3-8B-shaped decode
+step: 8 KV heads x 1,048,576 keys x 128 channels, 32 query heads (GQA 4),
+budget B = 92 bits, k = 2048.  Synthetic seeded keys (no model weights are
+available).  Several copies of the plane store are rotated so that
+consecutive steps never find their planes in the 256 MB Infinity Cache.
+
+Prints one JSON line (see the repository's design notes for the fields).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Gkeys/s and achieved HBM GB/s (% peak) for scan+top-k, 1M keys, B=92 bits"
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_main_qwen3_8b_1m_traffic.json")
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for f in ("scan.hip", "fathom_internal.h"):
+        with open(os.path.join(ROOT, "sparse_kv_cache_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def union_bytes(alloc: np.ndarray, group: int, ldw: int) -> int:
+    """Plane bytes a step must read: per KV head, per channel, the longest
+    prefix any of its queries reads (the union), times the row length."""
+    Q, d = alloc.shape
+    u = alloc.reshape(Q // group, group, d).max(axis=1).astype(np.int64)
+    return int(u.sum()) * ldw * 4
+
+
+def cpu_baseline(w, budget, target_s):
+    """Time the oracle (allocate + code-form scores + full-sort top-k) on one
+    KV head's GQA group over a bounded key sample, single-threaded."""
+    import threadpoolctl
+    import oracle as O
+    from sparse_kv_cache_amd import synth
+
+    rng = np.random.default_rng(w.seed)
+    keys = synth.head_keys(rng, w.n, w.d)
+    _, lo, step, var, codes = O.pack_head(keys)
+    del keys
+    # the queries of head 0 (same draws the GPU run uses come after all
+    # heads; the baseline only needs queries of the right distribution)
+    q = np.random.default_rng(w.seed + 1000).standard_normal((w.group, w.d)).astype(np.float32)
+    n_s = min(w.n, 1 << 16)
+    done_keys, elapsed = 0, 0.0
+    with threadpoolctl.threadpool_limits(1):
+        while elapsed < target_s:
+            start = (done_keys % w.n)
+            sl = slice(start, min(start + n_s, w.n))
+            t0 = time.perf_counter()
+            for g in range(w.group):
+                b = O.allocate(q[g], var, budget)
+                s = O.scores_from_codes(codes[sl], lo, step, q[g], b)
+                O.topk(s, min(w.k, s.shape[0]))
+            elapsed += time.perf_counter() - t0
+            done_keys += sl.stop - sl.start
+    return {
+        "value": done_keys / elapsed / 1e9,
+        "unit": "Gkeys/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"KV head 0 of the workload, {done_keys} keys scored for its {w.group} query heads "
+                  f"(allocate + float64 code-form scores + full-sort top-k, k={w.k}) in slices of "
+                  f"{n_s} keys, {elapsed:.1f} s, NumPy single thread",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qwen3_8b_1m")
+    ap.add_argument("--budget", type=int, default=None)
+    ap.add_argument("--copies", type=int, default=3, help="plane-store copies rotated across steps")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="also run a plain device copy of this size (for counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the plane store shards by KV head or session with no exchange; see the design notes)",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    from sparse_kv_cache_amd import fathom as fa
+    from sparse_kv_cache_amd import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    w = synth.WORKLOADS[args.workload]
+    budget = args.budget if args.budget is not None else w.budgets[0]
+    H, n, d, G, Q, k = w.num_kv_heads, w.n, w.d, w.group, w.num_q, w.k
+    store = fa.store_desc(H, n, d)
+    log(f"workload {w.name}: H={H} n={n} d={d} Q={Q} G={G} B={budget} k={k}")
+
+    # ---- inputs: keys -> device -> packed planes (pack timed once, for the record)
+    t0 = time.perf_counter()
+    keys = torch.empty((H, n, d), dtype=torch.float32, device=dev)
+    q_np = None
+    for kind, *rest in synth.stream_inputs(w.seed, H, n, Q, d):
+        if kind == "head":
+            h, kh = rest
+            keys[h].copy_(torch.from_numpy(kh))
+        else:
+            q_np = rest[0]
+    torch.cuda.synchronize()
+    log(f"generated keys in {time.perf_counter() - t0:.1f} s")
+    planes0 = torch.empty((H, d, 4, store.ldw), dtype=torch.int32, device=dev)
+    pack_ws = fa.alloc_workspace(fa.workspace_bytes(fa.FATHOM_OP_PACK, store), dev)
+    fa.pack_planes(keys, store, planes=planes0, workspace=pack_ws)   # warm
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    _, lo, step, var = fa.pack_planes(keys, store, planes=planes0, workspace=pack_ws)
+    e1.record()
+    torch.cuda.synchronize()
+    pack_ms = e0.elapsed_time(e1)
+    del keys
+    torch.cuda.empty_cache()
+    copies = [planes0] + [planes0.clone() for _ in range(max(1, args.copies) - 1)]
+    qd = torch.from_numpy(q_np).to(dev)
+    alloc = torch.empty((Q, d), dtype=torch.uint8, device=dev)
+    out_idx = torch.empty((Q, k), dtype=torch.int32, device=dev)
+    out_score = torch.empty((Q, k), dtype=torch.float32, device=dev)
+    scan_ws = fa.alloc_workspace(fa.workspace_bytes(fa.FATHOM_OP_SCAN, store, Q, k), dev)
+
+    def step_fn(i):
+        fa.allocate(qd, var, G, budget, store, out=alloc)
+        fa.scan_topk(copies[i % len(copies)], lo, step, store, qd, alloc, G, k, workspace=scan_ws,
+                     out_idx=out_idx, out_score=out_score)
+
+    for i in range(args.warmup):
+        step_fn(i)
+    torch.cuda.synchronize()
+    alg_plane_bytes = union_bytes(alloc.cpu().numpy(), G, store.ldw)
+    alg_bytes = alg_plane_bytes + H * d * 8 + Q * d * 5 + Q * k * 8
+
+    if args.calibrate_copy_mib:
+        nel = args.calibrate_copy_mib * (1 << 20) // 4
+        src = torch.ones(nel, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy: {args.calibrate_copy_mib} MiB read + written per launch, 3 launches")
+
+    fa.timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step_fn(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    main_ms_total, launches = fa.timing_read()
+    fa.timing_enable(False)
+
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    main_ms = main_ms_total / max(launches, 1)
+    gkeys = H * n / (ms_per_step * 1e-3) / 1e9
+    achieved = alg_bytes / (main_ms * 1e-3) / 1e9
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("source_digest") == source_digest() and tr.get("budget") == budget:
+            traffic = tr.get("bytes_per_launch")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle ...")
+        cpu = cpu_baseline(w, budget, args.cpu_seconds)
+
+    rec = {
+        "metric": METRIC,
+        "value": round(gkeys, 3),
+        "unit": "Gkeys/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "kv_heads": H, "keys_per_head": n, "d": d, "query_heads": Q,
+            "gqa_group": G, "budget_bits": budget, "k": k, "store_copies": len(copies),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+        },
+        "cpu_baseline": cpu,
+        "gscores_per_s": round(Q * n / (ms_per_step * 1e-3) / 1e9, 3),
+        "alg_bytes_per_step": alg_bytes,
+        "union_bits_per_key": round(alg_plane_bytes * 8 / (H * store.ldw * 32), 2),
+        "main_kernel_ms": round(main_ms, 4),
+        "step_gbs": round(alg_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "pack_ms": round(pack_ms, 3),
+        "kernel_source": source_digest(),
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,150 @@
+/*
+ * fathom.h -- C ABI of libfathom, a gfx950 (MI355X) implementation of the
+ * Fathom per-query variable-read-depth key scan over a bit-plane 4-bit K cache.
+ *
+ * Method pages:
+ *   [Art] "Fathom Makes KV-Cache Scans Query-Adaptive for Long-Context
+ *         Decoding" (paragraphs 1-3 and the limits paragraph);
+ *   [Abs] "Fathom: Per-Query Read Depth for Sparse Decoding over Offloaded
+ *         KV Caches", abstract sentences s1-s6.
+ * The pages state no programming interface; the arguments below follow their
+ * statement of the problem (a K cache, a query, a bit budget B, a top-k k)
+ * plus layout descriptors.
+ *
+ * Conventions shared by every entry point
+ *   - Ownership: the caller owns every buffer.  The library allocates nothing
+ *     inside fathom_pack_planes, fathom_allocate or fathom_scan_topk; scratch
+ *     memory comes in through `workspace`, sized by fathom_workspace_bytes.
+ *   - Pointers are device pointers (HBM), except `planes` in fathom_scan_topk,
+ *     which may also be the device view of pinned host memory obtained from
+ *     fathom_host_device_pointer (zero-copy reads over PCIe).
+ *   - Asynchrony: work is enqueued on `hip_stream` (a hipStream_t passed as
+ *     void*, NULL = the legacy default stream).  Outputs are valid once the
+ *     stream has been synchronized.
+ *   - Validation happens on the host before any HIP call.  On error nothing
+ *     is launched, outputs are untouched, a negative status is returned and
+ *     fathom_last_error() describes the problem.  No C++ exception crosses
+ *     this boundary.
+ *   - Layout of the plane store ("channel-major bit planes", [Art] para 2,
+ *     [Abs] s3): planes[h][c][j][w], uint32, j = 0 is the most significant
+ *     bit of the 4-bit code; word w of a row holds keys 32w..32w+31 with key
+ *     32w+b at bit b; rows are `ldw` words long (ldw % 4 == 0) and bits of
+ *     keys >= n are zero.  A t-plane prefix of channel c is the contiguous
+ *     run planes[h][c][0..t-1][*].
+ *   - Query head q reads KV head q / group; num_q must equal H * group
+ *     (grouped-query attention; sessions are flattened into H).
+ *   - Supported: d = 128 channels, 1 <= n <= 2^26 keys per head.  Keys and
+ *     queries must be finite.
+ */
+#ifndef FATHOM_H
+#define FATHOM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every int-returning entry point. */
+enum {
+  FATHOM_OK = 0,
+  FATHOM_ERR_INVALID_ARG = -1,  /* null/misaligned pointer, bad size or range */
+  FATHOM_ERR_UNSUPPORTED = -2,  /* valid but not implemented (d != 128, ...)  */
+  FATHOM_ERR_WORKSPACE = -3,    /* workspace missing, misaligned or too small */
+  FATHOM_ERR_HIP = -4           /* a HIP runtime call or launch failed        */
+};
+
+/* Operation selector for fathom_workspace_bytes. */
+enum { FATHOM_OP_PACK = 0, FATHOM_OP_SCAN = 1 };
+
+/* Largest k accepted by fathom_scan_topk. */
+#define FATHOM_MAX_K 4096
+
+/* Shape of a plane store: H KV heads, d channels, n keys per head, ldw words
+ * per plane row.  Passed by pointer; the library does not keep it. */
+typedef struct fathom_store_desc {
+  int32_t num_kv_heads;
+  int32_t d;
+  int64_t n;
+  int64_t ldw;
+} fathom_store_desc;
+
+/* Words per plane row for n keys: ceil(n / 32) rounded up to a multiple of 4
+ * (16-byte rows).  Returns -1 when n < 1. */
+int64_t fathom_plane_ldw(int64_t n);
+
+/* Bytes of device workspace needed by an operation (FATHOM_OP_PACK: num_q and
+ * k are ignored; FATHOM_OP_SCAN: the scan + top-k of num_q queries).  Returns
+ * 0 for an invalid description.  The workspace pointer must be 256-byte
+ * aligned. */
+size_t fathom_workspace_bytes(int32_t op, const fathom_store_desc* store, int32_t num_q, int32_t k);
+
+/* Quantize-and-transpose packer ([Art] para 2; [Abs] s3, s6).
+ * keys: float32, key i of head h at keys[h*stride_head + i*stride_token + c]
+ *   (channel stride 1; 16-byte aligned base, stride_token % 4 == 0).
+ * Per (head, channel) asymmetric 4-bit floor quantizer over the head's n keys:
+ *   lo = min K, r = fl32(max K - lo), step = r/16, inv = fl32(16/r) (0 if r=0),
+ *   code = min(15, floor(fl32(fl32(K - lo) * inv))).
+ * Writes planes [H][d][4][ldw] (all words, padding bits zero), lo [H][d],
+ * step [H][d], and, if var != NULL, var [H][d] = variance of the 4-bit
+ * reconstructions lo + (code + 1/2) step from exact integer moments:
+ *   fl32( fl64(S2 n - S1^2) / fl64(n^2) * fl64(step)^2 ).
+ * The result is bit-exact and independent of launch order.
+ * workspace: >= fathom_workspace_bytes(FATHOM_OP_PACK, ...) bytes. */
+int fathom_pack_planes(const float* keys, int64_t stride_head, int64_t stride_token,
+                       const fathom_store_desc* store, uint32_t* planes, float* lo, float* step,
+                       float* var, void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* Per-query bit allocation by reverse water-filling ([Art] para 3; [Abs] s2,
+ * s3).  q: float32 [num_q][d]; var: float32 [H][d] (any calibrated channel
+ * variance, e.g. the packer's); budget_bits B in [0, 4d].
+ * w_c = fl32(fl32(q_c^2) var_c); candidate (c, j) has the int32 ordering key
+ * bits(w_c) - j*2^24 (the order of w_c 4^-j); the B best candidates by
+ * (key desc, c asc, j asc) are taken and alloc[q][c] = number taken from c.
+ * Output alloc: uint8 [num_q][d], every row sums to B, entries in 0..4. */
+int fathom_allocate(const float* q, int32_t num_q, int32_t group, const float* var,
+                    const fathom_store_desc* store, int32_t budget_bits, uint8_t* alloc,
+                    void* hip_stream);
+
+/* Plane-prefix scan with fused top-k ([Art] paras 1-2; [Abs] s1-s3).
+ * For every query q (KV head h = q / group) and key i < n:
+ *   s_q(i) = C_q + sum_c sum_{j < b_qc} q_c step_c 2^(3-j) bit_{c,j}(i),
+ *   C_q = sum_c q_c (lo_c + step_c 2^(3-b_qc)),
+ * which is the dot product of q with the keys dequantized from their b_qc-bit
+ * prefixes at the bin centres.  Only the planes j < max over the group of
+ * b_qc are read.  Outputs, per query, the k best keys by (score desc,
+ * index asc): out_idx int32 [num_q][k], out_score float32 [num_q][k].
+ * all_scores: NULL, or float32 [num_q][n] receiving every score (a debug and
+ * parity aid; costs n*4 bytes of writes per query).
+ * alloc values above 4 are read as 4.  Scores are accumulated in fp32.
+ * workspace: >= fathom_workspace_bytes(FATHOM_OP_SCAN, store, num_q, k). */
+int fathom_scan_topk(const uint32_t* planes, const float* lo, const float* step,
+                     const fathom_store_desc* store, const float* q, const uint8_t* alloc,
+                     int32_t num_q, int32_t group, int32_t k, int32_t* out_idx, float* out_score,
+                     float* all_scores, void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* Device-visible address of pinned host memory (allocated with hipHostMalloc
+ * or torch pin_memory), for a plane store kept in host RAM ([Art] para 1;
+ * [Abs] s1: the index lives in host memory).  Not for registered memory. */
+int fathom_host_device_pointer(void* pinned_host, void** device_ptr);
+
+/* Static text for a status code. */
+const char* fathom_status_string(int32_t status);
+
+/* Detail of the last error on the calling thread ("" if none). */
+const char* fathom_last_error(void);
+
+/* Kernel timing for measurement: when enabled, the library records HIP
+ * events around the main scan kernel of each fathom_scan_topk call on the
+ * call's stream.  fathom_timing_read synchronizes on those events and
+ * returns the summed kernel time (ms) and the number of timed launches since
+ * the last read, then clears the record.  At most 4096 launches are kept. */
+int fathom_timing_enable(int32_t enable);
+int fathom_timing_read(double* total_ms, int32_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FATHOM_H */

@@ -1,0 +1,71 @@
+"""Build libfathom.so for gfx950 with hipcc, in-tree.
+
+Usage: python -m sparse_kv_cache_amd.build   (or call ``build()``)
+Each translation unit is compiled to an object in parallel, then linked.
+"""
+
+from __future__ import annotations
+
+import concurrent.futures
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+OBJ = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libfathom.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+SOURCES = ["pack.hip", "allocate.hip", "scan.hip", "fathom_api.hip"]
+
+COMMON = [
+    "--offload-arch=gfx950",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-fno-gpu-rdc",
+    "-Wall",
+    "-Wno-unused-result",
+    # packed fp32 ops stay off: ordinary float code only
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", os.path.join(ROOT, "include"),
+    "-I", CSRC,
+]
+# bit-exact translation units: no contraction of separate multiplies and adds
+EXACT = {"pack.hip": ["-ffp-contract=off"], "allocate.hip": ["-ffp-contract=off"]}
+
+
+def _compile(src: str) -> str:
+    out = os.path.join(OBJ, src.replace(".hip", ".o"))
+    cmd = [HIPCC, *COMMON, *EXACT.get(src, []), "-c", os.path.join(CSRC, src), "-o", out]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+    if res.stderr.strip():
+        # keep warnings visible but short (the host pass warns about the
+        # packed-fp32 feature it does not know)
+        lines = [l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l and l.strip()]
+        if lines:
+            print("\n".join(lines[:40]), file=sys.stderr)
+    return out
+
+
+def build(verbose: bool = True) -> str:
+    os.makedirs(OBJ, exist_ok=True)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        objs = list(ex.map(_compile, SOURCES))
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"built {LIB}")
+    return LIB
+
+
+if __name__ == "__main__":
+    build()

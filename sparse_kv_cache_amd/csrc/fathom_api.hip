@@ -1,0 +1,265 @@
+// libfathom C ABI: argument validation, workspace carving, kernel launches.
+// The declarations, with argument meaning, layout, ownership and error
+// behaviour, are in include/fathom.h.  Every check below runs on the host
+// before any HIP call, so an invalid call launches nothing.
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "fathom.h"
+#include "fathom_internal.h"
+
+using namespace fathom;
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_last_error[0] = '\0';
+  return FATHOM_OK;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+  return fail(FATHOM_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int check_store(const fathom_store_desc* s) {
+  if (!s) return fail(FATHOM_ERR_INVALID_ARG, "store descriptor is NULL");
+  if (s->num_kv_heads < 1) return fail(FATHOM_ERR_INVALID_ARG, "num_kv_heads must be >= 1");
+  if (s->d != kD) return fail(FATHOM_ERR_UNSUPPORTED, "d = %d: only d = %d is supported", s->d, kD);
+  if (s->n < 1) return fail(FATHOM_ERR_INVALID_ARG, "n must be >= 1");
+  if (s->n > kMaxKeys)
+    return fail(FATHOM_ERR_UNSUPPORTED, "n = %lld exceeds the supported %lld keys per head",
+                static_cast<long long>(s->n), static_cast<long long>(kMaxKeys));
+  const int64_t words = (s->n + 31) / 32;
+  if (s->ldw < words || s->ldw % 4 != 0)
+    return fail(FATHOM_ERR_INVALID_ARG, "ldw = %lld must be >= ceil(n/32) = %lld and a multiple of 4",
+                static_cast<long long>(s->ldw), static_cast<long long>(words));
+  if (static_cast<int64_t>(s->num_kv_heads) * kD * kPlanes * s->ldw > (int64_t(1) << 40))
+    return fail(FATHOM_ERR_UNSUPPORTED, "plane store larger than 4 TiB");
+  return FATHOM_OK;
+}
+
+// Workspace layouts (every section 256-byte aligned).
+struct PackLayout {
+  size_t kmin, kmax, s1, s2, total;
+};
+PackLayout pack_layout(int H) {
+  const size_t cnt = static_cast<size_t>(H) * kD;
+  PackLayout L{};
+  size_t off = 0;
+  L.kmin = off; off = round_up(off + cnt * 4, 256);
+  L.kmax = off; off = round_up(off + cnt * 4, 256);
+  L.s1 = off;   off = round_up(off + cnt * 8, 256);
+  L.s2 = off;   off = round_up(off + cnt * 8, 256);
+  L.total = off;
+  return L;
+}
+
+struct ScanLayout {
+  size_t theta, count, sample, cand, total;
+};
+ScanLayout scan_layout(int num_q) {
+  const size_t Q = static_cast<size_t>(num_q);
+  ScanLayout L{};
+  size_t off = 0;
+  L.theta = off;  off = round_up(off + Q * 4, 256);
+  L.count = off;  off = round_up(off + Q * 4, 256);
+  L.sample = off; off = round_up(off + Q * kSampleMaxKeys * 4, 256);
+  L.cand = off;   off = round_up(off + Q * kCandCap * 8, 256);
+  L.total = off;
+  return L;
+}
+
+// kernel timing record
+std::mutex g_timing_mu;
+bool g_timing_on = false;
+std::vector<std::pair<hipEvent_t, hipEvent_t>> g_events;   // created on enable
+size_t g_events_used = 0;
+constexpr size_t kMaxTimed = 4096;
+
+}  // namespace
+
+extern "C" {
+
+int64_t fathom_plane_ldw(int64_t n) {
+  if (n < 1) return -1;
+  const int64_t words = (n + 31) / 32;
+  return (words + 3) / 4 * 4;
+}
+
+size_t fathom_workspace_bytes(int32_t op, const fathom_store_desc* store, int32_t num_q, int32_t k) {
+  if (check_store(store) != FATHOM_OK) return 0;
+  if (op == FATHOM_OP_PACK) return pack_layout(store->num_kv_heads).total;
+  if (op == FATHOM_OP_SCAN) {
+    if (num_q < 1 || k < 1) return 0;
+    return scan_layout(num_q).total;
+  }
+  return 0;
+}
+
+int fathom_pack_planes(const float* keys, int64_t stride_head, int64_t stride_token,
+                       const fathom_store_desc* store, uint32_t* planes, float* lo, float* step,
+                       float* var, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  int st = check_store(store);
+  if (st != FATHOM_OK) return st;
+  if (!keys || !planes || !lo || !step) return fail(FATHOM_ERR_INVALID_ARG, "keys, planes, lo and step must be non-NULL");
+  if (!aligned(keys, 16)) return fail(FATHOM_ERR_INVALID_ARG, "keys must be 16-byte aligned");
+  if (stride_token < kD || stride_token % 4 != 0)
+    return fail(FATHOM_ERR_INVALID_ARG, "stride_token must be >= d and a multiple of 4");
+  if (store->num_kv_heads > 1 && (stride_head < store->n * stride_token || stride_head % 4 != 0))
+    return fail(FATHOM_ERR_INVALID_ARG, "stride_head must be >= n * stride_token and a multiple of 4");
+  if (!aligned(planes, 16)) return fail(FATHOM_ERR_INVALID_ARG, "planes must be 16-byte aligned");
+  if (!aligned(lo, 4) || !aligned(step, 4) || (var && !aligned(var, 4)))
+    return fail(FATHOM_ERR_INVALID_ARG, "lo, step and var must be 4-byte aligned");
+  const PackLayout L = pack_layout(store->num_kv_heads);
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < L.total)
+    return fail(FATHOM_ERR_WORKSPACE, "pack needs a 256-byte aligned workspace of %zu bytes (got %zu)",
+                L.total, workspace_bytes);
+  char* w = static_cast<char*>(workspace);
+  PackWorkspace ws{reinterpret_cast<uint32_t*>(w + L.kmin), reinterpret_cast<uint32_t*>(w + L.kmax),
+                   reinterpret_cast<unsigned long long*>(w + L.s1),
+                   reinterpret_cast<unsigned long long*>(w + L.s2)};
+  hipError_t e = launch_pack(keys, store->num_kv_heads > 1 ? stride_head : 0, stride_token,
+                             store->num_kv_heads, store->n, store->ldw, planes, lo, step, var, ws,
+                             static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return hip_fail(e, "fathom_pack_planes launch");
+  return ok();
+}
+
+int fathom_allocate(const float* q, int32_t num_q, int32_t group, const float* var,
+                    const fathom_store_desc* store, int32_t budget_bits, uint8_t* alloc,
+                    void* hip_stream) {
+  int st = check_store(store);
+  if (st != FATHOM_OK) return st;
+  if (!q || !var || !alloc) return fail(FATHOM_ERR_INVALID_ARG, "q, var and alloc must be non-NULL");
+  if (num_q < 1 || group < 1) return fail(FATHOM_ERR_INVALID_ARG, "num_q and group must be >= 1");
+  if (static_cast<int64_t>(store->num_kv_heads) * group != num_q)
+    return fail(FATHOM_ERR_INVALID_ARG, "num_q = %d must equal num_kv_heads (%d) * group (%d)", num_q,
+                store->num_kv_heads, group);
+  if (budget_bits < 0 || budget_bits > kPlanes * kD)
+    return fail(FATHOM_ERR_INVALID_ARG, "budget_bits = %d outside [0, %d]", budget_bits, kPlanes * kD);
+  if (!aligned(q, 8) || !aligned(var, 8) || !aligned(alloc, 2))
+    return fail(FATHOM_ERR_INVALID_ARG, "q and var must be 8-byte aligned, alloc 2-byte aligned");
+  hipError_t e = launch_allocate(q, num_q, group, var, budget_bits, alloc, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return hip_fail(e, "fathom_allocate launch");
+  return ok();
+}
+
+int fathom_scan_topk(const uint32_t* planes, const float* lo, const float* step,
+                     const fathom_store_desc* store, const float* q, const uint8_t* alloc,
+                     int32_t num_q, int32_t group, int32_t k, int32_t* out_idx, float* out_score,
+                     float* all_scores, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  int st = check_store(store);
+  if (st != FATHOM_OK) return st;
+  if (!planes || !lo || !step || !q || !alloc || !out_idx || !out_score)
+    return fail(FATHOM_ERR_INVALID_ARG, "planes, lo, step, q, alloc, out_idx and out_score must be non-NULL");
+  if (num_q < 1 || group < 1) return fail(FATHOM_ERR_INVALID_ARG, "num_q and group must be >= 1");
+  if (static_cast<int64_t>(store->num_kv_heads) * group != num_q)
+    return fail(FATHOM_ERR_INVALID_ARG, "num_q = %d must equal num_kv_heads (%d) * group (%d)", num_q,
+                store->num_kv_heads, group);
+  if (k < 1 || k > store->n) return fail(FATHOM_ERR_INVALID_ARG, "k = %d outside [1, n]", k);
+  if (k > FATHOM_MAX_K) return fail(FATHOM_ERR_UNSUPPORTED, "k = %d exceeds FATHOM_MAX_K (%d)", k, FATHOM_MAX_K);
+  if (!aligned(planes, 16)) return fail(FATHOM_ERR_INVALID_ARG, "planes must be 16-byte aligned");
+  if (!aligned(lo, 4) || !aligned(step, 4) || !aligned(q, 4) || !aligned(out_idx, 4) ||
+      !aligned(out_score, 4) || (all_scores && !aligned(all_scores, 4)))
+    return fail(FATHOM_ERR_INVALID_ARG, "float and int32 arrays must be 4-byte aligned");
+  const ScanLayout L = scan_layout(num_q);
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < L.total)
+    return fail(FATHOM_ERR_WORKSPACE, "scan needs a 256-byte aligned workspace of %zu bytes (got %zu)",
+                L.total, workspace_bytes);
+  char* w = static_cast<char*>(workspace);
+  ScanWorkspace ws{reinterpret_cast<float*>(w + L.theta), reinterpret_cast<uint32_t*>(w + L.count),
+                   reinterpret_cast<float*>(w + L.sample), reinterpret_cast<uint2*>(w + L.cand)};
+
+  ScanTiming timing;
+  bool timed = false;
+  {
+    std::lock_guard<std::mutex> lock(g_timing_mu);
+    if (g_timing_on && g_events_used < g_events.size()) {
+      timing.start = g_events[g_events_used].first;
+      timing.stop = g_events[g_events_used].second;
+      ++g_events_used;
+      timed = true;
+    }
+  }
+  hipError_t e = launch_scan_topk(planes, lo, step, store->num_kv_heads, store->n, store->ldw, q, alloc,
+                                  num_q, group, k, out_idx, out_score, all_scores, ws,
+                                  timed ? &timing : nullptr, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return hip_fail(e, "fathom_scan_topk launch");
+  return ok();
+}
+
+int fathom_host_device_pointer(void* pinned_host, void** device_ptr) {
+  if (!pinned_host || !device_ptr) return fail(FATHOM_ERR_INVALID_ARG, "pointers must be non-NULL");
+  hipError_t e = hipHostGetDevicePointer(device_ptr, pinned_host, 0);
+  if (e != hipSuccess) return hip_fail(e, "hipHostGetDevicePointer");
+  return ok();
+}
+
+const char* fathom_status_string(int32_t status) {
+  switch (status) {
+    case FATHOM_OK: return "ok";
+    case FATHOM_ERR_INVALID_ARG: return "invalid argument";
+    case FATHOM_ERR_UNSUPPORTED: return "unsupported";
+    case FATHOM_ERR_WORKSPACE: return "workspace missing or too small";
+    case FATHOM_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* fathom_last_error(void) { return g_last_error; }
+
+int fathom_timing_enable(int32_t enable) {
+  std::lock_guard<std::mutex> lock(g_timing_mu);
+  if (enable && g_events.empty()) {
+    g_events.reserve(kMaxTimed);
+    for (size_t i = 0; i < kMaxTimed; ++i) {
+      hipEvent_t a = nullptr, b = nullptr;
+      hipError_t e = hipEventCreate(&a);
+      if (e == hipSuccess) e = hipEventCreate(&b);
+      if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+      g_events.emplace_back(a, b);
+    }
+  }
+  g_timing_on = enable != 0;
+  g_events_used = 0;
+  return ok();
+}
+
+int fathom_timing_read(double* total_ms, int32_t* launches) {
+  if (!total_ms || !launches) return fail(FATHOM_ERR_INVALID_ARG, "outputs must be non-NULL");
+  std::lock_guard<std::mutex> lock(g_timing_mu);
+  double sum = 0.0;
+  for (size_t i = 0; i < g_events_used; ++i) {
+    hipError_t e = hipEventSynchronize(g_events[i].second);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    float ms = 0.0f;
+    e = hipEventElapsedTime(&ms, g_events[i].first, g_events[i].second);
+    if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+    sum += ms;
+  }
+  *total_ms = sum;
+  *launches = static_cast<int32_t>(g_events_used);
+  g_events_used = 0;
+  return ok();
+}
+
+}  // extern "C"

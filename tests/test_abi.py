@@ -1,0 +1,121 @@
+"""Host-side checks of the C ABI: the library loads, exports every function
+include/fathom.h declares, sizes workspaces, and rejects invalid arguments
+on the host before any HIP call (so these run without a GPU; every call
+here is built to fail validation and launches nothing)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fathom.h")
+
+fa = pytest.importorskip("sparse_kv_cache_amd.fathom", reason="libfathom.so not built")
+lib = fa.lib
+SD = fa.StoreDesc
+FAKE = ctypes.c_void_p(0x1000)        # 256-aligned, never dereferenced: validation fails first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(fathom_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_match_header():
+    names = declared_functions()
+    assert len(names) == len(fa.EXPORTS) and set(names) == set(fa.EXPORTS)
+    for name in names:
+        assert hasattr(lib, name), name
+    out = os.popen(f"nm -D --defined-only {fa._LIB_PATH}").read()
+    for name in names:
+        assert re.search(rf"\bT {name}$", out, re.M), name
+
+
+def test_plane_ldw_and_workspace():
+    assert fa.plane_ldw(1) == 4 and fa.plane_ldw(129) == 8 and fa.plane_ldw(1 << 20) == 32768
+    assert lib.fathom_plane_ldw(0) == -1
+    s = fa.store_desc(8, 1 << 20)
+    assert fa.workspace_bytes(fa.FATHOM_OP_PACK, s) >= 8 * 128 * 24
+    ws = fa.workspace_bytes(fa.FATHOM_OP_SCAN, s, 32, 2048)
+    assert ws >= 32 * (16384 * 8 + 8192 * 4)
+    assert fa.workspace_bytes(7, s) == 0
+    assert fa.workspace_bytes(fa.FATHOM_OP_SCAN, SD(8, 64, 1 << 20, 32768), 32, 2048) == 0
+
+
+def status_text(st):
+    return lib.fathom_status_string(st).decode()
+
+
+def test_status_strings():
+    assert status_text(0) == "ok"
+    for st in (-1, -2, -3, -4):
+        assert status_text(st) not in ("ok", "unknown status")
+    assert status_text(99) == "unknown status"
+
+
+def _pack(store, keys=FAKE, stride_head=None, stride_token=128, planes=FAKE, ws=FAKE, ws_bytes=1 << 20):
+    if stride_head is None:
+        stride_head = store.n * 128
+    return lib.fathom_pack_planes(keys, stride_head, stride_token, ctypes.byref(store), planes, FAKE,
+                                  FAKE, FAKE, ws, ws_bytes, None)
+
+
+def test_pack_validation():
+    good = SD(2, 128, 1000, fa.plane_ldw(1000))
+    assert _pack(SD(2, 64, 1000, 32)) == fa.FATHOM_ERR_UNSUPPORTED
+    assert _pack(SD(0, 128, 1000, 32)) == fa.FATHOM_ERR_INVALID_ARG
+    assert _pack(SD(2, 128, 0, 4)) == fa.FATHOM_ERR_INVALID_ARG
+    assert _pack(SD(2, 128, 1000, 30)) == fa.FATHOM_ERR_INVALID_ARG      # not a multiple of 4
+    assert _pack(SD(2, 128, 1000, 28)) == fa.FATHOM_ERR_INVALID_ARG      # < ceil(n/32)
+    assert _pack(SD(2, 128, (1 << 26) + 1, 1 << 22)) == fa.FATHOM_ERR_UNSUPPORTED
+    assert _pack(good, keys=None) == fa.FATHOM_ERR_INVALID_ARG
+    assert _pack(good, keys=ctypes.c_void_p(0x1004)) == fa.FATHOM_ERR_INVALID_ARG
+    assert _pack(good, stride_token=130) == fa.FATHOM_ERR_INVALID_ARG
+    assert _pack(good, stride_head=100) == fa.FATHOM_ERR_INVALID_ARG
+    assert _pack(good, planes=ctypes.c_void_p(0x1008)) == fa.FATHOM_ERR_INVALID_ARG
+    assert _pack(good, ws=None) == fa.FATHOM_ERR_WORKSPACE
+    assert _pack(good, ws_bytes=16) == fa.FATHOM_ERR_WORKSPACE
+    assert _pack(good, ws=ctypes.c_void_p(0x1010)) == fa.FATHOM_ERR_WORKSPACE
+    assert "workspace" in lib.fathom_last_error().decode()
+
+
+def _alloc(store, num_q=8, group=4, budget=92, q=FAKE, alloc=FAKE):
+    return lib.fathom_allocate(q, num_q, group, FAKE, ctypes.byref(store), budget, alloc, None)
+
+
+def test_allocate_validation():
+    s = SD(2, 128, 1000, 32)
+    assert _alloc(s, num_q=6) == fa.FATHOM_ERR_INVALID_ARG                 # != H * group
+    assert _alloc(s, budget=-1) == fa.FATHOM_ERR_INVALID_ARG
+    assert _alloc(s, budget=513) == fa.FATHOM_ERR_INVALID_ARG
+    assert _alloc(s, group=0) == fa.FATHOM_ERR_INVALID_ARG
+    assert _alloc(s, q=None) == fa.FATHOM_ERR_INVALID_ARG
+    assert _alloc(s, alloc=ctypes.c_void_p(0x1001)) == fa.FATHOM_ERR_INVALID_ARG
+    assert _alloc(SD(2, 256, 1000, 32)) == fa.FATHOM_ERR_UNSUPPORTED
+    assert "513" in (_alloc(s, budget=513) and lib.fathom_last_error().decode())
+
+
+def _scan(store, num_q=8, group=4, k=16, planes=FAKE, ws=FAKE, ws_bytes=1 << 30, out_idx=FAKE):
+    return lib.fathom_scan_topk(planes, FAKE, FAKE, ctypes.byref(store), FAKE, FAKE, num_q, group, k,
+                                out_idx, FAKE, None, ws, ws_bytes, None)
+
+
+def test_scan_validation():
+    s = SD(2, 128, 1000, 32)
+    assert _scan(s, k=0) == fa.FATHOM_ERR_INVALID_ARG
+    assert _scan(s, k=1001) == fa.FATHOM_ERR_INVALID_ARG
+    big = SD(1, 128, 10000, fa.plane_ldw(10000))
+    assert _scan(big, num_q=4, k=4097) == fa.FATHOM_ERR_UNSUPPORTED
+    assert _scan(s, num_q=7) == fa.FATHOM_ERR_INVALID_ARG
+    assert _scan(s, planes=ctypes.c_void_p(0x1004)) == fa.FATHOM_ERR_INVALID_ARG
+    assert _scan(s, out_idx=None) == fa.FATHOM_ERR_INVALID_ARG
+    assert _scan(s, ws_bytes=1024) == fa.FATHOM_ERR_WORKSPACE
+    assert _scan(s, ws=None) == fa.FATHOM_ERR_WORKSPACE
+    assert _scan(SD(2, 128, 1000, 36), ws_bytes=10) == fa.FATHOM_ERR_WORKSPACE
+
+
+def test_misc_validation():
+    assert lib.fathom_host_device_pointer(None, None) == fa.FATHOM_ERR_INVALID_ARG
+    assert lib.fathom_timing_read(None, None) == fa.FATHOM_ERR_INVALID_ARG
