@@ -7,38 +7,48 @@
 // channel c.  With the planes MSB-first, the b-plane prefix of a channel is
 // its b-bit quantized value, so the partially dequantized dot product is
 //
-//   s_q(i) = C_q + sum_c sum_{j < b_qc} q_c step_c 2^(3-j) bit_{c,j}(i),
+//   s_q(i) = C_q + sum_c sum_{j < b_qc} W_qcj bit_{c,j}(i),
+//   W_qcj  = q_c step_c 2^(3-j),
 //   C_q    = sum_c q_c (lo_c + step_c 2^(3-b_qc))      (bin-centre offsets).
 //
 // Launch sequence per call (all on the caller's stream):
-//   1. scan_sample_kernel    exact scores of up to 8 sampled 1024-key blocks
-//                            per KV head (lane = key);
+//   1. scan_sample_kernel    scores of up to 8 sampled 1024-key blocks per KV
+//                            head (lane = key, planes staged through LDS);
 //   2. scan_threshold_kernel per query, a radix select on the sample picks a
 //                            score theta expected to leave ~2k keys above it;
-//   3. scan_main_kernel      every key of every head: workgroup = (KV head,
-//                            query chunk, 256 plane words), lane = one 32-key
-//                            word; reads the union of the chunk's plane
-//                            prefixes once, accumulates all its queries, and
-//                            appends keys scoring >= theta to a per-query
-//                            candidate list;
-//   4. scan_merge_kernel     per query, sorts the candidates in LDS and emits
-//                            the top-k.  If the candidate list holds fewer
-//                            than k keys or overflowed, the workgroup instead
-//                            recomputes the query's scores and selects the
-//                            exact top-k by radix select (ties by index).
-// Every kernel accumulates a query's planes in the same order (channel asc,
-// plane asc), so the three score paths produce identical fp32 values.
+//   3. scan_main_kernel      every key of every head, see below; keys scoring
+//                            >= theta go to a per-query candidate list;
+//   4. scan_merge_kernel     per query, radix-selects the k-th candidate, sorts
+//                            the survivors and writes the top-k.  If the list
+//                            holds fewer than k keys or overflowed, the
+//                            workgroup recomputes the query's scores and
+//                            selects the exact top-k (ties by index).
+//
+// Main kernel.  A workgroup owns one KV head and a chunk of <= 4 of its GQA
+// query heads, and reads, once, the union of the chunk's plane prefixes.  The
+// union planes are taken 8 at a time ("LUT chunks"); for each chunk the
+// prologue tabulates, for all 256 patterns of the 8 bits, the partial score
+// of every query of the chunk (planes a query does not read weigh 0).  Lane =
+// one 32-key plane word: a lane loads its word of the chunk's 8 plane rows
+// (coalesced), transposes the 8x32 bit block in registers so that each key's
+// 8 bits form one byte, and adds one table entry per key.  No MFMA: the work
+// is a bit-sliced gather-accumulate, bound by VALU and LDS gathers.
 
 #include "fathom_internal.h"
 
 namespace fathom {
 namespace {
 
-constexpr int kScanThreads = 256;
 constexpr int kMaxUnion = kD * kPlanes;
-constexpr int kMergeThreads = 1024;
-constexpr int kThresholdThreads = 256;
-constexpr int kPrefetch = 4;
+constexpr int kChunk = 8;                      // union planes per LUT chunk
+constexpr int kMaxChunks = kMaxUnion / kChunk;
+constexpr int kMainThreads = 768;              // two lanes per plane word
+constexpr int kTileWords = kMainThreads / 2;     // 384 words = 12288 keys per tile
+constexpr int kLutBytes = 144 * 1024;          // LUT capacity in LDS
+constexpr int kSampleThreads = 256;            // lane = key
+constexpr int kSampleWgPerBlock = kSampleBlockKeys / kSampleThreads;
+constexpr int kSelectThreads = 1024;
+constexpr int kSelectWaves = kSelectThreads / 64;
 
 struct ScanArgs {
   const uint32_t* planes;
@@ -52,6 +62,8 @@ struct ScanArgs {
   int group;          // query heads per KV head
   int cph;            // query chunks of this launch per KV head
   int qoff;           // first query of chunk 0 within its head
+  int tiles;          // kTileWords-word tiles per head
+  int tiles_per_wg;   // tiles handled by one main workgroup
   float* theta;
   uint32_t* count;
   float* sample;
@@ -62,11 +74,12 @@ struct ScanArgs {
 
 template <int GQ>
 struct UnionLds {
-  float w[kMaxUnion][GQ];       // q_c step_c 2^(3-j); 0 where the query skips the plane
-  double cpart[GQ][kD];
-  uint16_t row[kMaxUnion];      // plane row c*4 + j, in (c asc, j asc) order
-  uint8_t mask[kMaxUnion];      // bit g: query g of the chunk reads the plane
-  int off[kD];
+  float w[kMaxUnion + 2 * kChunk][4];        // W_qcj per union plane; 0 where the query skips it
+  uint32_t rowoff[kMaxUnion + 2 * kChunk];   // byte offset of the plane row (c*4 + j) in the head
+  uint8_t mask[kMaxUnion + 2 * kChunk];      // bit g: query g of the chunk reads the plane
+  int off[kPlanes][kD];
+  int u[kD];
+  double cpart[2][GQ];
   float C[GQ];
   float theta[GQ];
   int U;
@@ -83,241 +96,495 @@ __device__ inline double pow2_3_minus(int b) {
   return b == 0 ? 8.0 : b == 1 ? 4.0 : b == 2 ? 2.0 : b == 3 ? 1.0 : 0.5;
 }
 
+__device__ inline double wave_sum(double v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d);
+  return v;
+}
+
 // Builds the union plane list of a query chunk (queries q0 .. q0+GQ-1 on
 // KV head h), the per-plane weights and the score offsets C_q.
 // Needs blockDim.x >= kD; ends with __syncthreads().
 template <int GQ>
 __device__ void build_union(const ScanArgs& a, int h, int q0, UnionLds<GQ>& s) {
   const int t = threadIdx.x;
-  int u = 0, bq[GQ];
-  float qv[GQ], st = 0.0f;
+  int u = 0, bq[4] = {0, 0, 0, 0};
+  float qv[4] = {0.0f, 0.0f, 0.0f, 0.0f}, st = 0.0f;
   if (t < kD) {
     const float lo = a.lo[h * kD + t];
     st = a.step[h * kD + t];
+    double cp[GQ];
 #pragma unroll
     for (int g = 0; g < GQ; ++g) {
       bq[g] = min(static_cast<int>(a.alloc[int64_t(q0 + g) * kD + t]), kPlanes);
       qv[g] = a.q[int64_t(q0 + g) * kD + t];
       u = max(u, bq[g]);
-      s.cpart[g][t] = static_cast<double>(qv[g]) *
-                      (static_cast<double>(lo) + static_cast<double>(st) * pow2_3_minus(bq[g]));
+      cp[g] = static_cast<double>(qv[g]) *
+              (static_cast<double>(lo) + static_cast<double>(st) * pow2_3_minus(bq[g]));
     }
-  }
-  // exclusive prefix sum of u over channels (wave 0: two channels per lane)
-  __shared__ int s_u[kD];
-  if (t < kD) s_u[t] = u;
-  __syncthreads();
-  if (t < 64) {
-    const int v0 = s_u[2 * t], v1 = s_u[2 * t + 1];
-    int incl = v0 + v1;
+    s.u[t] = u;
+    // C_q: per-wave double sums over 64 channels, then the two halves
 #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int o = __shfl_up(incl, d);
-      if (t >= d) incl += o;
+    for (int g = 0; g < GQ; ++g) {
+      const double v = wave_sum(cp[g]);
+      if ((t & 63) == 0) s.cpart[t >> 6][g] = v;
     }
-    const int excl = incl - v0 - v1;
-    s.off[2 * t] = excl;
-    s.off[2 * t + 1] = excl + v0;
-    if (t == 63) s.U = incl;
   }
+  __syncthreads();
+  // Union plane list in (plane j asc, channel c asc) order: plane j of
+  // channel c is present when j < u_c.  Listing one plane level across many
+  // channels makes the 8 bits of a LUT index come from 8 different channels,
+  // which keeps the index distribution (and so the LDS bank spread) close to
+  // uniform; the order is free because the score is a plain sum.
+  // cnt[j] = #channels with u > j; exclusive prefix over channels per level.
+  if (t < 64) {
+    int base = 0;
+    for (int j = 0; j < kPlanes; ++j) {
+      const int v0 = s.u[2 * t] > j, v1 = s.u[2 * t + 1] > j;
+      int incl = v0 + v1;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int o = __shfl_up(incl, d);
+        if (t >= d) incl += o;
+      }
+      const int excl = base + incl - v0 - v1;
+      s.off[j][2 * t] = excl;
+      s.off[j][2 * t + 1] = excl + v0;
+      base += __shfl(incl, 63);
+    }
+    if (t == 0) s.U = base;
+  }
+  if (t < GQ) s.C[t] = static_cast<float>(s.cpart[0][t] + s.cpart[1][t]);
   __syncthreads();
   if (t < kD) {
-    const int o = s.off[t];
     for (int j = 0; j < u; ++j) {
+      const int o = s.off[j][t];
       uint32_t m = 0;
 #pragma unroll
-      for (int g = 0; g < GQ; ++g) {
-        const bool on = j < bq[g];
+      for (int g = 0; g < 4; ++g) {
+        const bool on = g < GQ && j < bq[g];
         m |= on ? (1u << g) : 0u;
-        s.w[o + j][g] = on ? __fmul_rn(qv[g], st) * static_cast<float>(8 >> j) : 0.0f;
+        s.w[o][g] = on ? __fmul_rn(qv[g], st) * static_cast<float>(8 >> j) : 0.0f;
       }
-      s.row[o + j] = static_cast<uint16_t>(t * kPlanes + j);
-      s.mask[o + j] = static_cast<uint8_t>(m);
+      s.rowoff[o] = static_cast<uint32_t>((t * kPlanes + j) * a.ldw * 4);
+      s.mask[o] = static_cast<uint8_t>(m);
     }
   }
-  __syncthreads();
-  if (t < GQ) {
-    double c = 0.0;
-    for (int i = 0; i < kD; ++i) c += s.cpart[t][i];
-    s.C[t] = static_cast<float>(c);
+  // padding up to a whole pair of LUT chunks: row 0, weight 0
+  const int U = s.U;
+  const int pad = (2 * kChunk - U % (2 * kChunk)) % (2 * kChunk);
+  if (t < pad) {
+    s.w[U + t][0] = s.w[U + t][1] = s.w[U + t][2] = s.w[U + t][3] = 0.0f;
+    s.rowoff[U + t] = 0u;
+    s.mask[U + t] = 0u;
   }
   __syncthreads();
 }
 
 // ------------------------------------------------------------------ sample
 
+// Workgroup = (quarter of a sampled 1024-key block, KV head, query chunk):
+// the union plane words of its 256 keys are staged in LDS, then thread = key.
 template <int GQ>
-__global__ __launch_bounds__(kScanThreads) void scan_sample_kernel(ScanArgs a) {
+__global__ __launch_bounds__(kSampleThreads) void scan_sample_kernel(ScanArgs a) {
+  constexpr int kWords = kSampleThreads / 32;
   __shared__ UnionLds<GQ> s;
+  __shared__ uint32_t stage[kMaxUnion][kWords];
   const int h = blockIdx.y / a.cph;
   const int q0 = h * a.group + a.qoff + (blockIdx.y % a.cph) * kQueryChunk;
   build_union<GQ>(a, h, q0, s);
 
-  const int sbi = blockIdx.x >> 2;
-  const int local = (blockIdx.x & 3) * kScanThreads + threadIdx.x;   // 0..1023
-  const int64_t key = int64_t(sbi) * a.sample_stride * kSampleBlockKeys + local;
+  const int sbi = blockIdx.x / kSampleWgPerBlock;
+  const int part = blockIdx.x % kSampleWgPerBlock;
+  const int64_t word0 = int64_t(sbi) * a.sample_stride * (kSampleBlockKeys / 32) + part * kWords;
+  const char* head = reinterpret_cast<const char*>(a.planes + int64_t(h) * kD * kPlanes * a.ldw);
+  const int U = s.U;
+  // every thread issues all of its staging loads before the first store
+  constexpr int kPer = (kMaxUnion * kWords + kSampleThreads - 1) / kSampleThreads;
+  uint32_t tmp[kPer];
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    const int i = threadIdx.x + r * kSampleThreads;
+    const int p = i / kWords, wd = i % kWords;
+    const int64_t w = word0 + wd;
+    tmp[r] = (p < U && w < a.ldw) ? *reinterpret_cast<const uint32_t*>(head + s.rowoff[p] + w * 4) : 0u;
+  }
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    const int i = threadIdx.x + r * kSampleThreads;
+    if (i / kWords < U) stage[i / kWords][i % kWords] = tmp[r];
+  }
+  __syncthreads();
+  const int64_t key = word0 * 32 + threadIdx.x;
   const bool valid = key < a.n;
-  const uint32_t* base = a.planes + int64_t(h) * kD * kPlanes * a.ldw + (valid ? (key >> 5) : 0);
-  const int bit = static_cast<int>(key & 31);
+  const int sh = threadIdx.x & 31, wsel = threadIdx.x >> 5;
   float acc[GQ];
 #pragma unroll
   for (int g = 0; g < GQ; ++g) acc[g] = 0.0f;
-  const int U = s.U;
+#pragma unroll 8
   for (int p = 0; p < U; ++p) {
-    const uint32_t x = valid ? base[int64_t(s.row[p]) * a.ldw] : 0u;
-    const float f = static_cast<float>((x >> bit) & 1u);
+    const float f = static_cast<float>((stage[p][wsel] >> sh) & 1u);
     const uint32_t m = s.mask[p];
 #pragma unroll
     for (int g = 0; g < GQ; ++g)
       if (m & (1u << g)) acc[g] = fmaf(f, s.w[p][g], acc[g]);
   }
+  const int local = part * kSampleThreads + threadIdx.x;   // 0..1023 within the block
 #pragma unroll
   for (int g = 0; g < GQ; ++g)
     a.sample[int64_t(q0 + g) * kSampleMaxKeys + sbi * kSampleBlockKeys + local] =
         valid ? acc[g] + s.C[g] : -INFINITY;
 }
 
-// --------------------------------------------------------------- threshold
+// ----------------------------------------------------------- block select
 
-// Radix select of the r-th largest of `count` ordered keys held in LDS.
-// All threads of the block call it; returns the ordered key.
-__device__ uint32_t block_select_kth(const uint32_t* vals, int count, uint32_t r, uint32_t* hist,
-                                     uint32_t* s_scalar) {
-  uint32_t prefix = 0, pmask = 0;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = threadIdx.x; i < 256; i += blockDim.x) hist[i] = 0;
-    __syncthreads();
-    for (int i = threadIdx.x; i < count; i += blockDim.x) {
-      const uint32_t v = vals[i];
-      if ((v & pmask) == prefix) atomicAdd(&hist[(v >> shift) & 255u], 1u);
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      uint32_t cum = 0;
-      int sel = 0;
-      for (int bin = 255; bin >= 0; --bin) {
-        if (cum + hist[bin] >= r) { sel = bin; break; }
-        cum += hist[bin];
-      }
-      s_scalar[0] = static_cast<uint32_t>(sel);
-      s_scalar[1] = r - cum;
-    }
-    __syncthreads();
-    prefix |= s_scalar[0] << shift;
-    pmask |= 255u << shift;
-    r = s_scalar[1];
-    __syncthreads();
+struct SelectLds {
+  uint32_t hist[kSelectWaves][256];
+  uint32_t total[256];
+  uint32_t sel;
+  uint32_t rem;
+};
+
+// One radix pass of a block-wide select: given the per-wave histograms of
+// the current digit, finds the bin holding the r-th largest value.  Returns
+// (bin, r minus the count in the bins above it).
+__device__ uint2 select_bin(SelectLds& L, uint32_t r) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int b = tid; b < 256; b += blockDim.x) {
+    uint32_t sum = 0;
+    for (int w = 0; w < kSelectWaves; ++w) sum += L.hist[w][b];
+    L.total[b] = sum;
   }
-  return prefix;
+  __syncthreads();
+  if (wave == 0) {
+    // lane l owns bins 255-4l .. 252-4l (descending order across lanes)
+    uint32_t c[4], own = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { c[j] = L.total[255 - 4 * lane - j]; own += c[j]; }
+    uint32_t incl = own;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const uint32_t o = __shfl_up(incl, d);
+      if (lane >= d) incl += o;
+    }
+    uint32_t before = incl - own;   // count in the bins above this lane's bins
+    if (before < r && incl >= r) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (before + c[j] >= r) {
+          L.sel = static_cast<uint32_t>(255 - 4 * lane - j);
+          L.rem = r - before;
+          break;
+        }
+        before += c[j];
+      }
+    }
+  }
+  __syncthreads();
+  const uint2 out = make_uint2(L.sel, L.rem);
+  __syncthreads();
+  return out;
 }
 
-__global__ __launch_bounds__(kThresholdThreads) void scan_threshold_kernel(
+__device__ inline void clear_hist(SelectLds& L) {
+  for (int i = threadIdx.x; i < kSelectWaves * 256; i += blockDim.x) (&L.hist[0][0])[i] = 0;
+  __syncthreads();
+}
+
+// r-th largest (1-based) of the ordered keys v[j] held by the block's threads
+// (value j of thread t is element t + j*blockDim.x, present when < count).
+// Returns (key, r minus the number of values strictly above the key).
+template <int PT>
+__device__ uint2 block_select_regs(const uint32_t (&v)[PT], uint32_t count, uint32_t r, SelectLds& L) {
+  const int tid = threadIdx.x, wave = tid >> 6;
+  uint32_t prefix = 0, pmask = 0;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    clear_hist(L);
+#pragma unroll
+    for (int j = 0; j < PT; ++j) {
+      const uint32_t i = tid + j * blockDim.x;
+      if (i < count && (v[j] & pmask) == prefix) atomicAdd(&L.hist[wave][(v[j] >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    const uint2 b = select_bin(L, r);
+    prefix |= b.x << shift;
+    pmask |= 255u << shift;
+    r = b.y;
+  }
+  return make_uint2(prefix, r);
+}
+
+// Same, over values produced on demand by get(i) for i < count.
+template <class Get>
+__device__ uint2 block_select_fn(int64_t count, uint32_t r, SelectLds& L, Get get) {
+  const int tid = threadIdx.x, wave = tid >> 6;
+  uint32_t prefix = 0, pmask = 0;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    clear_hist(L);
+    for (int64_t i = tid; i < count; i += blockDim.x) {
+      const uint32_t v = get(i);
+      if ((v & pmask) == prefix) atomicAdd(&L.hist[wave][(v >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    const uint2 b = select_bin(L, r);
+    prefix |= b.x << shift;
+    pmask |= 255u << shift;
+    r = b.y;
+  }
+  return make_uint2(prefix, r);
+}
+
+// --------------------------------------------------------------- threshold
+
+__global__ __launch_bounds__(kSelectThreads) void scan_threshold_kernel(
     const float* __restrict__ sample, int stot, uint32_t rsel, float* __restrict__ theta,
     uint32_t* __restrict__ count) {
-  __shared__ uint32_t vals[kSampleMaxKeys];
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t s_scalar[2];
+  __shared__ SelectLds L;
+  constexpr int PT = kSampleMaxKeys / kSelectThreads;
   const int q = blockIdx.x;
-  for (int i = threadIdx.x; i < stot; i += blockDim.x)
-    vals[i] = float_to_ordered(sample[int64_t(q) * kSampleMaxKeys + i]);
-  __syncthreads();
-  const uint32_t key = block_select_kth(vals, stot, rsel, hist, s_scalar);
+  uint32_t v[PT];
+#pragma unroll
+  for (int j = 0; j < PT; ++j) {
+    const int i = threadIdx.x + j * kSelectThreads;
+    v[j] = i < stot ? float_to_ordered(sample[int64_t(q) * kSampleMaxKeys + i]) : 0u;
+  }
+  const uint2 sel = block_select_regs<PT>(v, static_cast<uint32_t>(stot), rsel, L);
   if (threadIdx.x == 0) {
-    theta[q] = ordered_to_float(key);
+    theta[q] = ordered_to_float(sel.x);
     count[q] = 0u;
   }
 }
 
 // -------------------------------------------------------------------- main
 
-template <int GQ, uint32_t M>
-__device__ __forceinline__ void accumulate_masked(uint32_t x, const float (&wv)[GQ],
-                                                  float (&acc)[32][GQ]) {
+template <int GQ> struct LutEntry { using T = float4; };
+template <> struct LutEntry<1> { using T = float; };
+template <> struct LutEntry<2> { using T = float2; };
+
+template <int GQ>
+struct MainLds {
+  using E = typename LutEntry<GQ>::T;
+  static constexpr int kCapRaw = kLutBytes / (256 * static_cast<int>(sizeof(E)));
+  static constexpr int kCap = kCapRaw < kMaxChunks ? kCapRaw : kMaxChunks;   // chunks per pass
+  E lut[kCap][256];
+  UnionLds<GQ> u;
+};
+
+__device__ inline float comp(float e, int) { return e; }
+__device__ inline float comp(float2 e, int g) { return g == 0 ? e.x : e.y; }
+__device__ inline float comp(float4 e, int g) { return g == 0 ? e.x : g == 1 ? e.y : g == 2 ? e.z : e.w; }
+
+// Tabulates chunks [m0, m1) of the union: entry e of chunk m holds, for every
+// query g, the sum of the weights of the chunk's planes whose bit is set in e
+// (plane 8m + t <-> bit t), added in t order.
+template <int GQ>
+__device__ void build_lut(MainLds<GQ>& S, int m0, int m1, int U) {
+  using E = typename MainLds<GQ>::E;
+  const int total = (m1 - m0) * 256;
+  for (int i = threadIdx.x; i < total; i += blockDim.x) {
+    const int m = m0 + (i >> 8), e = i & 255;
+    float sum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-  for (int b = 0; b < 32; ++b) {
-    const float f = static_cast<float>((x >> b) & 1u);
-#pragma unroll
-    for (int g = 0; g < GQ; ++g)
-      if (M & (1u << g)) acc[b][g] = fmaf(f, wv[g], acc[b][g]);
+    for (int t = 0; t < kChunk; ++t) {
+      const int p = m * kChunk + t;
+      if (((e >> t) & 1) && p < U) {
+        const float4 w = *reinterpret_cast<const float4*>(&S.u.w[p][0]);
+        sum[0] += w.x;
+        sum[1] += w.y;
+        sum[2] += w.z;
+        sum[3] += w.w;
+      }
+    }
+    E out;
+    if constexpr (GQ == 1) {
+      out = sum[0];
+    } else if constexpr (GQ == 2) {
+      out = make_float2(sum[0], sum[1]);
+    } else {
+      out = make_float4(sum[0], sum[1], sum[2], sum[3]);
+    }
+    S.lut[m - m0][e] = out;
   }
 }
 
-template <int GQ, uint32_t M = 1>
-__device__ __forceinline__ void accumulate(uint32_t m, uint32_t x, const float (&wv)[GQ],
-                                           float (&acc)[32][GQ]) {
-  if constexpr (M < (1u << GQ)) {
-    if (m == M) {
-      accumulate_masked<GQ, M>(x, wv, acc);
-      return;
-    }
-    accumulate<GQ, M + 1>(m, x, wv, acc);
+// In-register transpose of an 8x32 bit block: on entry x[t] holds plane t's
+// bits of 32 keys (key b at bit b); on exit byte g of x[k] holds the 8 plane
+// bits of key 8g + k (plane t at bit t).  Three rounds of block swaps.
+__device__ __forceinline__ void transpose8x32(uint32_t (&x)[8]) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const uint32_t d = ((x[t] >> 4) ^ x[t + 4]) & 0x0f0f0f0fu;
+    x[t + 4] ^= d;
+    x[t] ^= d << 4;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = (i & 1) + (i >> 1) * 4;    // 0, 1, 4, 5
+    const uint32_t d = ((x[t] >> 2) ^ x[t + 2]) & 0x33333333u;
+    x[t + 2] ^= d;
+    x[t] ^= d << 2;
+  }
+#pragma unroll
+  for (int t = 0; t < 8; t += 2) {
+    const uint32_t d = ((x[t] >> 1) ^ x[t + 1]) & 0x55555555u;
+    x[t + 1] ^= d;
+    x[t] ^= d << 1;
+  }
+}
+
+// Loads this lane's word of the 8 plane rows of chunk m.  The union list is
+// padded to whole chunk pairs with readable rows, and lanes past the store's
+// last word read that word instead, so every load is unconditional.
+template <int GQ>
+__device__ __forceinline__ void load_chunk(const char* head, const UnionLds<GQ>& s, int m,
+                                           uint32_t woff, uint32_t (&x)[8]) {
+#pragma unroll
+  for (int t = 0; t < kChunk; ++t)
+    x[t] = *reinterpret_cast<const uint32_t*>(head + s.rowoff[m * kChunk + t] + woff);
+}
+
+// Accumulates a pair of chunks (m, m+1) for this lane's 16 keys.  Two lanes
+// share a plane word: lane half h owns bits 16h..16h+15.  The lane packs its
+// halves of the two chunks into one word per plane (chunk m low, chunk m+1
+// high), so a single 8x32 transpose yields the LUT index bytes of 16 keys x 2
+// chunks: byte g of x[k] indexes chunk m + (g >> 1) for key 8(g & 1) + k.
+template <int GQ>
+__device__ __forceinline__ void accumulate_pair(const typename MainLds<GQ>::E* lut_m,
+                                                const typename MainLds<GQ>::E* lut_m1,
+                                                const uint32_t (&xa)[8], const uint32_t (&xb)[8],
+                                                uint32_t sel, float (&acc)[16][GQ]) {
+  using E = typename MainLds<GQ>::E;
+  uint32_t x[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) x[t] = __builtin_amdgcn_perm(xb[t], xa[t], sel);
+  transpose8x32(x);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    E e[4];
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) e[g4] = (g4 < 2 ? lut_m : lut_m1)[(x[k] >> (8 * g4)) & 0xffu];
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4)
+#pragma unroll
+      for (int g = 0; g < GQ; ++g) acc[8 * (g4 & 1) + k][g] += comp(e[g4], g);
   }
 }
 
 template <int GQ>
-__global__ __launch_bounds__(kScanThreads) void scan_main_kernel(ScanArgs a) {
-  __shared__ UnionLds<GQ> s;
+__global__ __launch_bounds__(kMainThreads) void scan_main_kernel(ScanArgs a) {
+  using E = typename MainLds<GQ>::E;
+  constexpr int kCapChunks = MainLds<GQ>::kCap & ~1;        // passes hold whole chunk pairs
+  __shared__ MainLds<GQ> S;
+  UnionLds<GQ>& s = S.u;
   const int h = blockIdx.y / a.cph;
   const int q0 = h * a.group + a.qoff + (blockIdx.y % a.cph) * kQueryChunk;
   if (threadIdx.x < GQ) s.theta[threadIdx.x] = a.theta[q0 + threadIdx.x];
   build_union<GQ>(a, h, q0, s);
 
   const int lane = threadIdx.x & 63;
-  const int w = blockIdx.x * kScanThreads + threadIdx.x;
-  const bool active = w < a.nwords;
-  const uint32_t* base = a.planes + int64_t(h) * kD * kPlanes * a.ldw + (active ? w : 0);
+  const int half = threadIdx.x & 1;
+  const uint32_t sel = half ? 0x07060302u : 0x05040100u;   // v_perm byte selectors
   const int U = s.U;
+  const int nchunks = ((U + 2 * kChunk - 1) / (2 * kChunk)) * 2;   // whole pairs
+  const int passes = (nchunks + kCapChunks - 1) / kCapChunks;
+  const char* head = reinterpret_cast<const char*>(a.planes + int64_t(h) * kD * kPlanes * a.ldw);
+  if (passes == 1) {
+    build_lut<GQ>(S, 0, nchunks, U);
+    __syncthreads();
+  }
+  const int tile_begin = blockIdx.x * a.tiles_per_wg;
+  const int tile_end = min(a.tiles, tile_begin + a.tiles_per_wg);
 
-  float acc[32][GQ];
+  for (int tile = tile_begin; tile < tile_end; ++tile) {
+    const int w = tile * kTileWords + (threadIdx.x >> 1);
+    const bool active = w < a.nwords;
+    const uint32_t woff = static_cast<uint32_t>(active ? w : a.nwords - 1) * 4u;
+    float acc[16][GQ];
 #pragma unroll
-  for (int b = 0; b < 32; ++b)
+    for (int b = 0; b < 16; ++b)
 #pragma unroll
-    for (int g = 0; g < GQ; ++g) acc[b][g] = 0.0f;
+      for (int g = 0; g < GQ; ++g) acc[b][g] = 0.0f;
 
-  uint32_t ring[kPrefetch];
-#pragma unroll
-  for (int r = 0; r < kPrefetch; ++r)
-    ring[r] = (r < U && active) ? base[int64_t(s.row[r]) * a.ldw] : 0u;
-
-  for (int p0 = 0; p0 < U; p0 += kPrefetch) {
-#pragma unroll
-    for (int r = 0; r < kPrefetch; ++r) {
-      const int p = p0 + r;
-      if (p < U) {
-        const uint32_t x = ring[r];
-        const int pn = p + kPrefetch;
-        ring[r] = (pn < U && active) ? base[int64_t(s.row[pn]) * a.ldw] : 0u;
-        const uint32_t m = __builtin_amdgcn_readfirstlane(s.mask[p]);
-        float wv[GQ];
-#pragma unroll
-        for (int g = 0; g < GQ; ++g) wv[g] = s.w[p][g];
-        accumulate<GQ>(m, x, wv, acc);
+    for (int pass = 0; pass < passes; ++pass) {
+      const int m_begin = pass * kCapChunks;
+      const int m_end = min(nchunks, m_begin + kCapChunks);
+      if (passes > 1) {
+        __syncthreads();
+        build_lut<GQ>(S, m_begin, m_end, U);
+        __syncthreads();
+      }
+      // Two pair buffers: while one pair is accumulated the next pair's loads
+      // are in flight.  Loads are unconditional (pair index clamped) so the
+      // compiler counts outstanding loads exactly, and scheduling barriers
+      // keep it from hoisting further loads into the accumulation.
+      const int npairs = (m_end - m_begin) / 2;
+      const int plast = npairs - 1;
+      uint32_t a0[8], a1[8], b0[8], b1[8];
+      load_chunk<GQ>(head, s, m_begin, woff, a0);
+      load_chunk<GQ>(head, s, m_begin + 1, woff, a1);
+      load_chunk<GQ>(head, s, m_begin + 2 * min(1, plast), woff, b0);
+      load_chunk<GQ>(head, s, m_begin + 2 * min(1, plast) + 1, woff, b1);
+      for (int pp = 0; pp < npairs; pp += 2) {
+        const int m = m_begin + 2 * pp;
+        accumulate_pair<GQ>(S.lut[m - m_begin], S.lut[m + 1 - m_begin], a0, a1, sel, acc);
+        __builtin_amdgcn_sched_barrier(0);
+        const int mn = m_begin + 2 * min(pp + 2, plast);
+        load_chunk<GQ>(head, s, mn, woff, a0);
+        load_chunk<GQ>(head, s, mn + 1, woff, a1);
+        __builtin_amdgcn_sched_barrier(0);
+        if (pp + 1 < npairs)
+          accumulate_pair<GQ>(S.lut[m + 2 - m_begin], S.lut[m + 3 - m_begin], b0, b1, sel, acc);
+        __builtin_amdgcn_sched_barrier(0);
+        const int mq = m_begin + 2 * min(pp + 3, plast);
+        load_chunk<GQ>(head, s, mq, woff, b0);
+        load_chunk<GQ>(head, s, mq + 1, woff, b1);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-  }
 
-  // epilogue: finish scores, optional dump, threshold filter + append
-  const int64_t key0 = int64_t(w) * 32;
+    // epilogue: finish scores, optional dump, then the threshold filter.
+    // Candidates are appended with one atomic per (wave, query): each lane
+    // counts its passing keys, a wave prefix sum gives every lane its offset.
+    const int64_t key0 = int64_t(w) * 32 + 16 * half;
+    const int nvalid = active ? static_cast<int>(max<int64_t>(0, min<int64_t>(16, a.n - key0))) : 0;
 #pragma unroll
-  for (int b = 0; b < 32; ++b) {
-    const int64_t i = key0 + b;
-    const bool valid = active && i < a.n;
+    for (int b = 0; b < 16; ++b)
+#pragma unroll
+      for (int g = 0; g < GQ; ++g) acc[b][g] += s.C[g];
+    if (a.all_scores) {
+#pragma unroll
+      for (int g = 0; g < GQ; ++g)
+#pragma unroll
+        for (int b = 0; b < 16; ++b)
+          if (b < nvalid) a.all_scores[int64_t(q0 + g) * a.n + key0 + b] = acc[b][g];
+    }
 #pragma unroll
     for (int g = 0; g < GQ; ++g) {
-      const float sc = acc[b][g] + s.C[g];
-      if (a.all_scores && valid) a.all_scores[int64_t(q0 + g) * a.n + i] = sc;
-      const bool pass = valid && sc >= s.theta[g];
-      const uint64_t bal = __ballot(pass);
-      if (bal) {
-        const int leader = __builtin_ctzll(bal);
-        uint32_t slot0 = 0;
-        if (lane == leader) slot0 = atomicAdd(&a.count[q0 + g], static_cast<uint32_t>(__popcll(bal)));
-        slot0 = __builtin_amdgcn_readlane(slot0, leader);
-        if (pass) {
-          const uint32_t slot = slot0 + lanes_below(bal);
+      const float th = s.theta[g];
+      uint32_t bits = 0;
+#pragma unroll
+      for (int b = 0; b < 16; ++b) bits |= (b < nvalid && acc[b][g] >= th) ? (1u << b) : 0u;
+      const uint32_t mine = __popc(bits);
+      uint32_t incl = mine;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t o = __shfl_up(incl, d);
+        if (lane >= d) incl += o;
+      }
+      const uint32_t total = __shfl(incl, 63);
+      if (total == 0) continue;                       // uniform
+      uint32_t base = 0;
+      if (lane == 0) base = atomicAdd(&a.count[q0 + g], total);
+      uint32_t slot = __shfl(base, 0) + incl - mine;
+      // static key index: a computed index into acc would move the whole
+      // accumulator array to scratch memory
+#pragma unroll
+      for (int b = 0; b < 16; ++b) {
+        if (bits & (1u << b)) {
           if (slot < static_cast<uint32_t>(kCandCap))
             a.cand[int64_t(q0 + g) * kCandCap + slot] =
-                make_uint2(__float_as_uint(sc), static_cast<uint32_t>(i));
+                make_uint2(__float_as_uint(acc[b][g]), static_cast<uint32_t>(key0 + b));
+          ++slot;
         }
       }
     }
@@ -326,8 +593,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_main_kernel(ScanArgs a) {
 
 // ------------------------------------------------------------------- merge
 
-__device__ inline unsigned long long sort_key(float score, uint32_t idx) {
-  return (static_cast<unsigned long long>(float_to_ordered(score)) << 32) | static_cast<uint32_t>(~idx);
+__device__ inline unsigned long long sort_key(uint32_t ordered, uint32_t idx) {
+  return (static_cast<unsigned long long>(ordered) << 32) | static_cast<uint32_t>(~idx);
 }
 
 // Descending bitonic sort of N (power of two) 64-bit keys in LDS.
@@ -352,12 +619,11 @@ __device__ void bitonic_sort_desc(unsigned long long* keys, unsigned N) {
 struct QueryLds {
   float w[kD][kPlanes];
   uint8_t b[kD];
-  double cpart[kD];
+  double cpart[2];
   float C;
 };
 
-// Score of key i for one query: same plane order and fp32 operations as the
-// chunked kernels, so the value is bit-identical to theirs.
+// Score of key i for one query, plane by plane (fallback path).
 __device__ inline float query_score(const uint32_t* head_planes, int64_t ldw, const QueryLds& s,
                                     int64_t i) {
   const uint32_t* base = head_planes + (i >> 5);
@@ -373,30 +639,53 @@ __device__ inline float query_score(const uint32_t* head_planes, int64_t ldw, co
   return acc + s.C;
 }
 
-__global__ __launch_bounds__(kMergeThreads) void scan_merge_kernel(ScanArgs a, int k,
-                                                                   int32_t* __restrict__ out_idx,
-                                                                   float* __restrict__ out_score) {
-  __shared__ unsigned long long keys[kCandCap];
+__global__ __launch_bounds__(kSelectThreads) void scan_merge_kernel(ScanArgs a, int k,
+                                                                    int32_t* __restrict__ out_idx,
+                                                                    float* __restrict__ out_score) {
+  constexpr int PT = kCandCap / kSelectThreads;
+  __shared__ unsigned long long keys[kCandCap];     // sort buffer (score, ~index)
+  __shared__ SelectLds L;
   __shared__ QueryLds qs;
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t s_scalar[4];
-  __shared__ uint32_t s_wave[kMergeThreads / 64];
+  __shared__ uint32_t s_count[2];
+  __shared__ uint32_t s_wave[kSelectWaves];
   const int q = blockIdx.x;
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const uint32_t cnt = a.count[q];
   unsigned N;
 
   if (cnt >= static_cast<uint32_t>(k) && cnt <= static_cast<uint32_t>(kCandCap)) {
-    N = 2;
-    while (N < cnt) N <<= 1;
-    for (unsigned i = tid; i < N; i += blockDim.x) {
+    const uint2* cand = a.cand + int64_t(q) * kCandCap;
+    uint32_t v[PT], id[PT];
+#pragma unroll
+    for (int j = 0; j < PT; ++j) {
+      const uint32_t i = tid + j * kSelectThreads;
       if (i < cnt) {
-        const uint2 e = a.cand[int64_t(q) * kCandCap + i];
-        keys[i] = sort_key(__uint_as_float(e.x), e.y);
+        const uint2 e = cand[i];
+        v[j] = float_to_ordered(__uint_as_float(e.x));
+        id[j] = e.y;
       } else {
-        keys[i] = 0ull;
+        v[j] = 0u;
+        id[j] = 0u;
       }
     }
+    // the k-th best candidate score; keep every candidate at or above it
+    const uint2 sel = block_select_regs<PT>(v, cnt, static_cast<uint32_t>(k), L);
+    if (tid == 0) s_count[0] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < PT; ++j) {
+      const uint32_t i = tid + j * kSelectThreads;
+      if (i < cnt && v[j] >= sel.x) {
+        const uint32_t slot = atomicAdd(&s_count[0], 1u);
+        keys[slot] = sort_key(v[j], id[j]);
+      }
+    }
+    __syncthreads();
+    const uint32_t kept = s_count[0];
+    N = 2;
+    while (N < kept) N <<= 1;
+    for (unsigned i = kept + tid; i < N; i += blockDim.x) keys[i] = 0ull;
     __syncthreads();
   } else {
     // exact fallback: radix select over recomputed scores
@@ -408,47 +697,22 @@ __global__ __launch_bounds__(kMergeThreads) void scan_merge_kernel(ScanArgs a, i
       const int bc = min(static_cast<int>(a.alloc[int64_t(q) * kD + tid]), kPlanes);
       qs.b[tid] = static_cast<uint8_t>(bc);
       for (int j = 0; j < kPlanes; ++j) qs.w[tid][j] = __fmul_rn(qv, st) * static_cast<float>(8 >> j);
-      qs.cpart[tid] = static_cast<double>(qv) *
-                      (static_cast<double>(lo) + static_cast<double>(st) * pow2_3_minus(bc));
+      const double v = wave_sum(static_cast<double>(qv) *
+                                (static_cast<double>(lo) + static_cast<double>(st) * pow2_3_minus(bc)));
+      if (lane == 0) qs.cpart[wave] = v;
     }
     __syncthreads();
-    if (tid == 0) {
-      double c = 0.0;
-      for (int i = 0; i < kD; ++i) c += qs.cpart[i];
-      qs.C = static_cast<float>(c);
-    }
+    if (tid == 0) qs.C = static_cast<float>(qs.cpart[0] + qs.cpart[1]);
     __syncthreads();
-    uint32_t prefix = 0, pmask = 0, r = static_cast<uint32_t>(k);
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      for (int i = tid; i < 256; i += blockDim.x) hist[i] = 0;
-      __syncthreads();
-      for (int64_t i = tid; i < a.n; i += blockDim.x) {
-        const uint32_t v = float_to_ordered(query_score(head_planes, a.ldw, qs, i));
-        if ((v & pmask) == prefix) atomicAdd(&hist[(v >> shift) & 255u], 1u);
-      }
-      __syncthreads();
-      if (tid == 0) {
-        uint32_t cum = 0;
-        int sel = 0;
-        for (int bin = 255; bin >= 0; --bin) {
-          if (cum + hist[bin] >= r) { sel = bin; break; }
-          cum += hist[bin];
-        }
-        s_scalar[0] = static_cast<uint32_t>(sel);
-        s_scalar[1] = r - cum;
-      }
-      __syncthreads();
-      prefix |= s_scalar[0] << shift;
-      pmask |= 255u << shift;
-      r = s_scalar[1];
-      __syncthreads();
-    }
-    const uint32_t kth = prefix;                 // ordered score of the k-th key
-    const uint32_t n_gt = static_cast<uint32_t>(k) - r;   // keys strictly above it
-    if (tid == 0) s_scalar[2] = 0;               // gt slots used
+    const uint2 sel = block_select_fn(a.n, static_cast<uint32_t>(k), L, [&](int64_t i) {
+      return float_to_ordered(query_score(head_planes, a.ldw, qs, i));
+    });
+    const uint32_t kth = sel.x;                                   // ordered score of the k-th key
+    const uint32_t need_eq = sel.y;                               // ties at kth to take
+    const uint32_t n_gt = static_cast<uint32_t>(k) - need_eq;     // keys strictly above it
+    if (tid == 0) s_count[0] = 0;
     __syncthreads();
     uint32_t eq_taken = 0;
-    const int lane = tid & 63, wave = tid >> 6;
     for (int64_t base = 0; base < a.n; base += blockDim.x) {
       const int64_t i = base + tid;
       const bool valid = i < a.n;
@@ -456,22 +720,21 @@ __global__ __launch_bounds__(kMergeThreads) void scan_merge_kernel(ScanArgs a, i
       const bool gt = valid && v > kth;
       const bool eq = valid && v == kth;
       if (gt) {
-        const uint32_t slot = atomicAdd(&s_scalar[2], 1u);
-        keys[slot] = (static_cast<unsigned long long>(v) << 32) | static_cast<uint32_t>(~static_cast<uint32_t>(i));
+        const uint32_t slot = atomicAdd(&s_count[0], 1u);
+        keys[slot] = sort_key(v, static_cast<uint32_t>(i));
       }
       const uint64_t bal = __ballot(eq);
       if (lane == 0) s_wave[wave] = static_cast<uint32_t>(__popcll(bal));
       __syncthreads();
       uint32_t before = 0, total = 0;
-      for (int wv = 0; wv < static_cast<int>(blockDim.x / 64); ++wv) {
+      for (int wv = 0; wv < kSelectWaves; ++wv) {
         const uint32_t c = s_wave[wv];
         before += wv < wave ? c : 0u;
         total += c;
       }
       if (eq) {
         const uint32_t rank = eq_taken + before + static_cast<uint32_t>(lanes_below(bal));
-        if (rank < r)
-          keys[n_gt + rank] = (static_cast<unsigned long long>(v) << 32) | static_cast<uint32_t>(~static_cast<uint32_t>(i));
+        if (rank < need_eq) keys[n_gt + rank] = sort_key(v, static_cast<uint32_t>(i));
       }
       eq_taken += total;
       __syncthreads();
@@ -490,25 +753,22 @@ __global__ __launch_bounds__(kMergeThreads) void scan_merge_kernel(ScanArgs a, i
 }
 
 template <int GQ>
-hipError_t launch_chunk_class(const ScanArgs& a, int H, int nsb, const ScanTiming* timing,
-                              bool sample_phase, hipStream_t stream) {
+void launch_chunk_class(const ScanArgs& a, int H, int nsb, bool sample_phase, hipStream_t stream) {
   if (sample_phase) {
-    hipLaunchKernelGGL(scan_sample_kernel<GQ>, dim3(nsb * 4, H * a.cph), dim3(kScanThreads), 0, stream, a);
+    hipLaunchKernelGGL(scan_sample_kernel<GQ>, dim3(nsb * kSampleWgPerBlock, H * a.cph),
+                       dim3(kSampleThreads), 0, stream, a);
   } else {
-    const int tiles = (a.nwords + kScanThreads - 1) / kScanThreads;
-    hipLaunchKernelGGL(scan_main_kernel<GQ>, dim3(tiles, H * a.cph), dim3(kScanThreads), 0, stream, a);
+    const int wgs = (a.tiles + a.tiles_per_wg - 1) / a.tiles_per_wg;
+    hipLaunchKernelGGL(scan_main_kernel<GQ>, dim3(wgs, H * a.cph), dim3(kMainThreads), 0, stream, a);
   }
-  (void)timing;
-  return hipGetLastError();
 }
 
-hipError_t launch_class(int gq, const ScanArgs& a, int H, int nsb, const ScanTiming* timing,
-                        bool sample_phase, hipStream_t stream) {
+void launch_class(int gq, const ScanArgs& a, int H, int nsb, bool sample_phase, hipStream_t stream) {
   switch (gq) {
-    case 1: return launch_chunk_class<1>(a, H, nsb, timing, sample_phase, stream);
-    case 2: return launch_chunk_class<2>(a, H, nsb, timing, sample_phase, stream);
-    case 3: return launch_chunk_class<3>(a, H, nsb, timing, sample_phase, stream);
-    default: return launch_chunk_class<4>(a, H, nsb, timing, sample_phase, stream);
+    case 1: launch_chunk_class<1>(a, H, nsb, sample_phase, stream); break;
+    case 2: launch_chunk_class<2>(a, H, nsb, sample_phase, stream); break;
+    case 3: launch_chunk_class<3>(a, H, nsb, sample_phase, stream); break;
+    default: launch_chunk_class<4>(a, H, nsb, sample_phase, stream); break;
   }
 }
 
@@ -529,6 +789,7 @@ hipError_t launch_scan_topk(const uint32_t* planes, const float* lo, const float
   a.ldw = ldw;
   a.nwords = static_cast<int>((n + 31) / 32);
   a.group = group;
+  a.tiles = (a.nwords + kTileWords - 1) / kTileWords;
   a.theta = ws.theta;
   a.count = ws.count;
   a.sample = ws.sample;
@@ -553,8 +814,14 @@ hipError_t launch_scan_topk(const uint32_t* planes, const float* lo, const float
   if (rsel < rmin) rsel = rmin;
   if (rsel > svalid) rsel = svalid;
 
+  // main-kernel work split: one resident workgroup per CU (the LUT fills LDS)
   const int full = group / kQueryChunk;
   const int rest = group % kQueryChunk;
+  const int64_t chunk_count = int64_t(H) * (full + (rest > 0 ? 1 : 0));
+  const int64_t total_tiles = chunk_count * a.tiles;
+  const int64_t target_wgs = 256;
+  a.tiles_per_wg = static_cast<int>((total_tiles + target_wgs - 1) / target_wgs);
+  if (a.tiles_per_wg < 1) a.tiles_per_wg = 1;
 
   for (int phase = 0; phase < 2; ++phase) {
     const bool sample_phase = phase == 0;
@@ -563,26 +830,23 @@ hipError_t launch_scan_topk(const uint32_t* planes, const float* lo, const float
       ScanArgs b = a;
       b.cph = full;
       b.qoff = 0;
-      hipError_t e = launch_class(kQueryChunk, b, H, nsb, timing, sample_phase, stream);
-      if (e != hipSuccess) return e;
+      launch_class(kQueryChunk, b, H, nsb, sample_phase, stream);
     }
     if (rest > 0) {
       ScanArgs b = a;
       b.cph = 1;
       b.qoff = full * kQueryChunk;
-      hipError_t e = launch_class(rest, b, H, nsb, timing, sample_phase, stream);
-      if (e != hipSuccess) return e;
+      launch_class(rest, b, H, nsb, sample_phase, stream);
     }
     if (!sample_phase && timing && timing->stop) (void)hipEventRecord(timing->stop, stream);
     if (sample_phase) {
-      hipLaunchKernelGGL(scan_threshold_kernel, dim3(num_q), dim3(kThresholdThreads), 0, stream,
-                         ws.sample, nsb * kSampleBlockKeys, static_cast<uint32_t>(rsel), ws.theta,
-                         ws.count);
-      hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(scan_threshold_kernel, dim3(num_q), dim3(kSelectThreads), 0, stream, ws.sample,
+                         nsb * kSampleBlockKeys, static_cast<uint32_t>(rsel), ws.theta, ws.count);
     }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(scan_merge_kernel, dim3(num_q), dim3(kMergeThreads), 0, stream, a, k, out_idx,
+  hipLaunchKernelGGL(scan_merge_kernel, dim3(num_q), dim3(kSelectThreads), 0, stream, a, k, out_idx,
                      out_score);
   return hipGetLastError();
 }
