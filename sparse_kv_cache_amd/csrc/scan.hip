@@ -82,6 +82,8 @@ struct UnionLds {
   double cpart[2][GQ];
   float C[GQ];
   float theta[GQ];
+  uint32_t tally[4];    // candidates of the current tile per query (main kernel)
+  uint32_t base[4];     // their first slot in the candidate list
   int U;
 };
 
@@ -440,7 +442,7 @@ __device__ __forceinline__ void load_chunk(const char* head, const UnionLds<GQ>&
                                            uint32_t woff, uint32_t (&x)[8]) {
 #pragma unroll
   for (int t = 0; t < kChunk; ++t)
-    x[t] = *reinterpret_cast<const uint32_t*>(head + s.rowoff[m * kChunk + t] + woff);
+    x[t] = *reinterpret_cast<const uint32_t*>(head + (s.rowoff[m * kChunk + t] + woff));
 }
 
 // Accumulates a pair of chunks (m, m+1) for this lane's 16 keys.  Two lanes
@@ -478,7 +480,10 @@ __global__ __launch_bounds__(kMainThreads) void scan_main_kernel(ScanArgs a) {
   UnionLds<GQ>& s = S.u;
   const int h = blockIdx.y / a.cph;
   const int q0 = h * a.group + a.qoff + (blockIdx.y % a.cph) * kQueryChunk;
-  if (threadIdx.x < GQ) s.theta[threadIdx.x] = a.theta[q0 + threadIdx.x];
+  if (threadIdx.x < GQ) {
+    s.theta[threadIdx.x] = a.theta[q0 + threadIdx.x];
+    s.tally[threadIdx.x] = 0u;
+  }
   build_union<GQ>(a, h, q0, s);
 
   const int lane = threadIdx.x & 63;
@@ -558,29 +563,47 @@ __global__ __launch_bounds__(kMainThreads) void scan_main_kernel(ScanArgs a) {
         for (int b = 0; b < 16; ++b)
           if (b < nvalid) a.all_scores[int64_t(q0 + g) * a.n + key0 + b] = acc[b][g];
     }
+    // Per query: each lane's passing keys -> wave prefix sum -> the wave's
+    // count goes to the workgroup's LDS tally (its offset there comes back),
+    // then one global atomic per (workgroup, query) reserves the slots.
+    uint32_t bits[GQ], lane_off[GQ], wave_off[GQ];
 #pragma unroll
     for (int g = 0; g < GQ; ++g) {
       const float th = s.theta[g];
-      uint32_t bits = 0;
+      uint32_t bm = 0;
 #pragma unroll
-      for (int b = 0; b < 16; ++b) bits |= (b < nvalid && acc[b][g] >= th) ? (1u << b) : 0u;
-      const uint32_t mine = __popc(bits);
+      for (int b = 0; b < 16; ++b) bm |= (b < nvalid && acc[b][g] >= th) ? (1u << b) : 0u;
+      bits[g] = bm;
+      const uint32_t mine = __popc(bm);
       uint32_t incl = mine;
 #pragma unroll
       for (int d = 1; d < 64; d <<= 1) {
         const uint32_t o = __shfl_up(incl, d);
         if (lane >= d) incl += o;
       }
+      lane_off[g] = incl - mine;
       const uint32_t total = __shfl(incl, 63);
-      if (total == 0) continue;                       // uniform
-      uint32_t base = 0;
-      if (lane == 0) base = atomicAdd(&a.count[q0 + g], total);
-      uint32_t slot = __shfl(base, 0) + incl - mine;
+      uint32_t off = 0;
+      if (lane == 0 && total != 0) off = atomicAdd(&s.tally[g], total);
+      wave_off[g] = __shfl(off, 0);
+    }
+    __syncthreads();
+    if (threadIdx.x < GQ) {
+      // no wave touches tally between these two barriers, so it is reset here
+      const uint32_t t = s.tally[threadIdx.x];
+      s.tally[threadIdx.x] = 0u;
+      s.base[threadIdx.x] = t ? atomicAdd(&a.count[q0 + threadIdx.x], t) : 0u;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int g = 0; g < GQ; ++g) {
+      if (bits[g] == 0) continue;
+      uint32_t slot = s.base[g] + wave_off[g] + lane_off[g];
       // static key index: a computed index into acc would move the whole
       // accumulator array to scratch memory
 #pragma unroll
       for (int b = 0; b < 16; ++b) {
-        if (bits & (1u << b)) {
+        if (bits[g] & (1u << b)) {
           if (slot < static_cast<uint32_t>(kCandCap))
             a.cand[int64_t(q0 + g) * kCandCap + slot] =
                 make_uint2(__float_as_uint(acc[b][g]), static_cast<uint32_t>(key0 + b));
