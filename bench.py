@@ -14,7 +14,6 @@ Prints one JSON line (see the repository's design notes for the fields).
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -32,14 +31,6 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_main_qwen3_8b_1m_traffic.jso
 
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
-
-
-def source_digest() -> str:
-    h = hashlib.sha256()
-    for f in ("scan.hip", "fathom_internal.h"):
-        with open(os.path.join(ROOT, "sparse_kv_cache_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
 
 
 def union_bytes(alloc: np.ndarray, group: int, ldw: int) -> int:
@@ -111,6 +102,7 @@ def main():
     import torch
     from sparse_kv_cache_amd import fathom as fa
     from sparse_kv_cache_amd import synth
+    from sparse_kv_cache_amd.profiling import source_digest
 
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
@@ -168,7 +160,7 @@ def main():
         src = torch.ones(nel, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
-            dst.copy_(src)
+            torch.mul(src, 1.0, out=dst)   # one elementwise kernel: reads and writes nel*4 bytes
         torch.cuda.synchronize()
         log(f"calibration copy: {args.calibrate_copy_mib} MiB read + written per launch, 3 launches")
 

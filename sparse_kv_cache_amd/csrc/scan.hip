@@ -34,6 +34,8 @@
 // 8 bits form one byte, and adds one table entry per key.  No MFMA: the work
 // is a bit-sliced gather-accumulate, bound by VALU and LDS gathers.
 
+#include <hip/hip_ext.h>
+
 #include "fathom_internal.h"
 
 namespace fathom {
@@ -93,16 +95,83 @@ __device__ inline int lanes_below(uint64_t mask) {
   return __popcll(mask & below);
 }
 
+// ------------------------------------------------ wavefront primitives
+// Cross-lane steps use DPP (operand routing inside the VALU instruction)
+// rather than ds_bpermute, whose LDS round trip is ~100 cycles per step.
+// GFX9 DPP controls: quad_perm, row_shr:n, row_mirror, row_half_mirror,
+// row_bcast:15 / row_bcast:31 (rows are 16 lanes).
+constexpr int kDppXor1 = 0xB1;          // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;          // quad_perm [2,3,0,1]
+constexpr int kDppRowShr = 0x110;       // + n: row_shr:n
+constexpr int kDppRowMirror = 0x140;
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowBcast15 = 0x142;
+constexpr int kDppRowBcast31 = 0x143;
+
+template <int Ctrl, int RowMask = 0xf>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(old), static_cast<int>(v), Ctrl,
+                                                           RowMask, 0xf, false));
+}
+
+template <int Ctrl, int RowMask = 0xf>
+__device__ __forceinline__ double dpp_f64(double old, double v) {
+  const uint64_t o = __builtin_bit_cast(uint64_t, old), x = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = dpp_u32<Ctrl, RowMask>(static_cast<uint32_t>(o), static_cast<uint32_t>(x));
+  const uint32_t hi = dpp_u32<Ctrl, RowMask>(static_cast<uint32_t>(o >> 32), static_cast<uint32_t>(x >> 32));
+  return __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// Inclusive prefix sum over the wavefront's 64 lanes.
+__device__ __forceinline__ uint32_t wave_incl_sum(uint32_t v) {
+  v += dpp_u32<kDppRowShr + 1>(0u, v);
+  v += dpp_u32<kDppRowShr + 2>(0u, v);
+  v += dpp_u32<kDppRowShr + 4>(0u, v);
+  v += dpp_u32<kDppRowShr + 8>(0u, v);
+  v += dpp_u32<kDppRowBcast15, 0xa>(0u, v);
+  v += dpp_u32<kDppRowBcast31, 0xc>(0u, v);
+  return v;
+}
+
+__device__ __forceinline__ uint32_t read_lane(uint32_t v, int lane) {
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), lane));
+}
+
+// Max and min over the wavefront, returned to every lane.
+__device__ __forceinline__ uint2 wave_max_min(uint32_t mx, uint32_t mn) {
+  mx = max(mx, dpp_u32<kDppXor1>(mx, mx));
+  mn = min(mn, dpp_u32<kDppXor1>(mn, mn));
+  mx = max(mx, dpp_u32<kDppXor2>(mx, mx));
+  mn = min(mn, dpp_u32<kDppXor2>(mn, mn));
+  mx = max(mx, dpp_u32<kDppRowHalfMirror>(mx, mx));
+  mn = min(mn, dpp_u32<kDppRowHalfMirror>(mn, mn));
+  mx = max(mx, dpp_u32<kDppRowMirror>(mx, mx));
+  mn = min(mn, dpp_u32<kDppRowMirror>(mn, mn));
+  mx = max(mx, dpp_u32<kDppRowBcast15, 0xa>(mx, mx));
+  mn = min(mn, dpp_u32<kDppRowBcast15, 0xa>(mn, mn));
+  mx = max(mx, dpp_u32<kDppRowBcast31, 0xc>(mx, mx));
+  mn = min(mn, dpp_u32<kDppRowBcast31, 0xc>(mn, mn));
+  return make_uint2(read_lane(mx, 63), read_lane(mn, 63));
+}
+
+// Sum over the wavefront (lane 63 ends with the total; returned to all).
+__device__ __forceinline__ double wave_sum(double v) {
+  v += dpp_f64<kDppXor1>(0.0, v);
+  v += dpp_f64<kDppXor2>(0.0, v);
+  v += dpp_f64<kDppRowHalfMirror>(0.0, v);
+  v += dpp_f64<kDppRowMirror>(0.0, v);
+  v += dpp_f64<kDppRowBcast15, 0xa>(0.0, v);
+  v += dpp_f64<kDppRowBcast31, 0xc>(0.0, v);
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = read_lane(static_cast<uint32_t>(b), 63), hi = read_lane(static_cast<uint32_t>(b >> 32), 63);
+  return __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
+}
+
 __device__ inline double pow2_3_minus(int b) {
   // 2^(3 - b) for b in 0..4
   return b == 0 ? 8.0 : b == 1 ? 4.0 : b == 2 ? 2.0 : b == 3 ? 1.0 : 0.5;
 }
 
-__device__ inline double wave_sum(double v) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d);
-  return v;
-}
 
 // Builds the union plane list of a query chunk (queries q0 .. q0+GQ-1 on
 // KV head h), the per-plane weights and the score offsets C_q.
@@ -143,16 +212,11 @@ __device__ void build_union(const ScanArgs& a, int h, int q0, UnionLds<GQ>& s) {
     int base = 0;
     for (int j = 0; j < kPlanes; ++j) {
       const int v0 = s.u[2 * t] > j, v1 = s.u[2 * t + 1] > j;
-      int incl = v0 + v1;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int o = __shfl_up(incl, d);
-        if (t >= d) incl += o;
-      }
+      const int incl = static_cast<int>(wave_incl_sum(static_cast<uint32_t>(v0 + v1)));
       const int excl = base + incl - v0 - v1;
       s.off[j][2 * t] = excl;
       s.off[j][2 * t + 1] = excl + v0;
-      base += __shfl(incl, 63);
+      base += static_cast<int>(read_lane(static_cast<uint32_t>(incl), 63));
     }
     if (t == 0) s.U = base;
   }
@@ -201,20 +265,26 @@ __global__ __launch_bounds__(kSampleThreads) void scan_sample_kernel(ScanArgs a)
   const int64_t word0 = int64_t(sbi) * a.sample_stride * (kSampleBlockKeys / 32) + part * kWords;
   const char* head = reinterpret_cast<const char*>(a.planes + int64_t(h) * kD * kPlanes * a.ldw);
   const int U = s.U;
-  // every thread issues all of its staging loads before the first store
+  // Every thread issues all of its staging loads before the first store, and
+  // no load is conditional (a load under a branch makes the compiler wait for
+  // it before the branch ends, turning the batch into a chain of round trips):
+  // entries past the union read row 0 and words past the row read its last
+  // word; both are ignored later.
   constexpr int kPer = (kMaxUnion * kWords + kSampleThreads - 1) / kSampleThreads;
+  static_assert(kPer * kSampleThreads == kMaxUnion * kWords, "staging covers the stage exactly");
   uint32_t tmp[kPer];
 #pragma unroll
   for (int r = 0; r < kPer; ++r) {
     const int i = threadIdx.x + r * kSampleThreads;
     const int p = i / kWords, wd = i % kWords;
-    const int64_t w = word0 + wd;
-    tmp[r] = (p < U && w < a.ldw) ? *reinterpret_cast<const uint32_t*>(head + s.rowoff[p] + w * 4) : 0u;
+    const int64_t w = min<int64_t>(word0 + wd, a.ldw - 1);
+    const uint32_t ro = p < U ? s.rowoff[p] : 0u;
+    tmp[r] = *reinterpret_cast<const uint32_t*>(head + ro + w * 4);
   }
 #pragma unroll
   for (int r = 0; r < kPer; ++r) {
     const int i = threadIdx.x + r * kSampleThreads;
-    if (i / kWords < U) stage[i / kWords][i % kWords] = tmp[r];
+    stage[i / kWords][i % kWords] = tmp[r];
   }
   __syncthreads();
   const int64_t key = word0 * 32 + threadIdx.x;
@@ -223,13 +293,15 @@ __global__ __launch_bounds__(kSampleThreads) void scan_sample_kernel(ScanArgs a)
   float acc[GQ];
 #pragma unroll
   for (int g = 0; g < GQ; ++g) acc[g] = 0.0f;
+  // branch-free: a query that skips plane p has weight 0 there, and a
+  // uniform branch per plane would serialize the LDS reads of the loop
 #pragma unroll 8
   for (int p = 0; p < U; ++p) {
     const float f = static_cast<float>((stage[p][wsel] >> sh) & 1u);
-    const uint32_t m = s.mask[p];
+    const float4 w = *reinterpret_cast<const float4*>(&s.w[p][0]);
+    const float wg[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-    for (int g = 0; g < GQ; ++g)
-      if (m & (1u << g)) acc[g] = fmaf(f, s.w[p][g], acc[g]);
+    for (int g = 0; g < GQ; ++g) acc[g] = fmaf(f, wg[g], acc[g]);
   }
   const int local = part * kSampleThreads + threadIdx.x;   // 0..1023 within the block
 #pragma unroll
@@ -263,12 +335,7 @@ __device__ uint2 select_bin(SelectLds& L, uint32_t r) {
     uint32_t c[4], own = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) { c[j] = L.total[255 - 4 * lane - j]; own += c[j]; }
-    uint32_t incl = own;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const uint32_t o = __shfl_up(incl, d);
-      if (lane >= d) incl += o;
-    }
+    const uint32_t incl = wave_incl_sum(own);
     uint32_t before = incl - own;   // count in the bins above this lane's bins
     if (before < r && incl >= r) {
 #pragma unroll
@@ -293,19 +360,73 @@ __device__ inline void clear_hist(SelectLds& L) {
   __syncthreads();
 }
 
-// r-th largest (1-based) of the ordered keys v[j] held by the block's threads
-// (value j of thread t is element t + j*blockDim.x, present when < count).
-// Returns (key, r minus the number of values strictly above the key).
+// Adds one to bin `bin` of this wave's histogram for every lane with `on`.
+// When all such lanes share one bin (common in the leading digits, where the
+// values agree) a single atomic adds the whole count.
+__device__ inline void hist_add(uint32_t* wave_hist, bool on, uint32_t bin) {
+  if (!on) return;
+  // exec now holds exactly the lanes with `on`
+  const uint32_t lead = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(bin)));
+  const uint64_t act = __ballot(1);
+  if (__ballot(bin == lead) == act) {
+    if ((threadIdx.x & 63) == __ffsll(static_cast<long long>(act)) - 1)
+      atomicAdd(&wave_hist[lead], static_cast<uint32_t>(__popcll(act)));
+  } else {
+    atomicAdd(&wave_hist[bin], 1u);
+  }
+}
+
+// Block-wide max and min of the present values (ordered keys).
+template <int PT>
+__device__ uint2 block_max_min(const uint32_t (&v)[PT], uint32_t count, SelectLds& L) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t mx = 0u, mn = 0xffffffffu;
+#pragma unroll
+  for (int j = 0; j < PT; ++j) {
+    const uint32_t i = tid + j * blockDim.x;
+    if (i < count) {
+      mx = max(mx, v[j]);
+      mn = min(mn, v[j]);
+    }
+  }
+  const uint2 w = wave_max_min(mx, mn);
+  mx = w.x;
+  mn = w.y;
+  if (lane == 0) {
+    L.hist[wave][0] = mx;
+    L.hist[wave][1] = mn;
+  }
+  __syncthreads();
+  mx = 0u;
+  mn = 0xffffffffu;
+  for (int w = 0; w < static_cast<int>(blockDim.x >> 6); ++w) {
+    mx = max(mx, L.hist[w][0]);
+    mn = min(mn, L.hist[w][1]);
+  }
+  __syncthreads();
+  return make_uint2(mx, mn);
+}
+
+// r-th largest (1-based, r <= count) of the ordered keys v[j] held by the
+// block's threads (value j of thread t is element t + j*blockDim.x, present
+// when < count).  Returns (key, r minus the number of values strictly above
+// the key).  Radix select, 8 bits per pass, starting at the highest byte in
+// which the present values differ.
 template <int PT>
 __device__ uint2 block_select_regs(const uint32_t (&v)[PT], uint32_t count, uint32_t r, SelectLds& L) {
   const int tid = threadIdx.x, wave = tid >> 6;
-  uint32_t prefix = 0, pmask = 0;
-  for (int shift = 24; shift >= 0; shift -= 8) {
+  const uint2 mm = block_max_min<PT>(v, count, L);
+  const uint32_t diff = mm.x ^ mm.y;
+  if (diff == 0) return make_uint2(mm.x, r);          // all present values equal
+  const int top = (31 - __clz(diff)) & ~7;             // shift of the highest differing byte
+  uint32_t pmask = top == 24 ? 0u : (0xffffffffu << (top + 8));
+  uint32_t prefix = mm.x & pmask;
+  for (int shift = top; shift >= 0; shift -= 8) {
     clear_hist(L);
 #pragma unroll
     for (int j = 0; j < PT; ++j) {
       const uint32_t i = tid + j * blockDim.x;
-      if (i < count && (v[j] & pmask) == prefix) atomicAdd(&L.hist[wave][(v[j] >> shift) & 255u], 1u);
+      hist_add(L.hist[wave], i < count && (v[j] & pmask) == prefix, (v[j] >> shift) & 255u);
     }
     __syncthreads();
     const uint2 b = select_bin(L, r);
@@ -314,6 +435,68 @@ __device__ uint2 block_select_regs(const uint32_t (&v)[PT], uint32_t count, uint
     r = b.y;
   }
   return make_uint2(prefix, r);
+}
+
+// ------------------------------------------------- one-pass digit select
+// An 11-bit digit taken just below the highest bit in which the present
+// values differ splits them into 2048 ordered buckets; one histogram and one
+// descending scan give every bucket's first rank and the bucket holding a
+// given rank.  Used for the threshold estimate (two passes) and for the
+// candidate merge, which then orders each small bucket by counting.
+
+constexpr int kDigitBits = 11;
+constexpr int kBins = 1 << kDigitBits;
+constexpr int kBucketMax = 64;          // largest bucket the merge orders by counting
+static_assert(kBins == 2 * kSelectThreads, "the scan gives each thread two bins");
+
+struct DigitLds {
+  uint32_t hist[kBins];     // elements per bucket
+  uint32_t start[kBins];    // elements in the buckets above
+  uint32_t cursor[kBins];   // scatter cursors
+  uint32_t wave_total[kSelectWaves];
+  uint32_t bstar;           // bucket holding the searched rank
+  uint32_t bstart;          // its first rank
+  uint32_t bcount;          // its size
+  uint32_t big;             // a bucket at or above it exceeds kBucketMax
+};
+
+// Zeroes the histogram and cursors (a barrier must follow before use).
+__device__ inline void digit_clear(DigitLds& D) {
+  for (int i = threadIdx.x; i < kBins; i += blockDim.x) {
+    D.hist[i] = 0u;
+    D.cursor[i] = 0u;
+  }
+  if (threadIdx.x == 0) D.big = 0u;
+}
+
+// Descending exclusive scan of the histogram and the bucket holding the
+// element of 0-based rank r (r < total).  Needs blockDim.x == kBins / 2;
+// begins after the histogram's barrier and ends with a barrier.
+__device__ void digit_scan(DigitLds& D, uint32_t r) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int bh = kBins - 1 - 2 * t, bl = bh - 1;     // descending across threads
+  const uint32_t ch = D.hist[bh], cl = D.hist[bl], own = ch + cl;
+  const uint32_t incl = wave_incl_sum(own);
+  if (lane == 63) D.wave_total[wave] = incl;
+  __syncthreads();
+  uint32_t base = 0;
+  for (int w = 0; w < wave; ++w) base += D.wave_total[w];
+  const uint32_t excl = base + incl - own;
+  D.start[bh] = excl;
+  D.start[bl] = excl + ch;
+  if (excl <= r && r < excl + ch) {
+    D.bstar = static_cast<uint32_t>(bh);
+    D.bstart = excl;
+    D.bcount = ch;
+  } else if (excl + ch <= r && r < excl + own) {
+    D.bstar = static_cast<uint32_t>(bl);
+    D.bstart = excl + ch;
+    D.bcount = cl;
+  }
+  if ((excl <= r && ch > static_cast<uint32_t>(kBucketMax)) ||
+      (excl + ch <= r && cl > static_cast<uint32_t>(kBucketMax)))
+    D.big = 1u;
+  __syncthreads();
 }
 
 // Same, over values produced on demand by get(i) for i < count.
@@ -338,21 +521,60 @@ __device__ uint2 block_select_fn(int64_t count, uint32_t r, SelectLds& L, Get ge
 
 // --------------------------------------------------------------- threshold
 
+// Per query: a score with about rsel sampled scores at or above it.  Two
+// digit passes (22 bits below the highest differing bit) locate the bucket
+// of the rsel-th largest sample; theta is that bucket's lowest value, so at
+// least rsel sampled keys score >= theta.
 __global__ __launch_bounds__(kSelectThreads) void scan_threshold_kernel(
     const float* __restrict__ sample, int stot, uint32_t rsel, float* __restrict__ theta,
     uint32_t* __restrict__ count) {
   __shared__ SelectLds L;
+  __shared__ DigitLds D;
   constexpr int PT = kSampleMaxKeys / kSelectThreads;
+  static_assert(PT * kSelectThreads == kSampleMaxKeys, "one register per sample slot");
   const int q = blockIdx.x;
+  const int tid = threadIdx.x;
   uint32_t v[PT];
+  // unconditional loads (the sample rows are allocated in full); slots past
+  // the sample are masked afterwards
+#pragma unroll
+  for (int j = 0; j < PT; ++j) v[j] = __float_as_uint(sample[int64_t(q) * kSampleMaxKeys + tid + j * kSelectThreads]);
 #pragma unroll
   for (int j = 0; j < PT; ++j) {
-    const int i = threadIdx.x + j * kSelectThreads;
-    v[j] = i < stot ? float_to_ordered(sample[int64_t(q) * kSampleMaxKeys + i]) : 0u;
+    const int i = tid + j * kSelectThreads;
+    v[j] = i < stot ? float_to_ordered(__uint_as_float(v[j])) : 0u;
   }
-  const uint2 sel = block_select_regs<PT>(v, static_cast<uint32_t>(stot), rsel, L);
-  if (threadIdx.x == 0) {
-    theta[q] = ordered_to_float(sel.x);
+  digit_clear(D);
+  const uint2 mm = block_max_min<PT>(v, static_cast<uint32_t>(stot), L);
+  uint32_t th = mm.x;
+  if (mm.x != mm.y) {
+    uint32_t r = rsel - 1u;
+    int hi = 32 - __clz(mm.x ^ mm.y);                // bits >= hi are common
+    uint32_t pmask = hi >= 32 ? 0u : ~((1u << hi) - 1u);
+    uint32_t prefix = mm.x & pmask;
+    for (int pass = 0; pass < 2 && hi > 0; ++pass) {
+      const int width = min(kDigitBits, hi), shift = hi - width;
+      const uint32_t dmask = (1u << width) - 1u;
+#pragma unroll
+      for (int j = 0; j < PT; ++j) {
+        const int i = tid + j * kSelectThreads;
+        hist_add(D.hist, i < stot && (v[j] & pmask) == prefix, (v[j] >> shift) & dmask);
+      }
+      __syncthreads();
+      digit_scan(D, r);
+      prefix |= D.bstar << shift;
+      pmask |= dmask << shift;
+      r -= D.bstart;
+      hi = shift;
+      // each thread clears the two bins it scanned; nobody reads them again
+      D.hist[kBins - 1 - 2 * tid] = 0u;
+      D.hist[kBins - 2 - 2 * tid] = 0u;
+      __syncthreads();
+    }
+    th = prefix;   // lowest value of the bucket: the low bits are zero
+  }
+  if (tid == 0) {
+    theta[q] = ordered_to_float(th);
     count[q] = 0u;
   }
 }
@@ -575,17 +797,12 @@ __global__ __launch_bounds__(kMainThreads) void scan_main_kernel(ScanArgs a) {
       for (int b = 0; b < 16; ++b) bm |= (b < nvalid && acc[b][g] >= th) ? (1u << b) : 0u;
       bits[g] = bm;
       const uint32_t mine = __popc(bm);
-      uint32_t incl = mine;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const uint32_t o = __shfl_up(incl, d);
-        if (lane >= d) incl += o;
-      }
+      const uint32_t incl = wave_incl_sum(mine);
       lane_off[g] = incl - mine;
-      const uint32_t total = __shfl(incl, 63);
+      const uint32_t total = read_lane(incl, 63);
       uint32_t off = 0;
       if (lane == 0 && total != 0) off = atomicAdd(&s.tally[g], total);
-      wave_off[g] = __shfl(off, 0);
+      wave_off[g] = read_lane(off, 0);
     }
     __syncthreads();
     if (threadIdx.x < GQ) {
@@ -616,25 +833,94 @@ __global__ __launch_bounds__(kMainThreads) void scan_main_kernel(ScanArgs a) {
 
 // ------------------------------------------------------------------- merge
 
+// The fast merge path keeps at most k - 1 + kBucketMax keys at the front of
+// the sort buffer; its digit tables live behind them.
+constexpr int kFastKept = 8192;
+static_assert(kMaxK - 1 + kBucketMax <= kFastKept, "kept keys stay in front of the digit tables");
+static_assert(kFastKept * 8 + sizeof(DigitLds) <= kCandCap * 8, "digit tables fit in the sort buffer");
+
 __device__ inline unsigned long long sort_key(uint32_t ordered, uint32_t idx) {
   return (static_cast<unsigned long long>(ordered) << 32) | static_cast<uint32_t>(~idx);
 }
 
-// Descending bitonic sort of N (power of two) 64-bit keys in LDS.
-__device__ void bitonic_sort_desc(unsigned long long* keys, unsigned N) {
+// Descending bitonic sort of N = kSelectThreads * E 64-bit keys, held E per
+// thread in blocked order (thread t holds elements tE .. tE+E-1).  A
+// compare-exchange at stride s runs in registers when s < E, between the
+// lanes of a wavefront (ds_bpermute) when s < 64E, and through LDS (buf, N
+// keys) otherwise, where consecutive large strides of one merge share a
+// single write-back of the registers.
+template <int E>
+__device__ void sort_regs_desc(unsigned long long (&x)[E], unsigned long long* buf) {
+  constexpr unsigned N = kSelectThreads * E;
+  const unsigned t = threadIdx.x;
   for (unsigned size = 2; size <= N; size <<= 1) {
-    for (unsigned stride = size >> 1; stride > 0; stride >>= 1) {
-      for (unsigned t = threadIdx.x; t < N / 2; t += blockDim.x) {
-        const unsigned lo_i = 2 * t - (t & (stride - 1));
-        const unsigned hi_i = lo_i + stride;
-        const bool desc = (lo_i & size) == 0;
-        const unsigned long long x = keys[lo_i], y = keys[hi_i];
-        if ((x < y) == desc) {
-          keys[lo_i] = y;
-          keys[hi_i] = x;
+    unsigned stride = size >> 1;
+    if (stride >= 64u * E) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) buf[t * E + e] = x[e];
+      __syncthreads();
+      for (; stride >= 64u * E; stride >>= 1) {
+        for (unsigned r = t; r < N / 2; r += kSelectThreads) {
+          const unsigned lo_i = 2 * r - (r & (stride - 1));
+          const unsigned hi_i = lo_i + stride;
+          const bool desc = (lo_i & size) == 0;
+          const unsigned long long a = buf[lo_i], b = buf[hi_i];
+          if ((a < b) == desc) {
+            buf[lo_i] = b;
+            buf[hi_i] = a;
+          }
+        }
+        __syncthreads();
+      }
+      // each thread reads back only its own elements, which no other thread
+      // writes before the next barrier
+#pragma unroll
+      for (int e = 0; e < E; ++e) x[e] = buf[t * E + e];
+    }
+    for (; stride >= static_cast<unsigned>(E); stride >>= 1) {
+      const int m = static_cast<int>(stride / E);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const unsigned i = t * E + e;
+        const unsigned long long y = __shfl_xor(x[e], m);
+        const bool keep_max = ((i & size) == 0) == ((i & stride) == 0);
+        x[e] = keep_max ? (x[e] > y ? x[e] : y) : (x[e] < y ? x[e] : y);
+      }
+    }
+#pragma unroll
+    for (int sr = E / 2; sr >= 1; sr >>= 1) {
+      if (static_cast<unsigned>(sr) < size) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          if (e & sr) continue;
+          const unsigned i = t * E + e;
+          const bool desc = (i & size) == 0;
+          const unsigned long long a = x[e], b = x[e | sr];
+          const unsigned long long hi = a > b ? a : b, lo = a > b ? b : a;
+          x[e] = desc ? hi : lo;
+          x[e | sr] = desc ? lo : hi;
         }
       }
-      __syncthreads();
+    }
+  }
+}
+
+// Sorts the first `kept` keys of buf (descending) and writes the first k.
+template <int E>
+__device__ void sort_and_write(unsigned long long* buf, unsigned kept, int k, int q,
+                               int32_t* __restrict__ out_idx, float* __restrict__ out_score) {
+  unsigned long long x[E];
+  const unsigned t = threadIdx.x;
+#pragma unroll
+  for (int e = 0; e < E; ++e) x[e] = t * E + e < kept ? buf[t * E + e] : 0ull;
+  __syncthreads();
+  sort_regs_desc<E>(x, buf);
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const unsigned i = t * E + e;
+    if (i < static_cast<unsigned>(k)) {
+      out_idx[int64_t(q) * k + i] = static_cast<int32_t>(~static_cast<uint32_t>(x[e]));
+      out_score[int64_t(q) * k + i] = ordered_to_float(static_cast<uint32_t>(x[e] >> 32));
     }
   }
 }
@@ -675,41 +961,88 @@ __global__ __launch_bounds__(kSelectThreads) void scan_merge_kernel(ScanArgs a, 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const uint32_t cnt = a.count[q];
-  unsigned N;
+  unsigned kept;
 
   if (cnt >= static_cast<uint32_t>(k) && cnt <= static_cast<uint32_t>(kCandCap)) {
     const uint2* cand = a.cand + int64_t(q) * kCandCap;
+    static_assert(PT * kSelectThreads == kCandCap, "one register per candidate slot");
     uint32_t v[PT], id[PT];
+    // unconditional loads (the list is allocated to its capacity), masked after
+#pragma unroll
+    for (int j = 0; j < PT; ++j) {
+      const uint2 e = cand[tid + j * kSelectThreads];
+      v[j] = e.x;
+      id[j] = e.y;
+    }
 #pragma unroll
     for (int j = 0; j < PT; ++j) {
       const uint32_t i = tid + j * kSelectThreads;
-      if (i < cnt) {
-        const uint2 e = cand[i];
-        v[j] = float_to_ordered(__uint_as_float(e.x));
-        id[j] = e.y;
-      } else {
-        v[j] = 0u;
-        id[j] = 0u;
+      v[j] = i < cnt ? float_to_ordered(__uint_as_float(v[j])) : 0u;
+    }
+    // Fast path: one digit pass puts the candidates into ordered buckets;
+    // those at or above the bucket holding rank k-1 are scattered in bucket
+    // order and each is placed by counting the larger keys of its bucket.
+    DigitLds& D = *reinterpret_cast<DigitLds*>(keys + kFastKept);
+    digit_clear(D);
+    const uint2 mm = block_max_min<PT>(v, cnt, L);
+    bool placed = false;
+    if (mm.x != mm.y) {
+      const int hi = 32 - __clz(mm.x ^ mm.y);
+      const int width = min(kDigitBits, hi), shift = hi - width;
+      const uint32_t dmask = (1u << width) - 1u;
+#pragma unroll
+      for (int j = 0; j < PT; ++j) {
+        const uint32_t i = tid + j * kSelectThreads;
+        hist_add(D.hist, i < cnt, (v[j] >> shift) & dmask);
+      }
+      __syncthreads();
+      digit_scan(D, static_cast<uint32_t>(k) - 1u);
+      if (D.big == 0u) {
+        const uint32_t bstar = D.bstar;
+        const uint32_t nkeep = D.bstart + D.bcount;   // <= k - 1 + kBucketMax
+#pragma unroll
+        for (int j = 0; j < PT; ++j) {
+          const uint32_t i = tid + j * kSelectThreads;
+          const uint32_t d = (v[j] >> shift) & dmask;
+          if (i < cnt && d >= bstar) keys[D.start[d] + atomicAdd(&D.cursor[d], 1u)] = sort_key(v[j], id[j]);
+        }
+        __syncthreads();
+        for (uint32_t p = tid; p < nkeep; p += kSelectThreads) {
+          const unsigned long long key = keys[p];
+          const uint32_t d = (static_cast<uint32_t>(key >> 32) >> shift) & dmask;
+          const uint32_t b0 = D.start[d], c = D.hist[d];
+          uint32_t rank = 0;
+          for (uint32_t i = 0; i < c; ++i) rank += keys[b0 + i] > key ? 1u : 0u;
+          const uint32_t pos = b0 + rank;
+          if (pos < static_cast<uint32_t>(k)) {
+            out_idx[int64_t(q) * k + pos] = static_cast<int32_t>(~static_cast<uint32_t>(key));
+            out_score[int64_t(q) * k + pos] = ordered_to_float(static_cast<uint32_t>(key >> 32));
+          }
+        }
+        placed = true;
       }
     }
-    // the k-th best candidate score; keep every candidate at or above it
+    if (placed) return;
+    // General path (all scores equal, or a bucket too large to order by
+    // counting): the k-th best candidate score by radix select; every
+    // candidate at or above it is kept and sorted.
     const uint2 sel = block_select_regs<PT>(v, cnt, static_cast<uint32_t>(k), L);
     if (tid == 0) s_count[0] = 0;
     __syncthreads();
+    // compaction: one LDS atomic per wave and register slot
 #pragma unroll
     for (int j = 0; j < PT; ++j) {
       const uint32_t i = tid + j * kSelectThreads;
-      if (i < cnt && v[j] >= sel.x) {
-        const uint32_t slot = atomicAdd(&s_count[0], 1u);
-        keys[slot] = sort_key(v[j], id[j]);
-      }
+      const bool keep = i < cnt && v[j] >= sel.x;
+      const uint64_t bal = __ballot(keep);
+      if (bal == 0) continue;
+      uint32_t base = 0;
+      if (lane == 0) base = atomicAdd(&s_count[0], static_cast<uint32_t>(__popcll(bal)));
+      base = read_lane(base, 0);
+      if (keep) keys[base + lanes_below(bal)] = sort_key(v[j], id[j]);
     }
     __syncthreads();
-    const uint32_t kept = s_count[0];
-    N = 2;
-    while (N < kept) N <<= 1;
-    for (unsigned i = kept + tid; i < N; i += blockDim.x) keys[i] = 0ull;
-    __syncthreads();
+    kept = s_count[0];
   } else {
     // exact fallback: radix select over recomputed scores
     const int h = q / a.group;
@@ -762,36 +1095,45 @@ __global__ __launch_bounds__(kSelectThreads) void scan_merge_kernel(ScanArgs a, 
       eq_taken += total;
       __syncthreads();
     }
-    N = 2;
-    while (N < static_cast<unsigned>(k)) N <<= 1;
-    for (unsigned i = k + tid; i < N; i += blockDim.x) keys[i] = 0ull;
     __syncthreads();
+    kept = static_cast<unsigned>(k);
   }
-  bitonic_sort_desc(keys, N);
-  for (int i = tid; i < k; i += blockDim.x) {
-    const unsigned long long e = keys[i];
-    out_idx[int64_t(q) * k + i] = static_cast<int32_t>(~static_cast<uint32_t>(e));
-    out_score[int64_t(q) * k + i] = ordered_to_float(static_cast<uint32_t>(e >> 32));
+  // kept >= k keys in keys[0, kept): sort them and write the first k
+  if (kept <= kSelectThreads) {
+    sort_and_write<1>(keys, kept, k, q, out_idx, out_score);
+  } else if (kept <= 2 * kSelectThreads) {
+    sort_and_write<2>(keys, kept, k, q, out_idx, out_score);
+  } else if (kept <= 4 * kSelectThreads) {
+    sort_and_write<4>(keys, kept, k, q, out_idx, out_score);
+  } else if (kept <= 8 * kSelectThreads) {
+    sort_and_write<8>(keys, kept, k, q, out_idx, out_score);
+  } else {
+    sort_and_write<16>(keys, kept, k, q, out_idx, out_score);
   }
 }
 
+// Main-kernel launches may carry a start and a stop event: recorded by the
+// dispatch itself (hipExtLaunchKernelGGL), they add no packets to the stream.
 template <int GQ>
-void launch_chunk_class(const ScanArgs& a, int H, int nsb, bool sample_phase, hipStream_t stream) {
+void launch_chunk_class(const ScanArgs& a, int H, int nsb, bool sample_phase, hipEvent_t ev_start,
+                        hipEvent_t ev_stop, hipStream_t stream) {
   if (sample_phase) {
     hipLaunchKernelGGL(scan_sample_kernel<GQ>, dim3(nsb * kSampleWgPerBlock, H * a.cph),
                        dim3(kSampleThreads), 0, stream, a);
   } else {
     const int wgs = (a.tiles + a.tiles_per_wg - 1) / a.tiles_per_wg;
-    hipLaunchKernelGGL(scan_main_kernel<GQ>, dim3(wgs, H * a.cph), dim3(kMainThreads), 0, stream, a);
+    hipExtLaunchKernelGGL(scan_main_kernel<GQ>, dim3(wgs, H * a.cph), dim3(kMainThreads), 0, stream,
+                          ev_start, ev_stop, 0, a);
   }
 }
 
-void launch_class(int gq, const ScanArgs& a, int H, int nsb, bool sample_phase, hipStream_t stream) {
+void launch_class(int gq, const ScanArgs& a, int H, int nsb, bool sample_phase, hipEvent_t ev_start,
+                  hipEvent_t ev_stop, hipStream_t stream) {
   switch (gq) {
-    case 1: launch_chunk_class<1>(a, H, nsb, sample_phase, stream); break;
-    case 2: launch_chunk_class<2>(a, H, nsb, sample_phase, stream); break;
-    case 3: launch_chunk_class<3>(a, H, nsb, sample_phase, stream); break;
-    default: launch_chunk_class<4>(a, H, nsb, sample_phase, stream); break;
+    case 1: launch_chunk_class<1>(a, H, nsb, sample_phase, ev_start, ev_stop, stream); break;
+    case 2: launch_chunk_class<2>(a, H, nsb, sample_phase, ev_start, ev_stop, stream); break;
+    case 3: launch_chunk_class<3>(a, H, nsb, sample_phase, ev_start, ev_stop, stream); break;
+    default: launch_chunk_class<4>(a, H, nsb, sample_phase, ev_start, ev_stop, stream); break;
   }
 }
 
@@ -846,22 +1188,23 @@ hipError_t launch_scan_topk(const uint32_t* planes, const float* lo, const float
   a.tiles_per_wg = static_cast<int>((total_tiles + target_wgs - 1) / target_wgs);
   if (a.tiles_per_wg < 1) a.tiles_per_wg = 1;
 
+  // timing events: start on the first main launch, stop on the last
+  hipEvent_t ev_start = timing ? timing->start : nullptr;
+  hipEvent_t ev_stop = timing ? timing->stop : nullptr;
   for (int phase = 0; phase < 2; ++phase) {
     const bool sample_phase = phase == 0;
-    if (!sample_phase && timing && timing->start) (void)hipEventRecord(timing->start, stream);
     if (full > 0) {
       ScanArgs b = a;
       b.cph = full;
       b.qoff = 0;
-      launch_class(kQueryChunk, b, H, nsb, sample_phase, stream);
+      launch_class(kQueryChunk, b, H, nsb, sample_phase, ev_start, rest > 0 ? nullptr : ev_stop, stream);
     }
     if (rest > 0) {
       ScanArgs b = a;
       b.cph = 1;
       b.qoff = full * kQueryChunk;
-      launch_class(rest, b, H, nsb, sample_phase, stream);
+      launch_class(rest, b, H, nsb, sample_phase, full > 0 ? nullptr : ev_start, ev_stop, stream);
     }
-    if (!sample_phase && timing && timing->stop) (void)hipEventRecord(timing->stop, stream);
     if (sample_phase) {
       hipLaunchKernelGGL(scan_threshold_kernel, dim3(num_q), dim3(kSelectThreads), 0, stream, ws.sample,
                          nsb * kSampleBlockKeys, static_cast<uint32_t>(rsel), ws.theta, ws.count);

@@ -189,6 +189,23 @@ def test_forced_ties_and_zero_query():
     check_full(keys, q, 4, 92, 512)
 
 
+@pytest.mark.parametrize("n_dup", [3000, 6000, 9000])
+def test_massive_ties_in_candidate_list(n_dup):
+    """Thousands of copies of the best key for query 0: they all reach the
+    candidate list with one score, so the merge keeps (and sorts) far more
+    than k keys; the result is the k lowest indices among the copies."""
+    say("massive ties", n_dup)
+    n = 12000
+    keys, q = synth.make_inputs(11, 1, n, 4)
+    rng = np.random.default_rng(n_dup)
+    dup = np.sort(rng.choice(n, n_dup, replace=False))
+    # past every channel's extreme: the copies sit in the extreme bin of every
+    # channel, on the side that query 0 weighs positively
+    keys[0, dup] = (np.sign(q[0]) * (np.abs(keys[0]).max(axis=0) + 1.0))[None, :]
+    res, _ = check_full(keys, q, 4, 92, 100)
+    assert np.array_equal(res["idx"][0], dup[:100])
+
+
 def test_constant_keys():
     say("constant keys")
     keys = np.full((1, 3000, 128), 2.5, np.float32)
