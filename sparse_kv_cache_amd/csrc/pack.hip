@@ -11,6 +11,8 @@
 // All float steps use explicit round-to-nearest intrinsics (no contraction),
 // so planes, lo, step and var are bit-exact and independent of launch order.
 
+#include <algorithm>
+
 #include "fathom_internal.h"
 
 namespace fathom {
@@ -18,11 +20,6 @@ namespace {
 
 constexpr int kRangeThreads = 256;
 constexpr int kRangeRows = 4096;        // key rows per range workgroup
-constexpr int kQuantThreads = 512;      // 8 waves, one wave per 64 keys
-constexpr int kTileKeys = 512;          // keys per quantize tile (16 plane words)
-constexpr int kTileWords = kTileKeys / 32;
-constexpr int kCodeStride = kD / 4 + 1; // u32 words per key row of codes in LDS (+1: bank spread)
-constexpr int kTilesPerBlock = 4;
 
 __global__ void pack_init_kernel(PackWorkspace ws, int count) {
   int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -76,110 +73,131 @@ __global__ __launch_bounds__(kRangeThreads) void pack_range_kernel(
   }
 }
 
-// Quantize a tile of 512 keys, transpose the codes into bit-plane words with
-// wavefront ballots (lane = key), and accumulate the integer moments.
+// Quantize-and-transpose.  A workgroup (4 wavefronts) packs tiles of 32
+// plane words (1024 keys) of one head.  Each half-wavefront owns one plane
+// word at a time: its 32 lanes cover the 128 channels (lane = 4-channel
+// group) and walk the word's 32 consecutive keys, so lane `cg` ends up with
+// the 4-bit codes of channels 4cg..4cg+3 for keys 32w..32w+31.  Packing the
+// four codes of key b as a 16-bit value x[b] and transposing the 32 x 16 bit
+// matrix in registers yields the 16 plane words of those channels directly
+// (bit b = key 32w+b).  The words are staged in LDS so each plane row is
+// stored as one 128-byte segment.
+constexpr int kQuantThreads = 256;
+constexpr int kQuantWords = 32;                       // plane words per tile
+constexpr int kHalfWaves = kQuantThreads / 32;        // 8 word slots in flight
+constexpr int kKeyBatch = 16;                         // loads in flight per lane
+
+// In-register transpose of the 16-bit values x[0..31] (bit p of x[b]) into
+// 16 words (bit b of word p).  The first swap round of the 32 x 32 network
+// only packs key b+16 into the upper half of x[b], because the upper halves
+// are zero; four rounds on 16 words remain.
+__device__ __forceinline__ void transpose32x16(uint32_t (&x)[32], uint32_t (&y)[16]) {
+#pragma unroll
+  for (int k = 0; k < 16; ++k) y[k] = x[k] | (x[k + 16] << 16);
+#pragma unroll
+  for (int sh = 8; sh >= 1; sh >>= 1) {
+    const uint32_t m = sh == 8 ? 0x00ff00ffu : sh == 4 ? 0x0f0f0f0fu : sh == 2 ? 0x33333333u : 0x55555555u;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      if (k & sh) continue;
+      const uint32_t t = ((y[k] >> sh) ^ y[k + sh]) & m;
+      y[k + sh] ^= t;
+      y[k] ^= t << sh;
+    }
+  }
+}
+
 __global__ __launch_bounds__(kQuantThreads) void pack_quant_kernel(
     const float* __restrict__ keys, int64_t stride_head, int64_t stride_token, int64_t n,
-    int64_t ldw, int num_tiles, uint32_t* __restrict__ planes, PackWorkspace ws) {
+    int64_t ldw, int num_tiles, int tiles_per_wg, uint32_t* __restrict__ planes, PackWorkspace ws) {
   const int h = blockIdx.y;
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int cg = tid & 31;          // channels 4cg .. 4cg+3
+  const int hw = tid >> 5;          // word slot 0..7
 
-  __shared__ float s_lo[kD], s_inv[kD];
-  __shared__ uint32_t s_code[kTileKeys * kCodeStride];          // 4 codes per word
-  __shared__ uint32_t s_words[kD * kPlanes * kTileWords];        // [c][j][word]
-  __shared__ uint32_t s_m1[16][kD], s_m2[16][kD];
+  __shared__ uint32_t s_words[kQuantWords][kD * kPlanes];   // [word][row = c*4 + j]
+  __shared__ uint32_t s_m1[kHalfWaves][kD], s_m2[kHalfWaves][kD];
 
-  if (tid < kD) {
-    const float lo = ordered_to_float(ws.kmin[h * kD + tid]);
-    const float hi = ordered_to_float(ws.kmax[h * kD + tid]);
-    const float r = __fsub_rn(hi, lo);
-    s_lo[tid] = lo;
-    s_inv[tid] = r > 0.0f ? __fdiv_rn(16.0f, r) : 0.0f;
-  }
-  __syncthreads();
-
-  const int cg = tid & 31;      // channel group for the load phase
-  const int rg = tid >> 5;      // row group 0..15
   float lo4[4], inv4[4];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) { lo4[t] = s_lo[4 * cg + t]; inv4[t] = s_inv[4 * cg + t]; }
-  uint32_t m1[4] = {0, 0, 0, 0}, m2[4] = {0, 0, 0, 0};
+  for (int t = 0; t < 4; ++t) {
+    const int c = h * kD + 4 * cg + t;
+    const float lo = ordered_to_float(ws.kmin[c]);
+    const float r = __fsub_rn(ordered_to_float(ws.kmax[c]), lo);
+    lo4[t] = lo;
+    inv4[t] = r > 0.0f ? __fdiv_rn(16.0f, r) : 0.0f;
+  }
+  uint32_t m1[4] = {0u, 0u, 0u, 0u}, m2[4] = {0u, 0u, 0u, 0u};
   const float* head_keys = keys + int64_t(h) * stride_head + 4 * cg;
 
-  for (int tile = blockIdx.x * kTilesPerBlock;
-       tile < num_tiles && tile < (blockIdx.x + 1) * kTilesPerBlock; ++tile) {
-    const int64_t key0 = int64_t(tile) * kTileKeys;
-    // 1) load + quantize: 16 row groups x 32 rows each
-    for (int r = rg; r < kTileKeys; r += 16) {
-      const int64_t i = key0 + r;
-      uint32_t packed = 0;
-      if (i < n) {
-        float4 v = *reinterpret_cast<const float4*>(head_keys + i * stride_token);
-        float kv[4] = {v.x, v.y, v.z, v.w};
+  const int tile_begin = blockIdx.x * tiles_per_wg;
+  const int tile_end = min(num_tiles, tile_begin + tiles_per_wg);
+  for (int tile = tile_begin; tile < tile_end; ++tile) {
+    const int64_t word_base = int64_t(tile) * kQuantWords;
+    for (int wl = hw; wl < kQuantWords; wl += kHalfWaves) {
+      const int64_t key0 = (word_base + wl) * 32;
+      uint32_t x[32];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const float u = __fmul_rn(__fsub_rn(kv[t], lo4[t]), inv4[t]);
-          const uint32_t code = u >= 15.0f ? 15u : static_cast<uint32_t>(u);  // u >= 0: trunc = floor
-          m1[t] += code;
-          m2[t] += code * code;
-          packed |= code << (8 * t);
+      for (int half = 0; half < 32; half += kKeyBatch) {
+        float4 v[kKeyBatch];
+        // unconditional loads: keys past n read key n-1 and are masked below
+#pragma unroll
+        for (int b = 0; b < kKeyBatch; ++b) {
+          const int64_t i = min<int64_t>(key0 + half + b, n - 1);
+          v[b] = *reinterpret_cast<const float4*>(head_keys + i * stride_token);
         }
-      }
-      s_code[r * kCodeStride + cg] = packed;
-    }
-    __syncthreads();
-    // 2) transpose: wave w owns keys 64w .. 64w+63 of the tile, lane = key
-    {
-      const int key = wave * 64 + lane;
-      for (int cw = 0; cw < kD / 4; ++cw) {
-        const uint32_t four = s_code[key * kCodeStride + cw];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int c = cw * 4 + t;
-          const uint32_t code = (four >> (8 * t)) & 0xffu;
+        for (int b = 0; b < kKeyBatch; ++b) {
+          const bool valid = key0 + half + b < n;
+          const float kv[4] = {v[b].x, v[b].y, v[b].z, v[b].w};
+          uint32_t packed = 0u;
 #pragma unroll
-          for (int j = 0; j < kPlanes; ++j) {
-            const uint64_t m = __ballot((code >> (3 - j)) & 1u);
-            // lanes 0 and 1 store the low / high 32-key words
-            if (lane < 2) {
-              const uint32_t word = lane == 0 ? static_cast<uint32_t>(m) : static_cast<uint32_t>(m >> 32);
-              s_words[(c * kPlanes + j) * kTileWords + wave * 2 + lane] = word;
-            }
+          for (int t = 0; t < 4; ++t) {
+            const float u = __fmul_rn(__fsub_rn(kv[t], lo4[t]), inv4[t]);
+            uint32_t code = u >= 15.0f ? 15u : static_cast<uint32_t>(u);   // u >= 0: trunc = floor
+            code = valid ? code : 0u;
+            m1[t] += code;
+            m2[t] += code * code;
+            packed |= code << (4 * t);
           }
+          x[half + b] = packed;
         }
       }
+      uint32_t y[16];
+      transpose32x16(x, y);
+      // word p = 4t + i holds bit i of channel t's code = plane 3 - i
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s_words[wl][(4 * cg + t) * kPlanes + (3 - i)] = y[4 * t + i];
     }
     __syncthreads();
-    // 3) store: one plane row segment (16 words = 64 B) per thread
-    {
-      const int row = tid;                          // c * 4 + j, 512 rows
-      const int64_t w0 = int64_t(tile) * kTileWords;
-      uint32_t* dst = planes + (int64_t(h) * kD * kPlanes + row) * ldw + w0;
-      const uint32_t* src = s_words + row * kTileWords;
-      if (w0 + kTileWords <= ldw) {
+    // store: thread = two plane rows, 32 words (128 bytes) each
 #pragma unroll
-        for (int v = 0; v < kTileWords / 4; ++v) {
-          reinterpret_cast<uint4*>(dst)[v] =
-              make_uint4(src[4 * v], src[4 * v + 1], src[4 * v + 2], src[4 * v + 3]);
-        }
+    for (int rr = 0; rr < 2; ++rr) {
+      const int row = tid + rr * kQuantThreads;           // c * 4 + j
+      uint32_t* dst = planes + (int64_t(h) * kD * kPlanes + row) * ldw + word_base;
+      if (word_base + kQuantWords <= ldw) {
+#pragma unroll
+        for (int v = 0; v < kQuantWords / 4; ++v)
+          reinterpret_cast<uint4*>(dst)[v] = make_uint4(s_words[4 * v][row], s_words[4 * v + 1][row],
+                                                        s_words[4 * v + 2][row], s_words[4 * v + 3][row]);
       } else {
-        for (int v = 0; w0 + v < ldw; ++v) dst[v] = src[v];
+        for (int v = 0; word_base + v < ldw; ++v) dst[v] = s_words[v][row];
       }
     }
     __syncthreads();
   }
-  // moments: fold the 16 row groups, then one 64-bit atomic per channel
+  // moments: fold the 8 word slots, then one 64-bit atomic per channel
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    s_m1[rg][4 * cg + t] = m1[t];
-    s_m2[rg][4 * cg + t] = m2[t];
+    s_m1[hw][4 * cg + t] = m1[t];
+    s_m2[hw][4 * cg + t] = m2[t];
   }
   __syncthreads();
   if (tid < kD) {
     unsigned long long a = 0, b = 0;
-    for (int r = 0; r < 16; ++r) {
+    for (int r = 0; r < kHalfWaves; ++r) {
       a += s_m1[r][tid];
       b += s_m2[r][tid];
     }
@@ -219,11 +237,14 @@ hipError_t launch_pack(const float* keys, int64_t stride_head, int64_t stride_to
   const int range_blocks = static_cast<int>((n + kRangeRows - 1) / kRangeRows);
   hipLaunchKernelGGL(pack_range_kernel, dim3(range_blocks, H), dim3(kRangeThreads), 0, stream, keys,
                      stride_head, stride_token, n, ws);
-  // tiles cover every word of the padded rows, so padding words are written as zero
-  const int num_tiles = static_cast<int>((ldw + kTileWords - 1) / kTileWords);
-  const int quant_blocks = (num_tiles + kTilesPerBlock - 1) / kTilesPerBlock;
+  // tiles cover every word of the padded rows, so padding words are written
+  // as zero; about 1024 workgroups in total, whatever H
+  const int num_tiles = static_cast<int>((ldw + kQuantWords - 1) / kQuantWords);
+  const int64_t want = (1024 + H - 1) / H;
+  const int tiles_per_wg = static_cast<int>(std::max<int64_t>(1, (num_tiles + want - 1) / want));
+  const int quant_blocks = (num_tiles + tiles_per_wg - 1) / tiles_per_wg;
   hipLaunchKernelGGL(pack_quant_kernel, dim3(quant_blocks, H), dim3(kQuantThreads), 0, stream, keys,
-                     stride_head, stride_token, n, ldw, num_tiles, planes, ws);
+                     stride_head, stride_token, n, ldw, num_tiles, tiles_per_wg, planes, ws);
   hipLaunchKernelGGL(pack_final_kernel, dim3((count + 255) / 256), dim3(256), 0, stream, count, n, ws,
                      lo, step, var);
   return hipGetLastError();
