@@ -74,7 +74,7 @@ PackLayout pack_layout(int H) {
 }
 
 struct ScanLayout {
-  size_t theta, count, sample, cand, total;
+  size_t theta, count, sample, cand, tables, total;
 };
 ScanLayout scan_layout(int num_q) {
   const size_t Q = static_cast<size_t>(num_q);
@@ -84,6 +84,7 @@ ScanLayout scan_layout(int num_q) {
   L.count = off;  off = round_up(off + Q * 4, 256);
   L.sample = off; off = round_up(off + Q * kSampleMaxKeys * 4, 256);
   L.cand = off;   off = round_up(off + Q * kCandCap * 8, 256);
+  L.tables = off; off = round_up(off + Q * kChunkTableBytes, 256);
   L.total = off;
   return L;
 }
@@ -187,7 +188,8 @@ int fathom_scan_topk(const uint32_t* planes, const float* lo, const float* step,
                 L.total, workspace_bytes);
   char* w = static_cast<char*>(workspace);
   ScanWorkspace ws{reinterpret_cast<float*>(w + L.theta), reinterpret_cast<uint32_t*>(w + L.count),
-                   reinterpret_cast<float*>(w + L.sample), reinterpret_cast<uint2*>(w + L.cand)};
+                   reinterpret_cast<float*>(w + L.sample), reinterpret_cast<uint2*>(w + L.cand),
+                   static_cast<void*>(w + L.tables)};
 
   ScanTiming timing;
   bool timed = false;

@@ -9,6 +9,7 @@ namespace fathom {
 constexpr int kD = 128;            // channels supported by this build
 constexpr int kPlanes = 4;         // 4-bit K cache -> 4 bit planes
 constexpr int kMaxK = 4096;        // largest top-k
+constexpr size_t kChunkTableBytes = 12288;   // one (KV head, query chunk) scan table
 constexpr int kCandCap = 16384;    // candidate slots per query (merge sorts them in LDS)
 constexpr int kSampleBlockKeys = 1024;  // keys per sampled block (32 plane words)
 constexpr int kSampleMaxBlocks = 8;     // sampled blocks per KV head
@@ -48,6 +49,7 @@ struct ScanWorkspace {
   uint32_t* count;   // [Q] candidates seen per query
   float* sample;     // [Q][kSampleMaxKeys] scores of the sampled keys
   uint2* cand;       // [Q][kCandCap] (score bits, key index)
+  void* tables;      // [Q][kChunkTableBytes] per (KV head, query chunk) scan tables (at most Q chunks)
 };
 
 struct ScanTiming {

@@ -42,11 +42,15 @@ namespace fathom {
 namespace {
 
 constexpr int kMaxUnion = kD * kPlanes;
-constexpr int kChunk = 8;                      // union planes per LUT chunk
-constexpr int kMaxChunks = kMaxUnion / kChunk;
-constexpr int kMainThreads = 768;              // two lanes per plane word
-constexpr int kTileWords = kMainThreads / 2;     // 384 words = 12288 keys per tile
-constexpr int kLutBytes = 144 * 1024;          // LUT capacity in LDS
+constexpr int kBlockPlanes = 64;               // union planes per MFMA (its K)
+constexpr int kMaxBlocks = kMaxUnion / kBlockPlanes;
+// the union is padded with readable zero-weight rows to whole K blocks
+constexpr int kPadPlanes = kBlockPlanes;
+constexpr int kMainThreads = 256;              // 4 wavefronts
+constexpr int kMainWgPerCu = 3;                // register budget: 3 resident workgroups per CU
+constexpr int kWaveWords = 8;                  // 16 MFMA columns = 8 words x 2 halves
+constexpr int kTileWords = (kMainThreads / 64) * kWaveWords;   // 32 words = 1024 keys
+constexpr int kLdsCand = 512;                 // candidates per query buffered in a main workgroup
 constexpr int kSampleThreads = 256;            // lane = key
 constexpr int kSampleWgPerBlock = kSampleBlockKeys / kSampleThreads;
 constexpr int kSelectThreads = 1024;
@@ -72,13 +76,15 @@ struct ScanArgs {
   uint2* cand;
   float* all_scores;
   int sample_stride;  // distance between sampled blocks, in 1024-key blocks
+  int chunks_per_head;
+  void* tables;       // [H * chunks_per_head] ChunkTable, written by the sample kernel
 };
 
 template <int GQ>
 struct UnionLds {
-  float w[kMaxUnion + 2 * kChunk][4];        // W_qcj per union plane; 0 where the query skips it
-  uint32_t rowoff[kMaxUnion + 2 * kChunk];   // byte offset of the plane row (c*4 + j) in the head
-  uint8_t mask[kMaxUnion + 2 * kChunk];      // bit g: query g of the chunk reads the plane
+  float w[kMaxUnion + kPadPlanes][4];        // W_qcj per union plane; 0 where the query skips it
+  uint32_t rowoff[kMaxUnion + kPadPlanes];   // byte offset of the plane row (c*4 + j) in the head
+  uint8_t mask[kMaxUnion + kPadPlanes];      // bit g: query g of the chunk reads the plane
   int off[kPlanes][kD];
   int u[kD];
   double cpart[2][GQ];
@@ -88,6 +94,27 @@ struct UnionLds {
   uint32_t base[4];     // their first slot in the candidate list
   int U;
 };
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// What the main kernel needs of a (KV head, query chunk): the union rows, the
+// MFMA A operands (int8 limbs of the fixed-point plane weights), the scales
+// and the score offsets.  Built once per call by the sample kernel.
+struct ChunkTable {
+  uint32_t rowoff[kMaxUnion + kPadPlanes];   // byte offset of each union row in the head
+  uint4 A[kMaxBlocks][4][16];                // [block][K slice][row 4g + limb]: 16 int8 limbs
+  float sigma[4];                            // fixed-point scale of each query's weights
+  float C[4];                                // score offsets C_q
+  int U;                                     // union planes
+  int pad_[3];
+};
+static_assert(sizeof(ChunkTable) <= kChunkTableBytes, "chunk table fits its workspace slot");
+static_assert(sizeof(ChunkTable) % 16 == 0, "chunk tables are copied as uint4");
+
+__device__ inline int chunk_index(const ScanArgs& a) {
+  const int h = blockIdx.y / a.cph;
+  return h * a.chunks_per_head + a.qoff / kQueryChunk + static_cast<int>(blockIdx.y % a.cph);
+}
 
 __device__ inline int lanes_below(uint64_t mask) {
   const int lane = threadIdx.x & 63;
@@ -236,15 +263,34 @@ __device__ void build_union(const ScanArgs& a, int h, int q0, UnionLds<GQ>& s) {
       s.mask[o] = static_cast<uint8_t>(m);
     }
   }
-  // padding up to a whole pair of LUT chunks: row 0, weight 0
+  // padding up to whole groups of 4 LUT chunks: row 0, weight 0
   const int U = s.U;
-  const int pad = (2 * kChunk - U % (2 * kChunk)) % (2 * kChunk);
+  const int pad = (kPadPlanes - U % kPadPlanes) % kPadPlanes;
   if (t < pad) {
     s.w[U + t][0] = s.w[U + t][1] = s.w[U + t][2] = s.w[U + t][3] = 0.0f;
     s.rowoff[U + t] = 0u;
     s.mask[U + t] = 0u;
   }
   __syncthreads();
+}
+
+// Builds the main kernel's table of this (KV head, query chunk) and stores it
+// in the workspace.  Needs blockDim.x >= 64; contains barriers.
+template <int GQ>
+__device__ void build_limbs(const UnionLds<GQ>& s, ChunkTable& T, double (&wsum)[4], int nblk);
+
+template <int GQ>
+__device__ void write_chunk_table(const ScanArgs& a, const UnionLds<GQ>& s, ChunkTable& T, double (&wsum)[4]) {
+  const int U = s.U;
+  const int nblk = (U + kBlockPlanes - 1) / kBlockPlanes;
+  for (int i = threadIdx.x; i < kMaxUnion + kPadPlanes; i += blockDim.x)
+    T.rowoff[i] = i < nblk * kBlockPlanes ? s.rowoff[i] : 0u;
+  if (threadIdx.x < 4) T.C[threadIdx.x] = static_cast<int>(threadIdx.x) < GQ ? s.C[threadIdx.x] : 0.0f;
+  if (threadIdx.x == 0) T.U = U;
+  build_limbs<GQ>(s, T, wsum, nblk);   // ends with a barrier
+  uint4* dst = reinterpret_cast<uint4*>(static_cast<char*>(a.tables) + size_t(chunk_index(a)) * kChunkTableBytes);
+  const uint4* src = reinterpret_cast<const uint4*>(&T);
+  for (int i = threadIdx.x; i < static_cast<int>(sizeof(ChunkTable) / 16); i += blockDim.x) dst[i] = src[i];
 }
 
 // ------------------------------------------------------------------ sample
@@ -256,9 +302,12 @@ __global__ __launch_bounds__(kSampleThreads) void scan_sample_kernel(ScanArgs a)
   constexpr int kWords = kSampleThreads / 32;
   __shared__ UnionLds<GQ> s;
   __shared__ uint32_t stage[kMaxUnion][kWords];
+  __shared__ ChunkTable T;
+  __shared__ double wsum[4];
   const int h = blockIdx.y / a.cph;
   const int q0 = h * a.group + a.qoff + (blockIdx.y % a.cph) * kQueryChunk;
   build_union<GQ>(a, h, q0, s);
+  if (blockIdx.x == 0) write_chunk_table<GQ>(a, s, T, wsum);   // uniform per workgroup
 
   const int sbi = blockIdx.x / kSampleWgPerBlock;
   const int part = blockIdx.x % kSampleWgPerBlock;
@@ -581,56 +630,6 @@ __global__ __launch_bounds__(kSelectThreads) void scan_threshold_kernel(
 
 // -------------------------------------------------------------------- main
 
-template <int GQ> struct LutEntry { using T = float4; };
-template <> struct LutEntry<1> { using T = float; };
-template <> struct LutEntry<2> { using T = float2; };
-
-template <int GQ>
-struct MainLds {
-  using E = typename LutEntry<GQ>::T;
-  static constexpr int kCapRaw = kLutBytes / (256 * static_cast<int>(sizeof(E)));
-  static constexpr int kCap = kCapRaw < kMaxChunks ? kCapRaw : kMaxChunks;   // chunks per pass
-  E lut[kCap][256];
-  UnionLds<GQ> u;
-};
-
-__device__ inline float comp(float e, int) { return e; }
-__device__ inline float comp(float2 e, int g) { return g == 0 ? e.x : e.y; }
-__device__ inline float comp(float4 e, int g) { return g == 0 ? e.x : g == 1 ? e.y : g == 2 ? e.z : e.w; }
-
-// Tabulates chunks [m0, m1) of the union: entry e of chunk m holds, for every
-// query g, the sum of the weights of the chunk's planes whose bit is set in e
-// (plane 8m + t <-> bit t), added in t order.
-template <int GQ>
-__device__ void build_lut(MainLds<GQ>& S, int m0, int m1, int U) {
-  using E = typename MainLds<GQ>::E;
-  const int total = (m1 - m0) * 256;
-  for (int i = threadIdx.x; i < total; i += blockDim.x) {
-    const int m = m0 + (i >> 8), e = i & 255;
-    float sum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int t = 0; t < kChunk; ++t) {
-      const int p = m * kChunk + t;
-      if (((e >> t) & 1) && p < U) {
-        const float4 w = *reinterpret_cast<const float4*>(&S.u.w[p][0]);
-        sum[0] += w.x;
-        sum[1] += w.y;
-        sum[2] += w.z;
-        sum[3] += w.w;
-      }
-    }
-    E out;
-    if constexpr (GQ == 1) {
-      out = sum[0];
-    } else if constexpr (GQ == 2) {
-      out = make_float2(sum[0], sum[1]);
-    } else {
-      out = make_float4(sum[0], sum[1], sum[2], sum[3]);
-    }
-    S.lut[m - m0][e] = out;
-  }
-}
-
 // In-register transpose of an 8x32 bit block: on entry x[t] holds plane t's
 // bits of 32 keys (key b at bit b); on exit byte g of x[k] holds the 8 plane
 // bits of key 8g + k (plane t at bit t).  Three rounds of block swaps.
@@ -656,178 +655,232 @@ __device__ __forceinline__ void transpose8x32(uint32_t (&x)[8]) {
   }
 }
 
-// Loads this lane's word of the 8 plane rows of chunk m.  The union list is
-// padded to whole chunk pairs with readable rows, and lanes past the store's
-// last word read that word instead, so every load is unconditional.
+// Bit i of the 4-bit value n becomes byte i (0 or 1): the four shifted copies
+// n << 7i do not overlap, and copy i puts bit i at position 8i.
+__device__ __forceinline__ int spread4(uint32_t n) { return static_cast<int>((n * 0x00204081u) & 0x01010101u); }
+
+// Per query: fixed-point weights V = round(W / sigma) with sigma = sum|W| /
+// 2^30, split into four balanced base-256 digits (int8 limbs), so the int8
+// MFMA accumulates each limb exactly and the score is
+// C + sigma * (l0 + 2^8 l1 + 2^16 l2 + 2^24 l3).  Rows of the A operand are
+// (query g, limb) = 4g + limb; K slice G of block b covers union planes
+// 64b + 16G .. 64b + 16G + 15.  Fills T.A and T.sigma; wsum is LDS scratch.
 template <int GQ>
-__device__ __forceinline__ void load_chunk(const char* head, const UnionLds<GQ>& s, int m,
-                                           uint32_t woff, uint32_t (&x)[8]) {
+__device__ void build_limbs(const UnionLds<GQ>& s, ChunkTable& T, double (&wsum)[4], int nblk) {
+  const int t = threadIdx.x;
+  const int P = nblk * kBlockPlanes;
+  if (t < 64) {
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+    for (int p = t; p < P; p += 64)
 #pragma unroll
-  for (int t = 0; t < kChunk; ++t)
-    x[t] = *reinterpret_cast<const uint32_t*>(head + (s.rowoff[m * kChunk + t] + woff));
+      for (int g = 0; g < 4; ++g) acc[g] += fabs(static_cast<double>(s.w[p][g]));
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const double v = wave_sum(acc[g]);
+      if (t == 0) {
+        wsum[g] = v;
+        T.sigma[g] = static_cast<float>(v * 0x1p-30);
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = t; i < P * 4; i += blockDim.x) {
+    const int p = i >> 2, g = i & 3;
+    const double ws = wsum[g];
+    long long v = ws > 0.0 ? llrint(static_cast<double>(s.w[p][g]) * (0x1p30 / ws)) : 0ll;
+    const int b = p / kBlockPlanes, G = (p % kBlockPlanes) / 16, byte = p % 16;
+    uint8_t* row = reinterpret_cast<uint8_t*>(&T.A[b][G][0]);
+#pragma unroll
+    for (int l = 0; l < 4; ++l) {
+      const long long d = ((v + 128) & 255) - 128;   // balanced digit in [-128, 127]
+      row[(4 * g + l) * 16 + byte] = static_cast<uint8_t>(static_cast<int8_t>(d));
+      v = (v - d) >> 8;
+    }
+  }
+  __syncthreads();
 }
 
-// Accumulates a pair of chunks (m, m+1) for this lane's 16 keys.  Two lanes
-// share a plane word: lane half h owns bits 16h..16h+15.  The lane packs its
-// halves of the two chunks into one word per plane (chunk m low, chunk m+1
-// high), so a single 8x32 transpose yields the LUT index bytes of 16 keys x 2
-// chunks: byte g of x[k] indexes chunk m + (g >> 1) for key 8(g & 1) + k.
-template <int GQ>
-__device__ __forceinline__ void accumulate_pair(const typename MainLds<GQ>::E* lut_m,
-                                                const typename MainLds<GQ>::E* lut_m1,
-                                                const uint32_t (&xa)[8], const uint32_t (&xb)[8],
-                                                uint32_t sel, float (&acc)[16][GQ]) {
-  using E = typename MainLds<GQ>::E;
-  uint32_t x[8];
+// Loads this lane's word of the 16 union planes of K slice G of block b.
+// The union is padded to whole blocks with readable rows, and lanes past the
+// store's last word read that word instead, so every load is unconditional.
+__device__ __forceinline__ void load_slice(const char* head, const uint32_t* rowoff, int b, int G,
+                                           uint32_t woff, uint32_t (&x)[16]) {
+  const int p0 = b * kBlockPlanes + G * 16;
 #pragma unroll
-  for (int t = 0; t < 8; ++t) x[t] = __builtin_amdgcn_perm(xb[t], xa[t], sel);
+  for (int t = 0; t < 16; ++t)
+    x[t] = *reinterpret_cast<const uint32_t*>(head + (rowoff[p0 + t] + woff));
+}
+
+// Packs this lane's halves of the two 8-plane groups of its 16 plane words
+// into one word per plane and transposes: byte h of x[k] holds planes 0..7
+// and byte 2 + h planes 8..15 of key 8h + k of the half word.
+__device__ __forceinline__ void slice_indices(const uint32_t (&w)[16], uint32_t sel, uint32_t (&x)[8]) {
+#pragma unroll
+  for (int t = 0; t < 8; ++t) x[t] = __builtin_amdgcn_perm(w[t + 8], w[t], sel);
   transpose8x32(x);
+}
+
+// One K block: per key of the half word, its 16 plane bits become 16 bytes
+// of 0/1 (the B operand) and the key position gets one MFMA.
+__device__ __forceinline__ void mfma_block(const uint32_t (&x)[8], v4i A, v4i (&acc)[16]) {
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    E e[4];
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) e[g4] = (g4 < 2 ? lut_m : lut_m1)[(x[k] >> (8 * g4)) & 0xffu];
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4)
-#pragma unroll
-      for (int g = 0; g < GQ; ++g) acc[8 * (g4 & 1) + k][g] += comp(e[g4], g);
+    for (int h = 0; h < 2; ++h) {
+      v4i bv;
+      bv.x = spread4(__builtin_amdgcn_ubfe(x[k], 8 * h, 4));
+      bv.y = spread4(__builtin_amdgcn_ubfe(x[k], 8 * h + 4, 4));
+      bv.z = spread4(__builtin_amdgcn_ubfe(x[k], 16 + 8 * h, 4));
+      bv.w = spread4(__builtin_amdgcn_ubfe(x[k], 20 + 8 * h, 4));
+      acc[8 * h + k] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, bv, acc[8 * h + k], 0, 0, 0);
+    }
   }
 }
 
+// Inclusive prefix sum over the 16 lanes of a DPP row.
+__device__ __forceinline__ uint32_t row_incl_sum(uint32_t v) {
+  v += dpp_u32<kDppRowShr + 1>(0u, v);
+  v += dpp_u32<kDppRowShr + 2>(0u, v);
+  v += dpp_u32<kDppRowShr + 4>(0u, v);
+  v += dpp_u32<kDppRowShr + 8>(0u, v);
+  return v;
+}
+
 template <int GQ>
-__global__ __launch_bounds__(kMainThreads) void scan_main_kernel(ScanArgs a) {
-  using E = typename MainLds<GQ>::E;
-  constexpr int kCapChunks = MainLds<GQ>::kCap & ~1;        // passes hold whole chunk pairs
-  __shared__ MainLds<GQ> S;
-  UnionLds<GQ>& s = S.u;
+__global__ __launch_bounds__(kMainThreads, kMainWgPerCu) void scan_main_kernel(ScanArgs a) {
+  __shared__ ChunkTable T;
+  __shared__ uint2 cbuf[4][kLdsCand];   // this workgroup's candidates per query
+  __shared__ uint32_t tally[4], cbase[4];
+  __shared__ float theta_s[4];
   const int h = blockIdx.y / a.cph;
   const int q0 = h * a.group + a.qoff + (blockIdx.y % a.cph) * kQueryChunk;
-  if (threadIdx.x < GQ) {
-    s.theta[threadIdx.x] = a.theta[q0 + threadIdx.x];
-    s.tally[threadIdx.x] = 0u;
+  {
+    const uint4* src = reinterpret_cast<const uint4*>(static_cast<const char*>(a.tables) +
+                                                      size_t(chunk_index(a)) * kChunkTableBytes);
+    uint4* dst = reinterpret_cast<uint4*>(&T);
+    for (int i = threadIdx.x; i < static_cast<int>(sizeof(ChunkTable) / 16); i += blockDim.x) dst[i] = src[i];
+    if (threadIdx.x < 4) {
+      theta_s[threadIdx.x] = static_cast<int>(threadIdx.x) < GQ ? a.theta[q0 + threadIdx.x] : 0.0f;
+      tally[threadIdx.x] = 0u;
+    }
   }
-  build_union<GQ>(a, h, q0, s);
+  __syncthreads();
+  const int nblk = (T.U + kBlockPlanes - 1) / kBlockPlanes;
 
+  const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-  const int half = threadIdx.x & 1;
+  const int col = lane & 15;            // MFMA column: word col >> 1, half col & 1
+  const int G = lane >> 4;              // K slice; in the result, the query of the lane
+  const int half = col & 1;
   const uint32_t sel = half ? 0x07060302u : 0x05040100u;   // v_perm byte selectors
-  const int U = s.U;
-  const int nchunks = ((U + 2 * kChunk - 1) / (2 * kChunk)) * 2;   // whole pairs
-  const int passes = (nchunks + kCapChunks - 1) / kCapChunks;
   const char* head = reinterpret_cast<const char*>(a.planes + int64_t(h) * kD * kPlanes * a.ldw);
-  if (passes == 1) {
-    build_lut<GQ>(S, 0, nchunks, U);
-    __syncthreads();
-  }
   const int tile_begin = blockIdx.x * a.tiles_per_wg;
   const int tile_end = min(a.tiles, tile_begin + a.tiles_per_wg);
+  const bool qvalid = G < GQ;
+  const float sigma = T.sigma[G];
+  const float Cq = T.C[G];
+  const float theta = theta_s[G];
 
+  auto word_of = [&](int tile) { return tile * kTileWords + wave * kWaveWords + (col >> 1); };
+  auto woff_of = [&](int tile) {
+    const int w = word_of(tile);
+    return static_cast<uint32_t>(w < a.nwords ? w : a.nwords - 1) * 4u;
+  };
+
+  // One word buffer: once a block's words are transposed into index bytes the
+  // buffer is refilled with the next step's words (the step after the last
+  // block of a tile is block 0 of the next tile), which are in flight while
+  // the block's MFMAs run.
+  uint32_t words[16];
+  if (nblk > 0 && tile_begin < tile_end) load_slice(head, T.rowoff, 0, G, woff_of(tile_begin), words);
   for (int tile = tile_begin; tile < tile_end; ++tile) {
-    const int w = tile * kTileWords + (threadIdx.x >> 1);
-    const bool active = w < a.nwords;
-    const uint32_t woff = static_cast<uint32_t>(active ? w : a.nwords - 1) * 4u;
-    float acc[16][GQ];
+    v4i acc[16];
 #pragma unroll
-    for (int b = 0; b < 16; ++b)
-#pragma unroll
-      for (int g = 0; g < GQ; ++g) acc[b][g] = 0.0f;
-
-    for (int pass = 0; pass < passes; ++pass) {
-      const int m_begin = pass * kCapChunks;
-      const int m_end = min(nchunks, m_begin + kCapChunks);
-      if (passes > 1) {
-        __syncthreads();
-        build_lut<GQ>(S, m_begin, m_end, U);
-        __syncthreads();
-      }
-      // Two pair buffers: while one pair is accumulated the next pair's loads
-      // are in flight.  Loads are unconditional (pair index clamped) so the
-      // compiler counts outstanding loads exactly, and scheduling barriers
-      // keep it from hoisting further loads into the accumulation.
-      const int npairs = (m_end - m_begin) / 2;
-      const int plast = npairs - 1;
-      uint32_t a0[8], a1[8], b0[8], b1[8];
-      load_chunk<GQ>(head, s, m_begin, woff, a0);
-      load_chunk<GQ>(head, s, m_begin + 1, woff, a1);
-      load_chunk<GQ>(head, s, m_begin + 2 * min(1, plast), woff, b0);
-      load_chunk<GQ>(head, s, m_begin + 2 * min(1, plast) + 1, woff, b1);
-      for (int pp = 0; pp < npairs; pp += 2) {
-        const int m = m_begin + 2 * pp;
-        accumulate_pair<GQ>(S.lut[m - m_begin], S.lut[m + 1 - m_begin], a0, a1, sel, acc);
-        __builtin_amdgcn_sched_barrier(0);
-        const int mn = m_begin + 2 * min(pp + 2, plast);
-        load_chunk<GQ>(head, s, mn, woff, a0);
-        load_chunk<GQ>(head, s, mn + 1, woff, a1);
-        __builtin_amdgcn_sched_barrier(0);
-        if (pp + 1 < npairs)
-          accumulate_pair<GQ>(S.lut[m + 2 - m_begin], S.lut[m + 3 - m_begin], b0, b1, sel, acc);
-        __builtin_amdgcn_sched_barrier(0);
-        const int mq = m_begin + 2 * min(pp + 3, plast);
-        load_chunk<GQ>(head, s, mq, woff, b0);
-        load_chunk<GQ>(head, s, mq + 1, woff, b1);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+    for (int i = 0; i < 16; ++i) acc[i] = (v4i){0, 0, 0, 0};
+    for (int b = 0; b < nblk; ++b) {
+      const bool last = b + 1 == nblk;
+      const int nb = last ? 0 : b + 1;
+      const int nt = last ? min(tile + 1, tile_end - 1) : tile;
+      uint32_t x[8];
+      slice_indices(words, sel, x);
+      __builtin_amdgcn_sched_barrier(0);
+      load_slice(head, T.rowoff, nb, G, woff_of(nt), words);
+      __builtin_amdgcn_sched_barrier(0);
+      const uint4 av = T.A[b][G][col];
+      const v4i A = {static_cast<int>(av.x), static_cast<int>(av.y), static_cast<int>(av.z), static_cast<int>(av.w)};
+      mfma_block(x, A, acc);
+      __builtin_amdgcn_sched_barrier(0);
     }
 
-    // epilogue: finish scores, optional dump, then the threshold filter.
-    // Candidates are appended with one atomic per (wave, query): each lane
-    // counts its passing keys, a wave prefix sum gives every lane its offset.
+    // epilogue: this lane holds query G's four limb sums for the 16 keys of
+    // its half word; combine, optional dump, threshold filter
+    const int w = word_of(tile);
     const int64_t key0 = int64_t(w) * 32 + 16 * half;
-    const int nvalid = active ? static_cast<int>(max<int64_t>(0, min<int64_t>(16, a.n - key0))) : 0;
+    const int nvalid = (w < a.nwords && qvalid) ? static_cast<int>(max<int64_t>(0, min<int64_t>(16, a.n - key0))) : 0;
+    float sc[16];
 #pragma unroll
-    for (int b = 0; b < 16; ++b)
-#pragma unroll
-      for (int g = 0; g < GQ; ++g) acc[b][g] += s.C[g];
+    for (int i = 0; i < 16; ++i) {
+      float tsum = static_cast<float>(acc[i].w);
+      tsum = fmaf(tsum, 256.0f, static_cast<float>(acc[i].z));
+      tsum = fmaf(tsum, 256.0f, static_cast<float>(acc[i].y));
+      tsum = fmaf(tsum, 256.0f, static_cast<float>(acc[i].x));
+      sc[i] = fmaf(tsum, sigma, Cq);
+    }
     if (a.all_scores) {
 #pragma unroll
-      for (int g = 0; g < GQ; ++g)
-#pragma unroll
-        for (int b = 0; b < 16; ++b)
-          if (b < nvalid) a.all_scores[int64_t(q0 + g) * a.n + key0 + b] = acc[b][g];
+      for (int i = 0; i < 16; ++i)
+        if (i < nvalid) a.all_scores[int64_t(q0 + G) * a.n + key0 + i] = sc[i];
     }
-    // Per query: each lane's passing keys -> wave prefix sum -> the wave's
-    // count goes to the workgroup's LDS tally (its offset there comes back),
-    // then one global atomic per (workgroup, query) reserves the slots.
-    uint32_t bits[GQ], lane_off[GQ], wave_off[GQ];
+    uint32_t bits = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) bits |= (i < nvalid && sc[i] >= theta) ? (1u << i) : 0u;
+    // Candidates go to this workgroup's LDS buffer: a DPP row holds one query
+    // (lanes 16G..16G+15), a row prefix sum orders its lanes and one LDS
+    // atomic per (wave, query) reserves the row's slots.  No barrier: each
+    // wave writes only the slots it reserved.  Slots past the buffer spill
+    // to the global list one by one.
+    const uint32_t mine = __popc(bits);
+    const uint32_t incl = row_incl_sum(mine);
+    uint32_t wave_off = 0;
 #pragma unroll
     for (int g = 0; g < GQ; ++g) {
-      const float th = s.theta[g];
-      uint32_t bm = 0;
-#pragma unroll
-      for (int b = 0; b < 16; ++b) bm |= (b < nvalid && acc[b][g] >= th) ? (1u << b) : 0u;
-      bits[g] = bm;
-      const uint32_t mine = __popc(bm);
-      const uint32_t incl = wave_incl_sum(mine);
-      lane_off[g] = incl - mine;
-      const uint32_t total = read_lane(incl, 63);
+      const uint32_t total = read_lane(incl, 16 * g + 15);
       uint32_t off = 0;
-      if (lane == 0 && total != 0) off = atomicAdd(&s.tally[g], total);
-      wave_off[g] = read_lane(off, 0);
+      if (lane == 0 && total != 0) off = atomicAdd(&tally[g], total);
+      off = read_lane(off, 0);
+      wave_off = G == g ? off : wave_off;
     }
-    __syncthreads();
-    if (threadIdx.x < GQ) {
-      // no wave touches tally between these two barriers, so it is reset here
-      const uint32_t t = s.tally[threadIdx.x];
-      s.tally[threadIdx.x] = 0u;
-      s.base[threadIdx.x] = t ? atomicAdd(&a.count[q0 + threadIdx.x], t) : 0u;
-    }
-    __syncthreads();
+    if (bits != 0) {
+      uint32_t slot = wave_off + incl - mine;
+      // static key index: a computed index into sc would move it to scratch
 #pragma unroll
-    for (int g = 0; g < GQ; ++g) {
-      if (bits[g] == 0) continue;
-      uint32_t slot = s.base[g] + wave_off[g] + lane_off[g];
-      // static key index: a computed index into acc would move the whole
-      // accumulator array to scratch memory
-#pragma unroll
-      for (int b = 0; b < 16; ++b) {
-        if (bits[g] & (1u << b)) {
-          if (slot < static_cast<uint32_t>(kCandCap))
-            a.cand[int64_t(q0 + g) * kCandCap + slot] =
-                make_uint2(__float_as_uint(acc[b][g]), static_cast<uint32_t>(key0 + b));
+      for (int i = 0; i < 16; ++i) {
+        if (bits & (1u << i)) {
+          const uint2 e = make_uint2(__float_as_uint(sc[i]), static_cast<uint32_t>(key0 + i));
+          if (slot < static_cast<uint32_t>(kLdsCand)) {
+            cbuf[G][slot] = e;
+          } else {
+            const uint32_t gs = atomicAdd(&a.count[q0 + G], 1u);
+            if (gs < static_cast<uint32_t>(kCandCap)) a.cand[int64_t(q0 + G) * kCandCap + gs] = e;
+          }
           ++slot;
         }
       }
     }
+  }
+  // flush: one global atomic per query reserves the buffered candidates' slots
+  __syncthreads();
+  if (threadIdx.x < GQ) {
+    const uint32_t kept = min(tally[threadIdx.x], static_cast<uint32_t>(kLdsCand));
+    tally[threadIdx.x] = kept;
+    cbase[threadIdx.x] = kept ? atomicAdd(&a.count[q0 + threadIdx.x], kept) : 0u;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int g = 0; g < GQ; ++g) {
+    const uint32_t kept = tally[g], b0 = cbase[g];
+    for (uint32_t i = threadIdx.x; i < kept; i += blockDim.x)
+      if (b0 + i < static_cast<uint32_t>(kCandCap)) a.cand[int64_t(q0 + g) * kCandCap + b0 + i] = cbuf[g][i];
   }
 }
 
@@ -1159,6 +1212,7 @@ hipError_t launch_scan_topk(const uint32_t* planes, const float* lo, const float
   a.count = ws.count;
   a.sample = ws.sample;
   a.cand = ws.cand;
+  a.tables = ws.tables;
   a.all_scores = all_scores;
 
   // sampled blocks: up to 8 blocks of 1024 keys spread evenly over the head
@@ -1179,12 +1233,14 @@ hipError_t launch_scan_topk(const uint32_t* planes, const float* lo, const float
   if (rsel < rmin) rsel = rmin;
   if (rsel > svalid) rsel = svalid;
 
-  // main-kernel work split: one resident workgroup per CU (the LUT fills LDS)
+  // main-kernel work split: kMainWgPerCu resident workgroups per CU, each
+  // taking a contiguous run of tiles of one (head, query chunk)
   const int full = group / kQueryChunk;
   const int rest = group % kQueryChunk;
-  const int64_t chunk_count = int64_t(H) * (full + (rest > 0 ? 1 : 0));
+  a.chunks_per_head = full + (rest > 0 ? 1 : 0);
+  const int64_t chunk_count = int64_t(H) * a.chunks_per_head;
   const int64_t total_tiles = chunk_count * a.tiles;
-  const int64_t target_wgs = 256;
+  const int64_t target_wgs = 256 * kMainWgPerCu;
   a.tiles_per_wg = static_cast<int>((total_tiles + target_wgs - 1) / target_wgs);
   if (a.tiles_per_wg < 1) a.tiles_per_wg = 1;
 
