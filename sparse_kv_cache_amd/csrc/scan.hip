@@ -36,6 +36,8 @@
 
 #include <hip/hip_ext.h>
 
+#include <type_traits>
+
 #include "fathom_internal.h"
 
 namespace fathom {
@@ -110,6 +112,10 @@ struct ChunkTable {
 };
 static_assert(sizeof(ChunkTable) <= kChunkTableBytes, "chunk table fits its workspace slot");
 static_assert(sizeof(ChunkTable) % 16 == 0, "chunk tables are copied as uint4");
+
+// K blocks of a union of U planes; at least one, so an empty union is one
+// block of zero weights
+__host__ __device__ inline int nblocks_of(int U) { return U > 0 ? (U + kBlockPlanes - 1) / kBlockPlanes : 1; }
 
 __device__ inline int chunk_index(const ScanArgs& a) {
   const int h = blockIdx.y / a.cph;
@@ -282,9 +288,8 @@ __device__ void build_limbs(const UnionLds<GQ>& s, ChunkTable& T, double (&wsum)
 template <int GQ>
 __device__ void write_chunk_table(const ScanArgs& a, const UnionLds<GQ>& s, ChunkTable& T, double (&wsum)[4]) {
   const int U = s.U;
-  const int nblk = (U + kBlockPlanes - 1) / kBlockPlanes;
-  for (int i = threadIdx.x; i < kMaxUnion + kPadPlanes; i += blockDim.x)
-    T.rowoff[i] = i < nblk * kBlockPlanes ? s.rowoff[i] : 0u;
+  const int nblk = nblocks_of(U);
+  for (int i = threadIdx.x; i < kMaxUnion + kPadPlanes; i += blockDim.x) T.rowoff[i] = i < U ? s.rowoff[i] : 0u;
   if (threadIdx.x < 4) T.C[threadIdx.x] = static_cast<int>(threadIdx.x) < GQ ? s.C[threadIdx.x] : 0.0f;
   if (threadIdx.x == 0) T.U = U;
   build_limbs<GQ>(s, T, wsum, nblk);   // ends with a barrier
@@ -425,46 +430,57 @@ __device__ inline void hist_add(uint32_t* wave_hist, bool on, uint32_t bin) {
   }
 }
 
-// Block-wide max and min of the present values (ordered keys).
+// Presence mask of a thread's register values: bit j set when value j
+// (element tid + j * blockDim.x) is one of the first `count` elements.
 template <int PT>
-__device__ uint2 block_max_min(const uint32_t (&v)[PT], uint32_t count, SelectLds& L) {
+__device__ inline uint32_t present_below(uint32_t count) {
+  uint32_t pm = 0;
+#pragma unroll
+  for (int j = 0; j < PT; ++j) pm |= (threadIdx.x + j * blockDim.x < count) ? (1u << j) : 0u;
+  return pm;
+}
+
+// Block-wide max, min and number of the present values (ordered keys;
+// value j of a thread is present when bit j of pm is set).
+template <int PT>
+__device__ uint3 block_max_min(const uint32_t (&v)[PT], uint32_t pm, SelectLds& L) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint32_t mx = 0u, mn = 0xffffffffu;
 #pragma unroll
   for (int j = 0; j < PT; ++j) {
-    const uint32_t i = tid + j * blockDim.x;
-    if (i < count) {
+    if ((pm >> j) & 1u) {
       mx = max(mx, v[j]);
       mn = min(mn, v[j]);
     }
   }
   const uint2 w = wave_max_min(mx, mn);
-  mx = w.x;
-  mn = w.y;
+  const uint32_t c = read_lane(wave_incl_sum(static_cast<uint32_t>(__popc(pm))), 63);
   if (lane == 0) {
-    L.hist[wave][0] = mx;
-    L.hist[wave][1] = mn;
+    L.hist[wave][0] = w.x;
+    L.hist[wave][1] = w.y;
+    L.hist[wave][2] = c;
   }
   __syncthreads();
   mx = 0u;
   mn = 0xffffffffu;
-  for (int w = 0; w < static_cast<int>(blockDim.x >> 6); ++w) {
-    mx = max(mx, L.hist[w][0]);
-    mn = min(mn, L.hist[w][1]);
+  uint32_t cnt = 0;
+  for (int ww = 0; ww < static_cast<int>(blockDim.x >> 6); ++ww) {
+    mx = max(mx, L.hist[ww][0]);
+    mn = min(mn, L.hist[ww][1]);
+    cnt += L.hist[ww][2];
   }
   __syncthreads();
-  return make_uint2(mx, mn);
+  return make_uint3(mx, mn, cnt);
 }
 
-// r-th largest (1-based, r <= count) of the ordered keys v[j] held by the
-// block's threads (value j of thread t is element t + j*blockDim.x, present
-// when < count).  Returns (key, r minus the number of values strictly above
-// the key).  Radix select, 8 bits per pass, starting at the highest byte in
-// which the present values differ.
+// r-th largest (1-based, r <= number present) of the present ordered keys
+// v[j] held by the block's threads.  Returns (key, r minus the number of
+// values strictly above the key).  Radix select, 8 bits per pass, starting
+// at the highest byte in which the present values differ.
 template <int PT>
-__device__ uint2 block_select_regs(const uint32_t (&v)[PT], uint32_t count, uint32_t r, SelectLds& L) {
-  const int tid = threadIdx.x, wave = tid >> 6;
-  const uint2 mm = block_max_min<PT>(v, count, L);
+__device__ uint2 block_select_regs(const uint32_t (&v)[PT], uint32_t pm, uint32_t r, SelectLds& L) {
+  const int wave = threadIdx.x >> 6;
+  const uint3 mm = block_max_min<PT>(v, pm, L);
   const uint32_t diff = mm.x ^ mm.y;
   if (diff == 0) return make_uint2(mm.x, r);          // all present values equal
   const int top = (31 - __clz(diff)) & ~7;             // shift of the highest differing byte
@@ -473,10 +489,8 @@ __device__ uint2 block_select_regs(const uint32_t (&v)[PT], uint32_t count, uint
   for (int shift = top; shift >= 0; shift -= 8) {
     clear_hist(L);
 #pragma unroll
-    for (int j = 0; j < PT; ++j) {
-      const uint32_t i = tid + j * blockDim.x;
-      hist_add(L.hist[wave], i < count && (v[j] & pmask) == prefix, (v[j] >> shift) & 255u);
-    }
+    for (int j = 0; j < PT; ++j)
+      hist_add(L.hist[wave], ((pm >> j) & 1u) && (v[j] & pmask) == prefix, (v[j] >> shift) & 255u);
     __syncthreads();
     const uint2 b = select_bin(L, r);
     prefix |= b.x << shift;
@@ -594,7 +608,8 @@ __global__ __launch_bounds__(kSelectThreads) void scan_threshold_kernel(
     v[j] = i < stot ? float_to_ordered(__uint_as_float(v[j])) : 0u;
   }
   digit_clear(D);
-  const uint2 mm = block_max_min<PT>(v, static_cast<uint32_t>(stot), L);
+  const uint32_t pm = present_below<PT>(static_cast<uint32_t>(stot));
+  const uint3 mm = block_max_min<PT>(v, pm, L);
   uint32_t th = mm.x;
   if (mm.x != mm.y) {
     uint32_t r = rsel - 1u;
@@ -605,10 +620,7 @@ __global__ __launch_bounds__(kSelectThreads) void scan_threshold_kernel(
       const int width = min(kDigitBits, hi), shift = hi - width;
       const uint32_t dmask = (1u << width) - 1u;
 #pragma unroll
-      for (int j = 0; j < PT; ++j) {
-        const int i = tid + j * kSelectThreads;
-        hist_add(D.hist, i < stot && (v[j] & pmask) == prefix, (v[j] >> shift) & dmask);
-      }
+      for (int j = 0; j < PT; ++j) hist_add(D.hist, ((pm >> j) & 1u) && (v[j] & pmask) == prefix, (v[j] >> shift) & dmask);
       __syncthreads();
       digit_scan(D, r);
       prefix |= D.bstar << shift;
@@ -669,9 +681,10 @@ template <int GQ>
 __device__ void build_limbs(const UnionLds<GQ>& s, ChunkTable& T, double (&wsum)[4], int nblk) {
   const int t = threadIdx.x;
   const int P = nblk * kBlockPlanes;
+  const int U = s.U;
   if (t < 64) {
     double acc[4] = {0.0, 0.0, 0.0, 0.0};
-    for (int p = t; p < P; p += 64)
+    for (int p = t; p < U; p += 64)
 #pragma unroll
       for (int g = 0; g < 4; ++g) acc[g] += fabs(static_cast<double>(s.w[p][g]));
 #pragma unroll
@@ -687,7 +700,7 @@ __device__ void build_limbs(const UnionLds<GQ>& s, ChunkTable& T, double (&wsum)
   for (int i = t; i < P * 4; i += blockDim.x) {
     const int p = i >> 2, g = i & 3;
     const double ws = wsum[g];
-    long long v = ws > 0.0 ? llrint(static_cast<double>(s.w[p][g]) * (0x1p30 / ws)) : 0ll;
+    long long v = (ws > 0.0 && p < U) ? llrint(static_cast<double>(s.w[p][g]) * (0x1p30 / ws)) : 0ll;
     const int b = p / kBlockPlanes, G = (p % kBlockPlanes) / 16, byte = p % 16;
     uint8_t* row = reinterpret_cast<uint8_t*>(&T.A[b][G][0]);
 #pragma unroll
@@ -721,8 +734,11 @@ __device__ __forceinline__ void slice_indices(const uint32_t (&w)[16], uint32_t 
 }
 
 // One K block: per key of the half word, its 16 plane bits become 16 bytes
-// of 0/1 (the B operand) and the key position gets one MFMA.
+// of 0/1 (the B operand) and the key position gets one MFMA.  The first
+// block of a tile starts from a zero accumulator (an inline constant).
+template <bool FIRST>
 __device__ __forceinline__ void mfma_block(const uint32_t (&x)[8], v4i A, v4i (&acc)[16]) {
+  const v4i zero = {0, 0, 0, 0};
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
 #pragma unroll
@@ -732,7 +748,7 @@ __device__ __forceinline__ void mfma_block(const uint32_t (&x)[8], v4i A, v4i (&
       bv.y = spread4(__builtin_amdgcn_ubfe(x[k], 8 * h + 4, 4));
       bv.z = spread4(__builtin_amdgcn_ubfe(x[k], 16 + 8 * h, 4));
       bv.w = spread4(__builtin_amdgcn_ubfe(x[k], 20 + 8 * h, 4));
-      acc[8 * h + k] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, bv, acc[8 * h + k], 0, 0, 0);
+      acc[8 * h + k] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, bv, FIRST ? zero : acc[8 * h + k], 0, 0, 0);
     }
   }
 }
@@ -750,8 +766,10 @@ template <int GQ>
 __global__ __launch_bounds__(kMainThreads, kMainWgPerCu) void scan_main_kernel(ScanArgs a) {
   __shared__ ChunkTable T;
   __shared__ uint2 cbuf[4][kLdsCand];   // this workgroup's candidates per query
-  __shared__ uint32_t tally[4], cbase[4];
+  __shared__ unsigned long long tally2[2];   // candidate counts of queries (0,1) and (2,3)
+  __shared__ uint32_t cbase[4];
   __shared__ float theta_s[4];
+  uint32_t* tally = reinterpret_cast<uint32_t*>(tally2);   // little endian: count of query g
   const int h = blockIdx.y / a.cph;
   const int q0 = h * a.group + a.qoff + (blockIdx.y % a.cph) * kQueryChunk;
   {
@@ -765,7 +783,7 @@ __global__ __launch_bounds__(kMainThreads, kMainWgPerCu) void scan_main_kernel(S
     }
   }
   __syncthreads();
-  const int nblk = (T.U + kBlockPlanes - 1) / kBlockPlanes;
+  const int nblk = nblocks_of(T.U);
 
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -780,6 +798,18 @@ __global__ __launch_bounds__(kMainThreads, kMainWgPerCu) void scan_main_kernel(S
   const float sigma = T.sigma[G];
   const float Cq = T.C[G];
   const float theta = theta_s[G];
+  // The filter runs on the unscaled limb sum t (score = fma(t, sigma, C)):
+  // t >= theta_t is a necessary condition for score >= theta (the margin
+  // covers the roundings), so every key scoring >= theta is a candidate,
+  // plus possibly a few just below it; the merge checks that the k-th
+  // candidate scores >= theta.
+  float theta_t;
+  if (sigma > 0.0f) {
+    const float slack = (fabsf(theta) + fabsf(Cq)) * 0x1p-20f;
+    theta_t = (theta - Cq - slack) / sigma - 1.0f;
+  } else {
+    theta_t = Cq >= theta ? -INFINITY : INFINITY;   // every score equals C
+  }
 
   auto word_of = [&](int tile) { return tile * kTileWords + wave * kWaveWords + (col >> 1); };
   auto woff_of = [&](int tile) {
@@ -792,12 +822,10 @@ __global__ __launch_bounds__(kMainThreads, kMainWgPerCu) void scan_main_kernel(S
   // block of a tile is block 0 of the next tile), which are in flight while
   // the block's MFMAs run.
   uint32_t words[16];
-  if (nblk > 0 && tile_begin < tile_end) load_slice(head, T.rowoff, 0, G, woff_of(tile_begin), words);
+  if (tile_begin < tile_end) load_slice(head, T.rowoff, 0, G, woff_of(tile_begin), words);
   for (int tile = tile_begin; tile < tile_end; ++tile) {
     v4i acc[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = (v4i){0, 0, 0, 0};
-    for (int b = 0; b < nblk; ++b) {
+    auto step = [&](auto first, int b) {
       const bool last = b + 1 == nblk;
       const int nb = last ? 0 : b + 1;
       const int nt = last ? min(tile + 1, tile_end - 1) : tile;
@@ -808,60 +836,83 @@ __global__ __launch_bounds__(kMainThreads, kMainWgPerCu) void scan_main_kernel(S
       __builtin_amdgcn_sched_barrier(0);
       const uint4 av = T.A[b][G][col];
       const v4i A = {static_cast<int>(av.x), static_cast<int>(av.y), static_cast<int>(av.z), static_cast<int>(av.w)};
-      mfma_block(x, A, acc);
+      mfma_block<decltype(first)::value>(x, A, acc);
       __builtin_amdgcn_sched_barrier(0);
-    }
+    };
+    step(std::true_type{}, 0);   // nblk >= 1: an empty union is one block of zero weights
+    for (int b = 1; b < nblk; ++b) step(std::false_type{}, b);
 
     // epilogue: this lane holds query G's four limb sums for the 16 keys of
-    // its half word; combine, optional dump, threshold filter
+    // its half word.  t = l0 + 2^8 l1 + 2^16 l2 + 2^24 l3 is formed from two
+    // exact int32 halves (|l| <= 128 * 512).
     const int w = word_of(tile);
     const int64_t key0 = int64_t(w) * 32 + 16 * half;
     const int nvalid = (w < a.nwords && qvalid) ? static_cast<int>(max<int64_t>(0, min<int64_t>(16, a.n - key0))) : 0;
-    float sc[16];
+    float tv[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      float tsum = static_cast<float>(acc[i].w);
-      tsum = fmaf(tsum, 256.0f, static_cast<float>(acc[i].z));
-      tsum = fmaf(tsum, 256.0f, static_cast<float>(acc[i].y));
-      tsum = fmaf(tsum, 256.0f, static_cast<float>(acc[i].x));
-      sc[i] = fmaf(tsum, sigma, Cq);
+      const float hi = static_cast<float>((acc[i].w << 8) + acc[i].z);
+      const float lo = static_cast<float>((acc[i].y << 8) + acc[i].x);
+      tv[i] = fmaf(hi, 65536.0f, lo);
     }
     if (a.all_scores) {
 #pragma unroll
       for (int i = 0; i < 16; ++i)
-        if (i < nvalid) a.all_scores[int64_t(q0 + G) * a.n + key0 + i] = sc[i];
+        if (i < nvalid) a.all_scores[int64_t(q0 + G) * a.n + key0 + i] = fmaf(tv[i], sigma, Cq);
     }
     uint32_t bits = 0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) bits |= (i < nvalid && sc[i] >= theta) ? (1u << i) : 0u;
+    for (int i = 0; i < 16; ++i) bits |= tv[i] >= theta_t ? (1u << i) : 0u;
+    bits &= nvalid >= 16 ? 0xffffu : ((1u << nvalid) - 1u);
     // Candidates go to this workgroup's LDS buffer: a DPP row holds one query
     // (lanes 16G..16G+15), a row prefix sum orders its lanes and one LDS
     // atomic per (wave, query) reserves the row's slots.  No barrier: each
     // wave writes only the slots it reserved.  Slots past the buffer spill
-    // to the global list one by one.
+    // to the global list, reserved the same way with one global atomic per
+    // (wave, query).
     const uint32_t mine = __popc(bits);
     const uint32_t incl = row_incl_sum(mine);
     uint32_t wave_off = 0;
+    {
+      // row totals of queries 0..3, reserved with two packed 64-bit atomics
+      const uint32_t t0 = read_lane(incl, 15), t1 = read_lane(incl, 31);
+      const uint32_t t2 = read_lane(incl, 47), t3 = read_lane(incl, 63);
+      unsigned long long o01 = 0, o23 = 0;
+      if (lane == 0) {
+        if ((t0 | t1) != 0) o01 = atomicAdd(&tally2[0], static_cast<unsigned long long>(t0) | (static_cast<unsigned long long>(t1) << 32));
+        if ((t2 | t3) != 0) o23 = atomicAdd(&tally2[1], static_cast<unsigned long long>(t2) | (static_cast<unsigned long long>(t3) << 32));
+      }
+      const uint32_t offs[4] = {read_lane(static_cast<uint32_t>(o01), 0), read_lane(static_cast<uint32_t>(o01 >> 32), 0),
+                                read_lane(static_cast<uint32_t>(o23), 0), read_lane(static_cast<uint32_t>(o23 >> 32), 0)};
+      wave_off = G == 0 ? offs[0] : G == 1 ? offs[1] : G == 2 ? offs[2] : offs[3];
+    }
+    const uint32_t slot0 = wave_off + incl - mine;
+    const uint32_t cap = static_cast<uint32_t>(kLdsCand);
+    const uint32_t spill = slot0 + mine > cap ? slot0 + mine - max(slot0, cap) : 0u;
+    uint32_t gpos = 0;
+    if (__ballot(spill != 0) != 0) {   // uniform; rare
+      const uint32_t sincl = row_incl_sum(spill);
 #pragma unroll
-    for (int g = 0; g < GQ; ++g) {
-      const uint32_t total = read_lane(incl, 16 * g + 15);
-      uint32_t off = 0;
-      if (lane == 0 && total != 0) off = atomicAdd(&tally[g], total);
-      off = read_lane(off, 0);
-      wave_off = G == g ? off : wave_off;
+      for (int g = 0; g < GQ; ++g) {
+        const uint32_t total = read_lane(sincl, 16 * g + 15);
+        uint32_t gb = 0;
+        if (lane == 0 && total != 0) gb = atomicAdd(&a.count[q0 + g], total);
+        gb = read_lane(gb, 0);
+        gpos = G == g ? gb + sincl - spill : gpos;
+      }
     }
     if (bits != 0) {
-      uint32_t slot = wave_off + incl - mine;
-      // static key index: a computed index into sc would move it to scratch
+      uint32_t slot = slot0;
+      // static key index: a computed index into tv would move it to scratch
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         if (bits & (1u << i)) {
-          const uint2 e = make_uint2(__float_as_uint(sc[i]), static_cast<uint32_t>(key0 + i));
-          if (slot < static_cast<uint32_t>(kLdsCand)) {
+          const uint2 e = make_uint2(__float_as_uint(fmaf(tv[i], sigma, Cq)), static_cast<uint32_t>(key0 + i));
+          if (slot < cap) {
             cbuf[G][slot] = e;
           } else {
-            const uint32_t gs = atomicAdd(&a.count[q0 + G], 1u);
-            if (gs < static_cast<uint32_t>(kCandCap)) a.cand[int64_t(q0 + G) * kCandCap + gs] = e;
+            if (gpos < static_cast<uint32_t>(kCandCap)) a.cand[int64_t(q0 + G) * kCandCap + gpos] = e;
+            ++gpos;
           }
           ++slot;
         }
@@ -1014,7 +1065,8 @@ __global__ __launch_bounds__(kSelectThreads) void scan_merge_kernel(ScanArgs a, 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const uint32_t cnt = a.count[q];
-  unsigned kept;
+  unsigned kept = 0;
+  bool fast = false;   // uniform
 
   if (cnt >= static_cast<uint32_t>(k) && cnt <= static_cast<uint32_t>(kCandCap)) {
     const uint2* cand = a.cand + int64_t(q) * kCandCap;
@@ -1027,76 +1079,82 @@ __global__ __launch_bounds__(kSelectThreads) void scan_merge_kernel(ScanArgs a, 
       v[j] = e.x;
       id[j] = e.y;
     }
+    // The scan's filter may also pass keys just below theta; only candidates
+    // scoring >= theta count, and the list is complete for the top k exactly
+    // when at least k of them do.
+    const uint32_t theta_o = float_to_ordered(a.theta[q]);
+    uint32_t pm = 0;
 #pragma unroll
     for (int j = 0; j < PT; ++j) {
       const uint32_t i = tid + j * kSelectThreads;
       v[j] = i < cnt ? float_to_ordered(__uint_as_float(v[j])) : 0u;
+      pm |= (i < cnt && v[j] >= theta_o) ? (1u << j) : 0u;
     }
-    // Fast path: one digit pass puts the candidates into ordered buckets;
-    // those at or above the bucket holding rank k-1 are scattered in bucket
-    // order and each is placed by counting the larger keys of its bucket.
     DigitLds& D = *reinterpret_cast<DigitLds*>(keys + kFastKept);
     digit_clear(D);
-    const uint2 mm = block_max_min<PT>(v, cnt, L);
-    bool placed = false;
-    if (mm.x != mm.y) {
-      const int hi = 32 - __clz(mm.x ^ mm.y);
-      const int width = min(kDigitBits, hi), shift = hi - width;
-      const uint32_t dmask = (1u << width) - 1u;
+    const uint3 mm = block_max_min<PT>(v, pm, L);
+    if (mm.z >= static_cast<uint32_t>(k)) {
+      fast = true;
+      // Fast path: one digit pass puts the candidates into ordered buckets;
+      // those at or above the bucket holding rank k-1 are scattered in
+      // bucket order and each is placed by counting the larger keys of its
+      // bucket.
+      bool placed = false;
+      if (mm.x != mm.y) {
+        const int hi = 32 - __clz(mm.x ^ mm.y);
+        const int width = min(kDigitBits, hi), shift = hi - width;
+        const uint32_t dmask = (1u << width) - 1u;
+#pragma unroll
+        for (int j = 0; j < PT; ++j) hist_add(D.hist, (pm >> j) & 1u, (v[j] >> shift) & dmask);
+        __syncthreads();
+        digit_scan(D, static_cast<uint32_t>(k) - 1u);
+        if (D.big == 0u) {
+          const uint32_t bstar = D.bstar;
+          const uint32_t nkeep = D.bstart + D.bcount;   // <= k - 1 + kBucketMax
+#pragma unroll
+          for (int j = 0; j < PT; ++j) {
+            const uint32_t d = (v[j] >> shift) & dmask;
+            if (((pm >> j) & 1u) && d >= bstar) keys[D.start[d] + atomicAdd(&D.cursor[d], 1u)] = sort_key(v[j], id[j]);
+          }
+          __syncthreads();
+          for (uint32_t p = tid; p < nkeep; p += kSelectThreads) {
+            const unsigned long long key = keys[p];
+            const uint32_t d = (static_cast<uint32_t>(key >> 32) >> shift) & dmask;
+            const uint32_t b0 = D.start[d], c = D.hist[d];
+            uint32_t rank = 0;
+            for (uint32_t i = 0; i < c; ++i) rank += keys[b0 + i] > key ? 1u : 0u;
+            const uint32_t pos = b0 + rank;
+            if (pos < static_cast<uint32_t>(k)) {
+              out_idx[int64_t(q) * k + pos] = static_cast<int32_t>(~static_cast<uint32_t>(key));
+              out_score[int64_t(q) * k + pos] = ordered_to_float(static_cast<uint32_t>(key >> 32));
+            }
+          }
+          placed = true;
+        }
+      }
+      if (placed) return;
+      // General path (all scores equal, or a bucket too large to order by
+      // counting): the k-th best candidate score by radix select; every
+      // candidate at or above it is kept and sorted.
+      const uint2 sel = block_select_regs<PT>(v, pm, static_cast<uint32_t>(k), L);
+      if (tid == 0) s_count[0] = 0;
+      __syncthreads();
+      // compaction: one LDS atomic per wave and register slot
 #pragma unroll
       for (int j = 0; j < PT; ++j) {
-        const uint32_t i = tid + j * kSelectThreads;
-        hist_add(D.hist, i < cnt, (v[j] >> shift) & dmask);
+        const bool keep = ((pm >> j) & 1u) && v[j] >= sel.x;
+        const uint64_t bal = __ballot(keep);
+        if (bal == 0) continue;
+        uint32_t base = 0;
+        if (lane == 0) base = atomicAdd(&s_count[0], static_cast<uint32_t>(__popcll(bal)));
+        base = read_lane(base, 0);
+        if (keep) keys[base + lanes_below(bal)] = sort_key(v[j], id[j]);
       }
       __syncthreads();
-      digit_scan(D, static_cast<uint32_t>(k) - 1u);
-      if (D.big == 0u) {
-        const uint32_t bstar = D.bstar;
-        const uint32_t nkeep = D.bstart + D.bcount;   // <= k - 1 + kBucketMax
-#pragma unroll
-        for (int j = 0; j < PT; ++j) {
-          const uint32_t i = tid + j * kSelectThreads;
-          const uint32_t d = (v[j] >> shift) & dmask;
-          if (i < cnt && d >= bstar) keys[D.start[d] + atomicAdd(&D.cursor[d], 1u)] = sort_key(v[j], id[j]);
-        }
-        __syncthreads();
-        for (uint32_t p = tid; p < nkeep; p += kSelectThreads) {
-          const unsigned long long key = keys[p];
-          const uint32_t d = (static_cast<uint32_t>(key >> 32) >> shift) & dmask;
-          const uint32_t b0 = D.start[d], c = D.hist[d];
-          uint32_t rank = 0;
-          for (uint32_t i = 0; i < c; ++i) rank += keys[b0 + i] > key ? 1u : 0u;
-          const uint32_t pos = b0 + rank;
-          if (pos < static_cast<uint32_t>(k)) {
-            out_idx[int64_t(q) * k + pos] = static_cast<int32_t>(~static_cast<uint32_t>(key));
-            out_score[int64_t(q) * k + pos] = ordered_to_float(static_cast<uint32_t>(key >> 32));
-          }
-        }
-        placed = true;
-      }
+      kept = s_count[0];
     }
-    if (placed) return;
-    // General path (all scores equal, or a bucket too large to order by
-    // counting): the k-th best candidate score by radix select; every
-    // candidate at or above it is kept and sorted.
-    const uint2 sel = block_select_regs<PT>(v, cnt, static_cast<uint32_t>(k), L);
-    if (tid == 0) s_count[0] = 0;
-    __syncthreads();
-    // compaction: one LDS atomic per wave and register slot
-#pragma unroll
-    for (int j = 0; j < PT; ++j) {
-      const uint32_t i = tid + j * kSelectThreads;
-      const bool keep = i < cnt && v[j] >= sel.x;
-      const uint64_t bal = __ballot(keep);
-      if (bal == 0) continue;
-      uint32_t base = 0;
-      if (lane == 0) base = atomicAdd(&s_count[0], static_cast<uint32_t>(__popcll(bal)));
-      base = read_lane(base, 0);
-      if (keep) keys[base + lanes_below(bal)] = sort_key(v[j], id[j]);
-    }
-    __syncthreads();
-    kept = s_count[0];
-  } else {
+  }
+  if (!fast) {
     // exact fallback: radix select over recomputed scores
     const int h = q / a.group;
     const uint32_t* head_planes = a.planes + int64_t(h) * kD * kPlanes * a.ldw;

@@ -206,6 +206,21 @@ def test_massive_ties_in_candidate_list(n_dup):
     assert np.array_equal(res["idx"][0], dup[:100])
 
 
+def test_clustered_candidates_spill_to_global_list():
+    """The best keys of query 0 form one contiguous run of 4000 keys, so a
+    few workgroups of the scan each see far more candidates than their
+    on-chip buffer holds and spill the rest to the global list."""
+    say("clustered candidates")
+    n = 100000
+    keys, q = synth.make_inputs(21, 1, n, 4)
+    rng = np.random.default_rng(5)
+    lo, hi = 30000, 34000
+    strong = np.sign(q[0]) * np.abs(keys[0]).max(axis=0) * 0.8
+    keys[0, lo:hi] = strong[None, :] + 0.05 * rng.standard_normal((hi - lo, 128)).astype(np.float32)
+    res, _ = check_full(keys, q, 4, 92, 2048)
+    assert np.all((res["idx"][0] >= lo) & (res["idx"][0] < hi))
+
+
 def test_constant_keys():
     say("constant keys")
     keys = np.full((1, 3000, 128), 2.5, np.float32)
