@@ -676,7 +676,8 @@ __device__ __forceinline__ int spread4(uint32_t n) { return static_cast<int>((n 
 // MFMA accumulates each limb exactly and the score is
 // C + sigma * (l0 + 2^8 l1 + 2^16 l2 + 2^24 l3).  Rows of the A operand are
 // (query g, limb) = 4g + limb; K slice G of block b covers union planes
-// 64b + 16G .. 64b + 16G + 15.  Fills T.A and T.sigma; wsum is LDS scratch.
+// 64b + 16G .. 64b + 16G + 15, in the byte order the B operand uses.
+// Fills T.A and T.sigma; wsum is LDS scratch.
 template <int GQ>
 __device__ void build_limbs(const UnionLds<GQ>& s, ChunkTable& T, double (&wsum)[4], int nblk) {
   const int t = threadIdx.x;
@@ -701,7 +702,9 @@ __device__ void build_limbs(const UnionLds<GQ>& s, ChunkTable& T, double (&wsum)
     const int p = i >> 2, g = i & 3;
     const double ws = wsum[g];
     long long v = (ws > 0.0 && p < U) ? llrint(static_cast<double>(s.w[p][g]) * (0x1p30 / ws)) : 0ll;
-    const int b = p / kBlockPlanes, G = (p % kBlockPlanes) / 16, byte = p % 16;
+    // slice plane pl sits at byte 4d + e with pl = (2d, 2d + 8, 2d + 1, 2d + 9)[e]
+    const int b = p / kBlockPlanes, G = (p % kBlockPlanes) / 16, pl = p % 16;
+    const int byte = pl < 8 ? 4 * (pl >> 1) + 2 * (pl & 1) : 4 * ((pl - 8) >> 1) + 1 + 2 * (pl & 1);
     uint8_t* row = reinterpret_cast<uint8_t*>(&T.A[b][G][0]);
 #pragma unroll
     for (int l = 0; l < 4; ++l) {
@@ -724,32 +727,32 @@ __device__ __forceinline__ void load_slice(const char* head, const uint32_t* row
     x[t] = *reinterpret_cast<const uint32_t*>(head + (rowoff[p0 + t] + woff));
 }
 
-// Packs this lane's halves of the two 8-plane groups of its 16 plane words
-// into one word per plane and transposes: byte h of x[k] holds planes 0..7
-// and byte 2 + h planes 8..15 of key 8h + k of the half word.
-__device__ __forceinline__ void slice_indices(const uint32_t (&w)[16], uint32_t sel, uint32_t (&x)[8]) {
+// Packs this lane's half of each pair of planes (m, m + 8) of its K slice
+// into one word: bits 0..15 hold plane m, bits 16..31 plane m + 8, bit i
+// of each half being key i of the half word.
+__device__ __forceinline__ void slice_pairs(const uint32_t (&w)[16], uint32_t sel, uint32_t (&x)[8]) {
 #pragma unroll
-  for (int t = 0; t < 8; ++t) x[t] = __builtin_amdgcn_perm(w[t + 8], w[t], sel);
-  transpose8x32(x);
+  for (int m = 0; m < 8; ++m) x[m] = __builtin_amdgcn_perm(w[m + 8], w[m], sel);
 }
 
-// One K block: per key of the half word, its 16 plane bits become 16 bytes
-// of 0/1 (the B operand) and the key position gets one MFMA.  The first
-// block of a tile starts from a zero accumulator (an inline constant).
+// One K block.  For key i of the half word, shifting a pair word left by
+// 15 - i puts key i's bits of its two planes at bits 15 and 31, and a
+// v_perm with sign-replicating selectors turns the four such bits of two
+// pair words into four bytes of 0x00 / 0xFF: the B operand holds 0 or -1,
+// byte 4d + e of the K slice being plane (2d, 2d + 8, 2d + 1, 2d + 9)[e].
+// The first block of a tile starts from a zero accumulator.
 template <bool FIRST>
-__device__ __forceinline__ void mfma_block(const uint32_t (&x)[8], v4i A, v4i (&acc)[16]) {
+__device__ __forceinline__ void mfma_block(const uint32_t (&x)[8], uint32_t sign_sel, v4i A, v4i (&acc)[16]) {
   const v4i zero = {0, 0, 0, 0};
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      v4i bv;
-      bv.x = spread4(__builtin_amdgcn_ubfe(x[k], 8 * h, 4));
-      bv.y = spread4(__builtin_amdgcn_ubfe(x[k], 8 * h + 4, 4));
-      bv.z = spread4(__builtin_amdgcn_ubfe(x[k], 16 + 8 * h, 4));
-      bv.w = spread4(__builtin_amdgcn_ubfe(x[k], 20 + 8 * h, 4));
-      acc[8 * h + k] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, bv, FIRST ? zero : acc[8 * h + k], 0, 0, 0);
-    }
+  for (int i = 0; i < 16; ++i) {
+    const int sh = 15 - i;
+    v4i bv;
+    bv.x = static_cast<int>(__builtin_amdgcn_perm(x[1] << sh, x[0] << sh, sign_sel));
+    bv.y = static_cast<int>(__builtin_amdgcn_perm(x[3] << sh, x[2] << sh, sign_sel));
+    bv.z = static_cast<int>(__builtin_amdgcn_perm(x[5] << sh, x[4] << sh, sign_sel));
+    bv.w = static_cast<int>(__builtin_amdgcn_perm(x[7] << sh, x[6] << sh, sign_sel));
+    acc[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, bv, FIRST ? zero : acc[i], 0, 0, 0);
   }
 }
 
@@ -791,6 +794,8 @@ __global__ __launch_bounds__(kMainThreads, kMainWgPerCu) void scan_main_kernel(S
   const int G = lane >> 4;              // K slice; in the result, the query of the lane
   const int half = col & 1;
   const uint32_t sel = half ? 0x07060302u : 0x05040100u;   // v_perm byte selectors
+  // selectors 8..11: 0xff if bit 15 / 31 / 47 / 63 of the 64-bit source is set
+  const uint32_t sign_sel = __builtin_amdgcn_readfirstlane(0x0b0a0908);
   const char* head = reinterpret_cast<const char*>(a.planes + int64_t(h) * kD * kPlanes * a.ldw);
   const int tile_begin = blockIdx.x * a.tiles_per_wg;
   const int tile_end = min(a.tiles, tile_begin + a.tiles_per_wg);
@@ -830,21 +835,22 @@ __global__ __launch_bounds__(kMainThreads, kMainWgPerCu) void scan_main_kernel(S
       const int nb = last ? 0 : b + 1;
       const int nt = last ? min(tile + 1, tile_end - 1) : tile;
       uint32_t x[8];
-      slice_indices(words, sel, x);
+      slice_pairs(words, sel, x);
       __builtin_amdgcn_sched_barrier(0);
       load_slice(head, T.rowoff, nb, G, woff_of(nt), words);
       __builtin_amdgcn_sched_barrier(0);
       const uint4 av = T.A[b][G][col];
       const v4i A = {static_cast<int>(av.x), static_cast<int>(av.y), static_cast<int>(av.z), static_cast<int>(av.w)};
-      mfma_block<decltype(first)::value>(x, A, acc);
+      mfma_block<decltype(first)::value>(x, sign_sel, A, acc);
       __builtin_amdgcn_sched_barrier(0);
     };
     step(std::true_type{}, 0);   // nblk >= 1: an empty union is one block of zero weights
     for (int b = 1; b < nblk; ++b) step(std::false_type{}, b);
 
     // epilogue: this lane holds query G's four limb sums for the 16 keys of
-    // its half word.  t = l0 + 2^8 l1 + 2^16 l2 + 2^24 l3 is formed from two
-    // exact int32 halves (|l| <= 128 * 512).
+    // its half word, negated (the B operand held -bit).  t = -(l0 + 2^8 l1 +
+    // 2^16 l2 + 2^24 l3) is formed from two exact int32 halves
+    // (|l| <= 128 * 512).
     const int w = word_of(tile);
     const int64_t key0 = int64_t(w) * 32 + 16 * half;
     const int nvalid = (w < a.nwords && qvalid) ? static_cast<int>(max<int64_t>(0, min<int64_t>(16, a.n - key0))) : 0;
@@ -853,7 +859,7 @@ __global__ __launch_bounds__(kMainThreads, kMainWgPerCu) void scan_main_kernel(S
     for (int i = 0; i < 16; ++i) {
       const float hi = static_cast<float>((acc[i].w << 8) + acc[i].z);
       const float lo = static_cast<float>((acc[i].y << 8) + acc[i].x);
-      tv[i] = fmaf(hi, 65536.0f, lo);
+      tv[i] = -fmaf(hi, 65536.0f, lo);
     }
     if (a.all_scores) {
 #pragma unroll
