@@ -26,6 +26,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "Gkeys/s and achieved HBM GB/s (% peak) for scan+top-k, 1M keys, B=92 bits"
 HBM_PEAK_GBS = 8000.0
+TIMING_EVERY = 4
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_main_qwen3_8b_1m_traffic.json")
 
 
@@ -82,13 +83,15 @@ def cpu_baseline(w, budget, target_s):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="qwen3_8b_1m")
     ap.add_argument("--budget", type=int, default=None)
     ap.add_argument("--copies", type=int, default=3, help="plane-store copies rotated across steps")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-timing", action="store_true",
+                    help="leave the main-kernel timing events off (for traces of the bare step)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this size (for counter calibration)")
     args = ap.parse_args()
@@ -149,8 +152,11 @@ def main():
         fa.scan_topk(copies[i % len(copies)], lo, step, store, qd, alloc, G, k, workspace=scan_ws,
                      out_idx=out_idx, out_score=out_score)
 
+    if not args.no_kernel_timing:
+        fa.timing_enable(True)    # creates the event pool outside the timed region
     for i in range(args.warmup):
         step_fn(i)
+    fa.timing_enable(False)
     torch.cuda.synchronize()
     alg_plane_bytes = union_bytes(alloc.cpu().numpy(), G, store.ldw)
     alg_bytes = alg_plane_bytes + H * d * 8 + Q * d * 5 + Q * k * 8
@@ -164,18 +170,25 @@ def main():
         torch.cuda.synchronize()
         log(f"calibration copy: {args.calibrate_copy_mib} MiB read + written per launch, 3 launches")
 
-    fa.timing_enable(True)
+    # The main kernel's duration is read from HIP events carried by its own
+    # dispatch, on every TIMING_EVERY-th step of the timed region (events on
+    # every launch would add their own gaps to the step).
+    fa.timing_read()   # clear the record
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
+        timed = not args.no_kernel_timing and i % TIMING_EVERY == 0
+        if timed:
+            fa.timing_enable(True)
         step_fn(i)
+        if timed:
+            fa.timing_enable(False)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     main_ms_total, launches = fa.timing_read()
-    fa.timing_enable(False)
 
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    main_ms = main_ms_total / max(launches, 1)
+    main_ms = main_ms_total / launches if launches else float("nan")
     gkeys = H * n / (ms_per_step * 1e-3) / 1e9
     achieved = alg_bytes / (main_ms * 1e-3) / 1e9
 

@@ -135,11 +135,12 @@ const char* fathom_status_string(int32_t status);
 /* Detail of the last error on the calling thread ("" if none). */
 const char* fathom_last_error(void);
 
-/* Kernel timing for measurement: when enabled, the library records HIP
- * events around the main scan kernel of each fathom_scan_topk call on the
- * call's stream.  fathom_timing_read synchronizes on those events and
+/* Kernel timing for measurement: while enabled, the library records HIP
+ * events carried by the dispatch of the main scan kernel of each
+ * fathom_scan_topk call (on the call's stream).  Enabling or disabling keeps
+ * the record; fathom_timing_read synchronizes on the recorded events,
  * returns the summed kernel time (ms) and the number of timed launches since
- * the last read, then clears the record.  At most 4096 launches are kept. */
+ * the last read, and clears the record.  At most 4096 launches are kept. */
 int fathom_timing_enable(int32_t enable);
 int fathom_timing_read(double* total_ms, int32_t* launches);
 

@@ -242,7 +242,6 @@ int fathom_timing_enable(int32_t enable) {
     }
   }
   g_timing_on = enable != 0;
-  g_events_used = 0;
   return ok();
 }
 

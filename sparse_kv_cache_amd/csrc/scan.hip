@@ -25,14 +25,20 @@
 //                            selects the exact top-k (ties by index).
 //
 // Main kernel.  A workgroup owns one KV head and a chunk of <= 4 of its GQA
-// query heads, and reads, once, the union of the chunk's plane prefixes.  The
-// union planes are taken 8 at a time ("LUT chunks"); for each chunk the
-// prologue tabulates, for all 256 patterns of the 8 bits, the partial score
-// of every query of the chunk (planes a query does not read weigh 0).  Lane =
-// one 32-key plane word: a lane loads its word of the chunk's 8 plane rows
-// (coalesced), transposes the 8x32 bit block in registers so that each key's
-// 8 bits form one byte, and adds one table entry per key.  No MFMA: the work
-// is a bit-sliced gather-accumulate, bound by VALU and LDS gathers.
+// query heads, and reads, once, the union U of the chunk's plane prefixes
+// (padded with zero-weight rows to whole 64-plane blocks).  The score is a
+// dense contraction over the union planes, S[q][key] = sum_p W[q][p] bit[p][key],
+// done on the matrix cores as v_mfma_i32_16x16x64_i8:
+//   A (16 x 64): each query's weights of the block in fixed point,
+//       V = round(W 2^30 / sum|W|), split into four balanced base-256 int8
+//       digits ("limbs"); row 4g+l holds limb l of query g;
+//   B (64 x 16): bit[p][key] as int8 0 or -1, built from the 32-bit plane
+//       words with byte permutes (no transpose: a column is a 2-key pair);
+// so one MFMA gives all 4 queries' 4 limb sums of 16 keys over 64 planes, and
+// the int32 sums recombine into sum_p V bit in fp32 (two roundings).  The weights'
+// tables (limbs, scale, offset C_q) are built once per chunk by the sample
+// kernel.  Keys whose score can reach theta are kept in an LDS buffer per
+// query and flushed to the global candidate list at the end.
 
 #include <hip/hip_ext.h>
 
@@ -49,7 +55,7 @@ constexpr int kMaxBlocks = kMaxUnion / kBlockPlanes;
 // the union is padded with readable zero-weight rows to whole K blocks
 constexpr int kPadPlanes = kBlockPlanes;
 constexpr int kMainThreads = 256;              // 4 wavefronts
-constexpr int kMainWgPerCu = 3;                // register budget: 3 resident workgroups per CU
+constexpr int kMainWgPerCu = 4;                // register budget: 4 resident workgroups per CU
 constexpr int kWaveWords = 8;                  // 16 MFMA columns = 8 words x 2 halves
 constexpr int kTileWords = (kMainThreads / 64) * kWaveWords;   // 32 words = 1024 keys
 constexpr int kLdsCand = 512;                 // candidates per query buffered in a main workgroup
@@ -302,6 +308,7 @@ __device__ void write_chunk_table(const ScanArgs& a, const UnionLds<GQ>& s, Chun
 
 // Workgroup = (quarter of a sampled 1024-key block, KV head, query chunk):
 // the union plane words of its 256 keys are staged in LDS, then thread = key.
+// One more workgroup per chunk writes the chunk's main-kernel table.
 template <int GQ>
 __global__ __launch_bounds__(kSampleThreads) void scan_sample_kernel(ScanArgs a) {
   constexpr int kWords = kSampleThreads / 32;
@@ -312,7 +319,12 @@ __global__ __launch_bounds__(kSampleThreads) void scan_sample_kernel(ScanArgs a)
   const int h = blockIdx.y / a.cph;
   const int q0 = h * a.group + a.qoff + (blockIdx.y % a.cph) * kQueryChunk;
   build_union<GQ>(a, h, q0, s);
-  if (blockIdx.x == 0) write_chunk_table<GQ>(a, s, T, wsum);   // uniform per workgroup
+  // the last workgroup of each chunk builds the main kernel's table instead
+  // of sampling, in parallel with the sampling workgroups
+  if (blockIdx.x == gridDim.x - 1) {   // uniform per workgroup
+    write_chunk_table<GQ>(a, s, T, wsum);
+    return;
+  }
 
   const int sbi = blockIdx.x / kSampleWgPerBlock;
   const int part = blockIdx.x % kSampleWgPerBlock;
@@ -642,41 +654,12 @@ __global__ __launch_bounds__(kSelectThreads) void scan_threshold_kernel(
 
 // -------------------------------------------------------------------- main
 
-// In-register transpose of an 8x32 bit block: on entry x[t] holds plane t's
-// bits of 32 keys (key b at bit b); on exit byte g of x[k] holds the 8 plane
-// bits of key 8g + k (plane t at bit t).  Three rounds of block swaps.
-__device__ __forceinline__ void transpose8x32(uint32_t (&x)[8]) {
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const uint32_t d = ((x[t] >> 4) ^ x[t + 4]) & 0x0f0f0f0fu;
-    x[t + 4] ^= d;
-    x[t] ^= d << 4;
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int t = (i & 1) + (i >> 1) * 4;    // 0, 1, 4, 5
-    const uint32_t d = ((x[t] >> 2) ^ x[t + 2]) & 0x33333333u;
-    x[t + 2] ^= d;
-    x[t] ^= d << 2;
-  }
-#pragma unroll
-  for (int t = 0; t < 8; t += 2) {
-    const uint32_t d = ((x[t] >> 1) ^ x[t + 1]) & 0x55555555u;
-    x[t + 1] ^= d;
-    x[t] ^= d << 1;
-  }
-}
-
-// Bit i of the 4-bit value n becomes byte i (0 or 1): the four shifted copies
-// n << 7i do not overlap, and copy i puts bit i at position 8i.
-__device__ __forceinline__ int spread4(uint32_t n) { return static_cast<int>((n * 0x00204081u) & 0x01010101u); }
-
 // Per query: fixed-point weights V = round(W / sigma) with sigma = sum|W| /
 // 2^30, split into four balanced base-256 digits (int8 limbs), so the int8
 // MFMA accumulates each limb exactly and the score is
 // C + sigma * (l0 + 2^8 l1 + 2^16 l2 + 2^24 l3).  Rows of the A operand are
 // (query g, limb) = 4g + limb; K slice G of block b covers union planes
-// 64b + 16G .. 64b + 16G + 15, in the byte order the B operand uses.
+// 64b + 16G .. 64b + 16G + 15, slice plane pl at byte pl.
 // Fills T.A and T.sigma; wsum is LDS scratch.
 template <int GQ>
 __device__ void build_limbs(const UnionLds<GQ>& s, ChunkTable& T, double (&wsum)[4], int nblk) {
@@ -702,9 +685,7 @@ __device__ void build_limbs(const UnionLds<GQ>& s, ChunkTable& T, double (&wsum)
     const int p = i >> 2, g = i & 3;
     const double ws = wsum[g];
     long long v = (ws > 0.0 && p < U) ? llrint(static_cast<double>(s.w[p][g]) * (0x1p30 / ws)) : 0ll;
-    // slice plane pl sits at byte 4d + e with pl = (2d, 2d + 8, 2d + 1, 2d + 9)[e]
-    const int b = p / kBlockPlanes, G = (p % kBlockPlanes) / 16, pl = p % 16;
-    const int byte = pl < 8 ? 4 * (pl >> 1) + 2 * (pl & 1) : 4 * ((pl - 8) >> 1) + 1 + 2 * (pl & 1);
+    const int b = p / kBlockPlanes, G = (p % kBlockPlanes) / 16, byte = p % 16;
     uint8_t* row = reinterpret_cast<uint8_t*>(&T.A[b][G][0]);
 #pragma unroll
     for (int l = 0; l < 4; ++l) {
@@ -727,31 +708,41 @@ __device__ __forceinline__ void load_slice(const char* head, const uint32_t* row
     x[t] = *reinterpret_cast<const uint32_t*>(head + (rowoff[p0 + t] + woff));
 }
 
-// Packs this lane's half of each pair of planes (m, m + 8) of its K slice
-// into one word: bits 0..15 hold plane m, bits 16..31 plane m + 8, bit i
-// of each half being key i of the half word.
-__device__ __forceinline__ void slice_pairs(const uint32_t (&w)[16], uint32_t sel, uint32_t (&x)[8]) {
+// Byte-transposes this lane's half word of the 16 planes of its K slice:
+// t[2d + o] holds, in byte e, byte o of the half word of slice plane 4d + e,
+// i.e. bit i of each byte of t[2d + o] is key 8o + i of the half word.
+// sel picks the half (bytes 0-1 or 2-3) of two plane words.
+__device__ __forceinline__ void slice_bytes(const uint32_t (&w)[16], uint32_t sel, uint32_t (&t)[8]) {
 #pragma unroll
-  for (int m = 0; m < 8; ++m) x[m] = __builtin_amdgcn_perm(w[m + 8], w[m], sel);
+  for (int d = 0; d < 4; ++d) {
+    const uint32_t p0 = __builtin_amdgcn_perm(w[4 * d + 1], w[4 * d], sel);       // a0 a1 b0 b1
+    const uint32_t p1 = __builtin_amdgcn_perm(w[4 * d + 3], w[4 * d + 2], sel);   // c0 c1 d0 d1
+    t[2 * d] = __builtin_amdgcn_perm(p1, p0, 0x06040200u);       // a0 b0 c0 d0
+    t[2 * d + 1] = __builtin_amdgcn_perm(p1, p0, 0x07050301u);   // a1 b1 c1 d1
+  }
 }
 
-// One K block.  For key i of the half word, shifting a pair word left by
-// 15 - i puts key i's bits of its two planes at bits 15 and 31, and a
-// v_perm with sign-replicating selectors turns the four such bits of two
-// pair words into four bytes of 0x00 / 0xFF: the B operand holds 0 or -1,
-// byte 4d + e of the K slice being plane (2d, 2d + 8, 2d + 1, 2d + 9)[e].
-// The first block of a tile starts from a zero accumulator.
+// One K block.  For key i = 8o + e of the half word, masking the
+// transposed words t[2d + o] with bit e of every byte leaves, in byte e' of
+// dword d, slice plane (4d + e')'s bit of the key times 2^e: the B operand
+// column is the key's bits scaled by 2^e (as int8, -128 for e = 7), so
+// acc[i] holds the key's limb sums times that scale.  The first block of a
+// tile starts from a zero accumulator.
+// Scale of the B operand column of key 8o + e of a half word: 2^e as int8.
+__host__ __device__ constexpr float key_scale(int e) { return e == 7 ? -128.0f : static_cast<float>(1 << e); }
+
 template <bool FIRST>
-__device__ __forceinline__ void mfma_block(const uint32_t (&x)[8], uint32_t sign_sel, v4i A, v4i (&acc)[16]) {
+__device__ __forceinline__ void mfma_block(const uint32_t (&t)[8], v4i A, v4i (&acc)[16]) {
   const v4i zero = {0, 0, 0, 0};
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const int sh = 15 - i;
+    const uint32_t m = 0x01010101u << (i & 7);
+    const int o = i >> 3;
     v4i bv;
-    bv.x = static_cast<int>(__builtin_amdgcn_perm(x[1] << sh, x[0] << sh, sign_sel));
-    bv.y = static_cast<int>(__builtin_amdgcn_perm(x[3] << sh, x[2] << sh, sign_sel));
-    bv.z = static_cast<int>(__builtin_amdgcn_perm(x[5] << sh, x[4] << sh, sign_sel));
-    bv.w = static_cast<int>(__builtin_amdgcn_perm(x[7] << sh, x[6] << sh, sign_sel));
+    bv.x = static_cast<int>(t[0 + o] & m);
+    bv.y = static_cast<int>(t[2 + o] & m);
+    bv.z = static_cast<int>(t[4 + o] & m);
+    bv.w = static_cast<int>(t[6 + o] & m);
     acc[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, bv, FIRST ? zero : acc[i], 0, 0, 0);
   }
 }
@@ -794,8 +785,6 @@ __global__ __launch_bounds__(kMainThreads, kMainWgPerCu) void scan_main_kernel(S
   const int G = lane >> 4;              // K slice; in the result, the query of the lane
   const int half = col & 1;
   const uint32_t sel = half ? 0x07060302u : 0x05040100u;   // v_perm byte selectors
-  // selectors 8..11: 0xff if bit 15 / 31 / 47 / 63 of the 64-bit source is set
-  const uint32_t sign_sel = __builtin_amdgcn_readfirstlane(0x0b0a0908);
   const char* head = reinterpret_cast<const char*>(a.planes + int64_t(h) * kD * kPlanes * a.ldw);
   const int tile_begin = blockIdx.x * a.tiles_per_wg;
   const int tile_end = min(a.tiles, tile_begin + a.tiles_per_wg);
@@ -815,6 +804,12 @@ __global__ __launch_bounds__(kMainThreads, kMainWgPerCu) void scan_main_kernel(S
   } else {
     theta_t = Cq >= theta ? -INFINITY : INFINITY;   // every score equals C
   }
+  // key i of a half word comes out scaled by key_scale(i & 7); its threshold
+  // is scaled alike (exactly: powers of two), the comparison flipping for
+  // the negative scale
+  float th[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) th[e] = theta_t * key_scale(e);
 
   auto word_of = [&](int tile) { return tile * kTileWords + wave * kWaveWords + (col >> 1); };
   auto woff_of = [&](int tile) {
@@ -835,22 +830,24 @@ __global__ __launch_bounds__(kMainThreads, kMainWgPerCu) void scan_main_kernel(S
       const int nb = last ? 0 : b + 1;
       const int nt = last ? min(tile + 1, tile_end - 1) : tile;
       uint32_t x[8];
-      slice_pairs(words, sel, x);
+      slice_bytes(words, sel, x);
       __builtin_amdgcn_sched_barrier(0);
       load_slice(head, T.rowoff, nb, G, woff_of(nt), words);
       __builtin_amdgcn_sched_barrier(0);
       const uint4 av = T.A[b][G][col];
       const v4i A = {static_cast<int>(av.x), static_cast<int>(av.y), static_cast<int>(av.z), static_cast<int>(av.w)};
-      mfma_block<decltype(first)::value>(x, sign_sel, A, acc);
+      mfma_block<decltype(first)::value>(x, A, acc);
       __builtin_amdgcn_sched_barrier(0);
     };
     step(std::true_type{}, 0);   // nblk >= 1: an empty union is one block of zero weights
     for (int b = 1; b < nblk; ++b) step(std::false_type{}, b);
 
-    // epilogue: this lane holds query G's four limb sums for the 16 keys of
-    // its half word, negated (the B operand held -bit).  t = -(l0 + 2^8 l1 +
-    // 2^16 l2 + 2^24 l3) is formed from two exact int32 halves
-    // (|l| <= 128 * 512).
+    // epilogue: this lane holds query G's four limb sums l0..l3 for the 16
+    // keys of its half word, key i scaled by key_scale(i & 7).  The scaled
+    // t' = l0 + 2^8 l1 + 2^16 l2 + 2^24 l3 is formed in fp32: every l
+    // converts exactly (|l| <= 128 * 128 * 576 < 2^24) and the top half
+    // (l3 << 8) + l2 fits int32 (sum |l3 digits| <= 2^30 / 2^24 + planes).
+    // t = t' / scale exactly.
     const int w = word_of(tile);
     const int64_t key0 = int64_t(w) * 32 + 16 * half;
     const int nvalid = (w < a.nwords && qvalid) ? static_cast<int>(max<int64_t>(0, min<int64_t>(16, a.n - key0))) : 0;
@@ -858,17 +855,21 @@ __global__ __launch_bounds__(kMainThreads, kMainWgPerCu) void scan_main_kernel(S
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const float hi = static_cast<float>((acc[i].w << 8) + acc[i].z);
-      const float lo = static_cast<float>((acc[i].y << 8) + acc[i].x);
-      tv[i] = -fmaf(hi, 65536.0f, lo);
+      const float lo = fmaf(static_cast<float>(acc[i].y), 256.0f, static_cast<float>(acc[i].x));
+      tv[i] = fmaf(hi, 65536.0f, lo);
     }
     if (a.all_scores) {
 #pragma unroll
       for (int i = 0; i < 16; ++i)
-        if (i < nvalid) a.all_scores[int64_t(q0 + G) * a.n + key0 + i] = fmaf(tv[i], sigma, Cq);
+        if (i < nvalid)
+          a.all_scores[int64_t(q0 + G) * a.n + key0 + i] = fmaf(tv[i] * (1.0f / key_scale(i & 7)), sigma, Cq);
     }
     uint32_t bits = 0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) bits |= tv[i] >= theta_t ? (1u << i) : 0u;
+    for (int i = 0; i < 16; ++i) {
+      const bool pass = (i & 7) == 7 ? tv[i] <= th[7] : tv[i] >= th[i & 7];
+      bits |= pass ? (1u << i) : 0u;
+    }
     bits &= nvalid >= 16 ? 0xffffu : ((1u << nvalid) - 1u);
     // Candidates go to this workgroup's LDS buffer: a DPP row holds one query
     // (lanes 16G..16G+15), a row prefix sum orders its lanes and one LDS
@@ -913,7 +914,8 @@ __global__ __launch_bounds__(kMainThreads, kMainWgPerCu) void scan_main_kernel(S
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         if (bits & (1u << i)) {
-          const uint2 e = make_uint2(__float_as_uint(fmaf(tv[i], sigma, Cq)), static_cast<uint32_t>(key0 + i));
+          const float sc = fmaf(tv[i] * (1.0f / key_scale(i & 7)), sigma, Cq);
+          const uint2 e = make_uint2(__float_as_uint(sc), static_cast<uint32_t>(key0 + i));
           if (slot < cap) {
             cbuf[G][slot] = e;
           } else {
@@ -1235,7 +1237,8 @@ template <int GQ>
 void launch_chunk_class(const ScanArgs& a, int H, int nsb, bool sample_phase, hipEvent_t ev_start,
                         hipEvent_t ev_stop, hipStream_t stream) {
   if (sample_phase) {
-    hipLaunchKernelGGL(scan_sample_kernel<GQ>, dim3(nsb * kSampleWgPerBlock, H * a.cph),
+    // one extra workgroup per chunk builds its table
+    hipLaunchKernelGGL(scan_sample_kernel<GQ>, dim3(nsb * kSampleWgPerBlock + 1, H * a.cph),
                        dim3(kSampleThreads), 0, stream, a);
   } else {
     const int wgs = (a.tiles + a.tiles_per_wg - 1) / a.tiles_per_wg;
