@@ -42,6 +42,7 @@
 
 #include <hip/hip_ext.h>
 
+#include <climits>
 #include <type_traits>
 
 #include "fathom_internal.h"
@@ -55,10 +56,17 @@ constexpr int kMaxBlocks = kMaxUnion / kBlockPlanes;
 // the union is padded with readable zero-weight rows to whole K blocks
 constexpr int kPadPlanes = kBlockPlanes;
 constexpr int kMainThreads = 256;              // 4 wavefronts
-constexpr int kMainWgPerCu = 4;                // register budget: 4 resident workgroups per CU
+constexpr int kMainWaves = kMainThreads / 64;
+constexpr int kMainWgPerCu = 3;                // LDS budget: 3 resident workgroups per CU
 constexpr int kWaveWords = 8;                  // 16 MFMA columns = 8 words x 2 halves
-constexpr int kTileWords = (kMainThreads / 64) * kWaveWords;   // 32 words = 1024 keys
-constexpr int kLdsCand = 512;                 // candidates per query buffered in a main workgroup
+constexpr int kTileWords = kMainWaves * kWaveWords;   // 32 words = 1024 keys
+// Per-wave LDS ring of plane words: a stage holds one K block of the wave's
+// 8 words (64 planes x 8 words), written by two 16-byte-per-lane LDS DMA
+// loads; loads run kMainStages - 1 stages ahead of the stage being read.
+constexpr int kMainStages = 3;
+constexpr int kStageHalfDwords = 32 * kWaveWords + 32;   // 32 planes x 8 words + bank padding
+constexpr int kStageDwords = 2 * kStageHalfDwords;
+constexpr int kWaveCand = 32;                  // candidates per (wave, query) buffered in LDS
 constexpr int kSampleThreads = 256;            // lane = key
 constexpr int kSampleWgPerBlock = kSampleBlockKeys / kSampleThreads;
 constexpr int kSelectThreads = 1024;
@@ -697,52 +705,66 @@ __device__ void build_limbs(const UnionLds<GQ>& s, ChunkTable& T, double (&wsum)
   __syncthreads();
 }
 
-// Loads this lane's word of the 16 union planes of K slice G of block b.
-// The union is padded to whole blocks with readable rows, and lanes past the
-// store's last word read that word instead, so every load is unconditional.
-__device__ __forceinline__ void load_slice(const char* head, const uint32_t* rowoff, int b, int G,
-                                           uint32_t woff, uint32_t (&x)[16]) {
-  const int p0 = b * kBlockPlanes + G * 16;
-#pragma unroll
-  for (int t = 0; t < 16; ++t)
-    x[t] = *reinterpret_cast<const uint32_t*>(head + (rowoff[p0 + t] + woff));
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+
+// Reads this lane's B operand bytes of a ring stage once the stage's loads
+// have landed.  VMEM operations complete in issue order, so with VM loads
+// outstanding issued after the stage's own, the stage is complete when at
+// most VM remain.  Written as inline asm because the compiler, not knowing
+// which LDS DMA an LDS read depends on, would wait for all of them; the block
+// waits for its own reads.
+//
+// ds_read_b64_tr_b8 transposes bytes within each group of 16 lanes: lane j
+// of the group receives, in byte m, byte j % 8 of the 8-byte row addressed by
+// lane j / 8 + 2m of the group.  Lane (G, j) addresses plane 16G + 8k + j / 2
+// (k = 0, 1) of key segment 2X + (j & 1) (X = 0, 1; a segment is 64 keys, two
+// words), so it receives octet j % 8 of segment 2X + j / 8 for planes
+// 16G + 8k .. + 7, one plane per byte: t[4X + 2k + h] holds planes
+// 16G + 8k + 4h .. + 3 in bytes 0..3, bit e of each byte being key 8 (j % 8)
+// + e of the segment.  The block also reads the lane's A operand (16 bytes
+// at a_addr), which the compiler would otherwise fence the same way.
+template <int VM>
+__device__ __forceinline__ void read_stage(uint32_t addr, uint32_t a_addr, uint32_t (&t)[8], v4i& A) {
+  v2u r0, r1, r2, r3;
+  asm volatile(
+      "s_waitcnt vmcnt(%5)\n\t"
+      "ds_read_b128 %4, %7\n\t"
+      "ds_read_b64_tr_b8 %0, %6\n\t"
+      "ds_read_b64_tr_b8 %1, %6 offset:512\n\t"
+      "ds_read_b64_tr_b8 %2, %6 offset:16\n\t"
+      "ds_read_b64_tr_b8 %3, %6 offset:528\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(A)
+      : "n"(VM), "v"(addr), "v"(a_addr)
+      : "memory");
+  t[0] = r0.x;
+  t[1] = r0.y;
+  t[2] = r1.x;
+  t[3] = r1.y;
+  t[4] = r2.x;
+  t[5] = r2.y;
+  t[6] = r3.x;
+  t[7] = r3.y;
 }
 
-// Byte-transposes this lane's half word of the 16 planes of its K slice:
-// t[2d + o] holds, in byte e, byte o of the half word of slice plane 4d + e,
-// i.e. bit i of each byte of t[2d + o] is key 8o + i of the half word.
-// sel picks the half (bytes 0-1 or 2-3) of two plane words.
-__device__ __forceinline__ void slice_bytes(const uint32_t (&w)[16], uint32_t sel, uint32_t (&t)[8]) {
-#pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    const uint32_t p0 = __builtin_amdgcn_perm(w[4 * d + 1], w[4 * d], sel);       // a0 a1 b0 b1
-    const uint32_t p1 = __builtin_amdgcn_perm(w[4 * d + 3], w[4 * d + 2], sel);   // c0 c1 d0 d1
-    t[2 * d] = __builtin_amdgcn_perm(p1, p0, 0x06040200u);       // a0 b0 c0 d0
-    t[2 * d + 1] = __builtin_amdgcn_perm(p1, p0, 0x07050301u);   // a1 b1 c1 d1
-  }
-}
-
-// One K block.  For key i = 8o + e of the half word, masking the
-// transposed words t[2d + o] with bit e of every byte leaves, in byte e' of
-// dword d, slice plane (4d + e')'s bit of the key times 2^e: the B operand
-// column is the key's bits scaled by 2^e (as int8, -128 for e = 7), so
-// acc[i] holds the key's limb sums times that scale.  The first block of a
-// tile starts from a zero accumulator.
-// Scale of the B operand column of key 8o + e of a half word: 2^e as int8.
-__host__ __device__ constexpr float key_scale(int e) { return e == 7 ? -128.0f : static_cast<float>(1 << e); }
-
+// One K block: two sets X of 16 columns, 8 MFMAs each.  For key e of a
+// column's octet, masking t[4X + d] with bit e of every byte leaves, in byte
+// e' of dword d, slice plane (4d + e')'s bit of the key times 2^e: the B
+// operand column is the key's bits scaled by 2^e (as int8, -128 for e = 7),
+// so acc[8X + e] holds the key's limb sums times that scale.  The first
+// block of a tile starts from a zero accumulator.
 template <bool FIRST>
 __device__ __forceinline__ void mfma_block(const uint32_t (&t)[8], v4i A, v4i (&acc)[16]) {
   const v4i zero = {0, 0, 0, 0};
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const uint32_t m = 0x01010101u << (i & 7);
-    const int o = i >> 3;
+    const int X = i >> 3;
     v4i bv;
-    bv.x = static_cast<int>(t[0 + o] & m);
-    bv.y = static_cast<int>(t[2 + o] & m);
-    bv.z = static_cast<int>(t[4 + o] & m);
-    bv.w = static_cast<int>(t[6 + o] & m);
+    bv.x = static_cast<int>(t[4 * X + 0] & m);
+    bv.y = static_cast<int>(t[4 * X + 1] & m);
+    bv.z = static_cast<int>(t[4 * X + 2] & m);
+    bv.w = static_cast<int>(t[4 * X + 3] & m);
     acc[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, bv, FIRST ? zero : acc[i], 0, 0, 0);
   }
 }
@@ -759,11 +781,11 @@ __device__ __forceinline__ uint32_t row_incl_sum(uint32_t v) {
 template <int GQ>
 __global__ __launch_bounds__(kMainThreads, kMainWgPerCu) void scan_main_kernel(ScanArgs a) {
   __shared__ ChunkTable T;
-  __shared__ uint2 cbuf[4][kLdsCand];   // this workgroup's candidates per query
-  __shared__ unsigned long long tally2[2];   // candidate counts of queries (0,1) and (2,3)
-  __shared__ uint32_t cbase[4];
+  __shared__ uint32_t ring[kMainWaves][kMainStages][kStageDwords];
+  __shared__ uint2 cbuf[kMainWaves][4][kWaveCand];   // candidates per (wave, query)
+  __shared__ uint32_t wkept[kMainWaves][4];
+  __shared__ uint32_t wbase_s[kMainWaves][4];
   __shared__ float theta_s[4];
-  uint32_t* tally = reinterpret_cast<uint32_t*>(tally2);   // little endian: count of query g
   const int h = blockIdx.y / a.cph;
   const int q0 = h * a.group + a.qoff + (blockIdx.y % a.cph) * kQueryChunk;
   {
@@ -771,130 +793,150 @@ __global__ __launch_bounds__(kMainThreads, kMainWgPerCu) void scan_main_kernel(S
                                                       size_t(chunk_index(a)) * kChunkTableBytes);
     uint4* dst = reinterpret_cast<uint4*>(&T);
     for (int i = threadIdx.x; i < static_cast<int>(sizeof(ChunkTable) / 16); i += blockDim.x) dst[i] = src[i];
-    if (threadIdx.x < 4) {
-      theta_s[threadIdx.x] = static_cast<int>(threadIdx.x) < GQ ? a.theta[q0 + threadIdx.x] : 0.0f;
-      tally[threadIdx.x] = 0u;
-    }
+    if (threadIdx.x < 4) theta_s[threadIdx.x] = static_cast<int>(threadIdx.x) < GQ ? a.theta[q0 + threadIdx.x] : 0.0f;
   }
   __syncthreads();
   const int nblk = nblocks_of(T.U);
 
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int lane = threadIdx.x & 63;
-  const int col = lane & 15;            // MFMA column: word col >> 1, half col & 1
+  const int col = lane & 15;            // MFMA column: octet col & 7 of key segments 2X + (col >> 3)
   const int G = lane >> 4;              // K slice; in the result, the query of the lane
-  const int half = col & 1;
-  const uint32_t sel = half ? 0x07060302u : 0x05040100u;   // v_perm byte selectors
-  const char* head = reinterpret_cast<const char*>(a.planes + int64_t(h) * kD * kPlanes * a.ldw);
+  const bool qvalid = G < GQ;
+  // The filter runs on the exact integer limb sum t (|t| <= 2^30 (1 + eps);
+  // score = fma(float(t), sigma, C)): t >= theta_i is a necessary condition
+  // for score >= theta.  The margins cover the roundings of float(t) (at most
+  // 64), of the fma and of this set-up (done in fp64), so every key scoring
+  // >= theta is a candidate, plus possibly a few just below it; the merge
+  // checks that the k-th candidate scores >= theta.
+  int theta_i;
+  {
+    const float sigma = T.sigma[G], Cq = T.C[G], theta = theta_s[G];
+    double tt;
+    if (sigma > 0.0f) {
+      const double slack = (fabs(static_cast<double>(theta)) + fabs(static_cast<double>(Cq))) * 0x1p-20;
+      tt = (static_cast<double>(theta) - static_cast<double>(Cq) - slack) / static_cast<double>(sigma) - 65.0;
+    } else {
+      tt = Cq >= theta ? -INFINITY : INFINITY;   // every score equals C
+    }
+    theta_i = tt <= -0x1p31 ? INT_MIN : tt >= 0x1p31 ? INT_MAX : static_cast<int>(ceil(tt));
+  }
+
   const int tile_begin = blockIdx.x * a.tiles_per_wg;
   const int tile_end = min(a.tiles, tile_begin + a.tiles_per_wg);
-  const bool qvalid = G < GQ;
-  const float sigma = T.sigma[G];
-  const float Cq = T.C[G];
-  const float theta = theta_s[G];
-  // The filter runs on the unscaled limb sum t (score = fma(t, sigma, C)):
-  // t >= theta_t is a necessary condition for score >= theta (the margin
-  // covers the roundings), so every key scoring >= theta is a candidate,
-  // plus possibly a few just below it; the merge checks that the k-th
-  // candidate scores >= theta.
-  float theta_t;
-  if (sigma > 0.0f) {
-    const float slack = (fabsf(theta) + fabsf(Cq)) * 0x1p-20f;
-    theta_t = (theta - Cq - slack) / sigma - 1.0f;
-  } else {
-    theta_t = Cq >= theta ? -INFINITY : INFINITY;   // every score equals C
-  }
-  // key i of a half word comes out scaled by key_scale(i & 7); its threshold
-  // is scaled alike (exactly: powers of two), the comparison flipping for
-  // the negative scale
-  float th[8];
+  const int nsteps = max(0, tile_end - tile_begin) * nblk;   // (tile, block) steps of this workgroup
+
+  // Loads.  Stage half j, lane l: ring row r = l >> 1 (plane 16 (2j + (r & 1))
+  // + (r >> 1) of the block), words 4 (l & 1) .. + 3 of the wave's 8.  The
+  // buffer's size bounds the reads: words past the head's last plane row
+  // read as zero (past a row's end they read the next row; such keys are
+  // masked out).
+  const char* head = reinterpret_cast<const char*>(a.planes + int64_t(h) * kD * kPlanes * a.ldw);
+  const int64_t head_bytes = int64_t(kD) * kPlanes * a.ldw * 4;
+  const uint32_t nrec = head_bytes > int64_t(0xffffffff) ? 0xffffffffu : static_cast<uint32_t>(head_bytes);
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(head), static_cast<short>(0), static_cast<int>(nrec), 0x00020000);
+  const int r = lane >> 1;
+  const int dma_plane0 = 16 * (r & 1) + (r >> 1);   // plane of row r in half 0; half 1 adds 32
+  const uint32_t dma_lane_off = 16u * static_cast<uint32_t>(lane & 1);
+  int it_tile = tile_begin, it_b = 0, it_slot = 0, issued = 0;   // next step to load (uniform)
+  auto issue = [&]() {
+    if (issued < nsteps) {
+      const uint32_t woff = static_cast<uint32_t>(it_tile * kTileWords + wave * kWaveWords) * 4u;
+      uint32_t* dst = &ring[wave][it_slot][0];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) th[e] = theta_t * key_scale(e);
-
-  auto word_of = [&](int tile) { return tile * kTileWords + wave * kWaveWords + (col >> 1); };
-  auto woff_of = [&](int tile) {
-    const int w = word_of(tile);
-    return static_cast<uint32_t>(w < a.nwords ? w : a.nwords - 1) * 4u;
+      for (int j = 0; j < 2; ++j) {
+        const uint32_t vo = T.rowoff[it_b * kBlockPlanes + 32 * j + dma_plane0] + dma_lane_off + woff;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst + j * kStageHalfDwords, 16, vo, 0, 0, 0);
+      }
+      ++issued;
+      if (++it_b == nblk) { it_b = 0; ++it_tile; }
+      it_slot = it_slot + 1 == kMainStages ? 0 : it_slot + 1;
+    }
   };
+  // transpose-read address of lane (G, col): plane 16G + col / 2 of segment
+  // col & 1 (ring row 2 (col / 2) + (G & 1) of stage half G / 2)
+  const uint32_t ring_lane = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&ring[wave][0][0])) +
+                             static_cast<uint32_t>((G >> 1) * kStageHalfDwords + (2 * (col >> 1) + (G & 1)) * kWaveWords) * 4u +
+                             8u * static_cast<uint32_t>(col & 1);
+  const uint32_t a_lane = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&T.A[0][G][col]));
+#pragma unroll
+  for (int i = 0; i < kMainStages - 1; ++i) issue();
 
-  // One word buffer: once a block's words are transposed into index bytes the
-  // buffer is refilled with the next step's words (the step after the last
-  // block of a tile is block 0 of the next tile), which are in flight while
-  // the block's MFMAs run.
-  uint32_t words[16];
-  if (tile_begin < tile_end) load_slice(head, T.rowoff, 0, G, woff_of(tile_begin), words);
+  uint32_t wc0 = 0, wc1 = 0, wc2 = 0, wc3 = 0;   // this wave's candidates per query so far (uniform)
+  int step_i = 0, slot = 0;
   for (int tile = tile_begin; tile < tile_end; ++tile) {
     v4i acc[16];
     auto step = [&](auto first, int b) {
-      const bool last = b + 1 == nblk;
-      const int nb = last ? 0 : b + 1;
-      const int nt = last ? min(tile + 1, tile_end - 1) : tile;
+      issue();
       uint32_t x[8];
-      slice_bytes(words, sel, x);
-      __builtin_amdgcn_sched_barrier(0);
-      load_slice(head, T.rowoff, nb, G, woff_of(nt), words);
-      __builtin_amdgcn_sched_barrier(0);
-      const uint4 av = T.A[b][G][col];
-      const v4i A = {static_cast<int>(av.x), static_cast<int>(av.y), static_cast<int>(av.z), static_cast<int>(av.w)};
+      const uint32_t addr = ring_lane + static_cast<uint32_t>(slot * kStageDwords) * 4u;
+      // the last steps have fewer loads behind them: wait for all
+      const uint32_t a_addr = a_lane + static_cast<uint32_t>(b * 4 * 16 * 16);
+      v4i A;
+      if (step_i + kMainStages - 1 < nsteps) {
+        read_stage<2 * (kMainStages - 1)>(addr, a_addr, x, A);
+      } else {
+        read_stage<0>(addr, a_addr, x, A);
+      }
+      ++step_i;
+      slot = slot + 1 == kMainStages ? 0 : slot + 1;
       mfma_block<decltype(first)::value>(x, A, acc);
-      __builtin_amdgcn_sched_barrier(0);
     };
     step(std::true_type{}, 0);   // nblk >= 1: an empty union is one block of zero weights
     for (int b = 1; b < nblk; ++b) step(std::false_type{}, b);
 
     // epilogue: this lane holds query G's four limb sums l0..l3 for the 16
-    // keys of its half word, key i scaled by key_scale(i & 7).  The scaled
-    // t' = l0 + 2^8 l1 + 2^16 l2 + 2^24 l3 is formed in fp32: every l
-    // converts exactly (|l| <= 128 * 128 * 576 < 2^24) and the top half
-    // (l3 << 8) + l2 fits int32 (sum |l3 digits| <= 2^30 / 2^24 + planes).
-    // t = t' / scale exactly.
-    const int w = word_of(tile);
-    const int64_t key0 = int64_t(w) * 32 + 16 * half;
-    const int nvalid = (w < a.nwords && qvalid) ? static_cast<int>(max<int64_t>(0, min<int64_t>(16, a.n - key0))) : 0;
-    float tv[16];
+    // keys of its column, key i = 8X + e scaled by 2^e (-128 for e = 7).
+    // Unscaling limb j is a shift by 8j - e, exact (the sums are multiples of
+    // 2^e), and t = l0 + 2^8 l1 + 2^16 l2 + 2^24 l3 is exact in wrapping
+    // int32 arithmetic because |t| < 2^31.  Keys with e = 7 give -t.
+    // key 8X + e of the column: key_of(X) + e
+    const int64_t kbase = (int64_t(tile) * kTileWords + wave * kWaveWords) * 32 + (col >> 3) * 64 + 8 * (col & 7);
+    auto key_of = [&](int X) { return kbase + 128 * X; };
+    auto nvalid_of = [&](int X) {
+      return qvalid ? static_cast<int>(max<int64_t>(0, min<int64_t>(8, a.n - key_of(X)))) : 0;
+    };
+    const int nv0 = nvalid_of(0), nv1 = nvalid_of(1);
+    int tv[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const float hi = static_cast<float>((acc[i].w << 8) + acc[i].z);
-      const float lo = fmaf(static_cast<float>(acc[i].y), 256.0f, static_cast<float>(acc[i].x));
-      tv[i] = fmaf(hi, 65536.0f, lo);
+      const int e = i & 7;
+      // (empty asm: keeps the Horner form, which needs one op per limb)
+      uint32_t z = (static_cast<uint32_t>(acc[i].w) << 8) + static_cast<uint32_t>(acc[i].z);
+      asm("" : "+v"(z));
+      uint32_t y = (z << 8) + static_cast<uint32_t>(acc[i].y);   // 2^e (l1 + 2^8 l2 + 2^16 l3)
+      asm("" : "+v"(y));
+      tv[i] = static_cast<int>((y << (8 - e)) + static_cast<uint32_t>(acc[i].x >> e));
     }
+    auto t_of = [&](int i) { return (i & 7) == 7 ? -tv[i] : tv[i]; };
+    // (scale and offset re-read from LDS: only candidates need them)
+    auto score_of = [&](int i) { return fmaf(static_cast<float>(t_of(i)), T.sigma[G], T.C[G]); };
     if (a.all_scores) {
 #pragma unroll
       for (int i = 0; i < 16; ++i)
-        if (i < nvalid)
-          a.all_scores[int64_t(q0 + G) * a.n + key0 + i] = fmaf(tv[i] * (1.0f / key_scale(i & 7)), sigma, Cq);
+        if ((i & 7) < (i < 8 ? nv0 : nv1)) a.all_scores[int64_t(q0 + G) * a.n + key_of(i >> 3) + (i & 7)] = score_of(i);
     }
     uint32_t bits = 0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const bool pass = (i & 7) == 7 ? tv[i] <= th[7] : tv[i] >= th[i & 7];
-      bits |= pass ? (1u << i) : 0u;
-    }
-    bits &= nvalid >= 16 ? 0xffffu : ((1u << nvalid) - 1u);
-    // Candidates go to this workgroup's LDS buffer: a DPP row holds one query
-    // (lanes 16G..16G+15), a row prefix sum orders its lanes and one LDS
-    // atomic per (wave, query) reserves the row's slots.  No barrier: each
-    // wave writes only the slots it reserved.  Slots past the buffer spill
-    // to the global list, reserved the same way with one global atomic per
-    // (wave, query).
+    for (int i = 0; i < 16; ++i) bits |= t_of(i) >= theta_i ? (1u << i) : 0u;
+    bits &= ((1u << nv0) - 1u) | (((1u << nv1) - 1u) << 8);
+    if (__ballot(bits != 0) == 0) continue;   // uniform
+    // Candidates go to this wave's LDS buffer of their query: a DPP row holds
+    // one query (lanes 16G..16G+15) and a row prefix sum orders its lanes.
+    // Slots past the buffer spill to the global list, reserved with one
+    // global atomic per (wave, query).
     const uint32_t mine = __popc(bits);
     const uint32_t incl = row_incl_sum(mine);
-    uint32_t wave_off = 0;
-    {
-      // row totals of queries 0..3, reserved with two packed 64-bit atomics
-      const uint32_t t0 = read_lane(incl, 15), t1 = read_lane(incl, 31);
-      const uint32_t t2 = read_lane(incl, 47), t3 = read_lane(incl, 63);
-      unsigned long long o01 = 0, o23 = 0;
-      if (lane == 0) {
-        if ((t0 | t1) != 0) o01 = atomicAdd(&tally2[0], static_cast<unsigned long long>(t0) | (static_cast<unsigned long long>(t1) << 32));
-        if ((t2 | t3) != 0) o23 = atomicAdd(&tally2[1], static_cast<unsigned long long>(t2) | (static_cast<unsigned long long>(t3) << 32));
-      }
-      const uint32_t offs[4] = {read_lane(static_cast<uint32_t>(o01), 0), read_lane(static_cast<uint32_t>(o01 >> 32), 0),
-                                read_lane(static_cast<uint32_t>(o23), 0), read_lane(static_cast<uint32_t>(o23 >> 32), 0)};
-      wave_off = G == 0 ? offs[0] : G == 1 ? offs[1] : G == 2 ? offs[2] : offs[3];
-    }
+    const uint32_t t0 = read_lane(incl, 15), t1 = read_lane(incl, 31);
+    const uint32_t t2 = read_lane(incl, 47), t3 = read_lane(incl, 63);
+    const uint32_t wave_off = G == 0 ? wc0 : G == 1 ? wc1 : G == 2 ? wc2 : wc3;
+    wc0 += t0;
+    wc1 += t1;
+    wc2 += t2;
+    wc3 += t3;
     const uint32_t slot0 = wave_off + incl - mine;
-    const uint32_t cap = static_cast<uint32_t>(kLdsCand);
+    const uint32_t cap = static_cast<uint32_t>(kWaveCand);
     const uint32_t spill = slot0 + mine > cap ? slot0 + mine - max(slot0, cap) : 0u;
     uint32_t gpos = 0;
     if (__ballot(spill != 0) != 0) {   // uniform; rare
@@ -909,37 +951,50 @@ __global__ __launch_bounds__(kMainThreads, kMainWgPerCu) void scan_main_kernel(S
       }
     }
     if (bits != 0) {
-      uint32_t slot = slot0;
+      uint32_t slot_c = slot0;
       // static key index: a computed index into tv would move it to scratch
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         if (bits & (1u << i)) {
-          const float sc = fmaf(tv[i] * (1.0f / key_scale(i & 7)), sigma, Cq);
-          const uint2 e = make_uint2(__float_as_uint(sc), static_cast<uint32_t>(key0 + i));
-          if (slot < cap) {
-            cbuf[G][slot] = e;
+          const uint2 e = make_uint2(__float_as_uint(score_of(i)), static_cast<uint32_t>(key_of(i >> 3) + (i & 7)));
+          if (slot_c < cap) {
+            cbuf[wave][G][slot_c] = e;
           } else {
             if (gpos < static_cast<uint32_t>(kCandCap)) a.cand[int64_t(q0 + G) * kCandCap + gpos] = e;
             ++gpos;
           }
-          ++slot;
+          ++slot_c;
         }
       }
     }
   }
-  // flush: one global atomic per query reserves the buffered candidates' slots
+  // flush: one global atomic per query reserves the buffered candidates'
+  // slots, in wave order
+  if (lane == 0) {
+    wkept[wave][0] = min(wc0, static_cast<uint32_t>(kWaveCand));
+    wkept[wave][1] = min(wc1, static_cast<uint32_t>(kWaveCand));
+    wkept[wave][2] = min(wc2, static_cast<uint32_t>(kWaveCand));
+    wkept[wave][3] = min(wc3, static_cast<uint32_t>(kWaveCand));
+  }
   __syncthreads();
   if (threadIdx.x < GQ) {
-    const uint32_t kept = min(tally[threadIdx.x], static_cast<uint32_t>(kLdsCand));
-    tally[threadIdx.x] = kept;
-    cbase[threadIdx.x] = kept ? atomicAdd(&a.count[q0 + threadIdx.x], kept) : 0u;
+    const int g = threadIdx.x;
+    uint32_t total = 0;
+#pragma unroll
+    for (int v = 0; v < kMainWaves; ++v) total += wkept[v][g];
+    uint32_t base = total ? atomicAdd(&a.count[q0 + g], total) : 0u;
+#pragma unroll
+    for (int v = 0; v < kMainWaves; ++v) {
+      wbase_s[v][g] = base;
+      base += wkept[v][g];
+    }
   }
   __syncthreads();
 #pragma unroll
   for (int g = 0; g < GQ; ++g) {
-    const uint32_t kept = tally[g], b0 = cbase[g];
-    for (uint32_t i = threadIdx.x; i < kept; i += blockDim.x)
-      if (b0 + i < static_cast<uint32_t>(kCandCap)) a.cand[int64_t(q0 + g) * kCandCap + b0 + i] = cbuf[g][i];
+    const uint32_t kept = wkept[wave][g], b0 = wbase_s[wave][g];
+    for (uint32_t i = lane; i < kept; i += 64)
+      if (b0 + i < static_cast<uint32_t>(kCandCap)) a.cand[int64_t(q0 + g) * kCandCap + b0 + i] = cbuf[wave][g][i];
   }
 }
 
