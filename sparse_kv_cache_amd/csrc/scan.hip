@@ -60,12 +60,14 @@ constexpr int kMainWaves = kMainThreads / 64;
 constexpr int kMainWgPerCu = 3;                // LDS budget: 3 resident workgroups per CU
 constexpr int kWaveWords = 8;                  // 16 MFMA columns = 8 words x 2 halves
 constexpr int kTileWords = kMainWaves * kWaveWords;   // 32 words = 1024 keys
-// Per-wave LDS ring of plane words: a stage holds one K block of the wave's
-// 8 words (64 planes x 8 words), written by two 16-byte-per-lane LDS DMA
-// loads; loads run kMainStages - 1 stages ahead of the stage being read.
+// Workgroup LDS ring of plane words: a stage holds one K block of the
+// workgroup's tile (64 planes x 32 words), written by eight LDS DMA loads of
+// 8 planes x 128 bytes (two per wave; whole 128-byte lines).  Loads run
+// kMainStages - 2 stages ahead of the stage being read, plus the one issued
+// while it is read.
 constexpr int kMainStages = 3;
-constexpr int kStageHalfDwords = 32 * kWaveWords + 32;   // 32 planes x 8 words + bank padding
-constexpr int kStageDwords = 2 * kStageHalfDwords;
+constexpr int kDmaDwords = 8 * kTileWords + 8;           // one DMA load (8 planes x 32 words) + bank padding
+constexpr int kStageDwords = 8 * kDmaDwords;
 constexpr int kWaveCand = 32;                  // candidates per (wave, query) buffered in LDS
 constexpr int kSampleThreads = 256;            // lane = key
 constexpr int kSampleWgPerBlock = kSampleBlockKeys / kSampleThreads;
@@ -707,35 +709,43 @@ __device__ void build_limbs(const UnionLds<GQ>& s, ChunkTable& T, double (&wsum)
 
 typedef uint32_t v2u __attribute__((ext_vector_type(2)));
 
-// Reads this lane's B operand bytes of a ring stage once the stage's loads
-// have landed.  VMEM operations complete in issue order, so with VM loads
-// outstanding issued after the stage's own, the stage is complete when at
-// most VM remain.  Written as inline asm because the compiler, not knowing
-// which LDS DMA an LDS read depends on, would wait for all of them; the block
-// waits for its own reads.
+// Waits until this wave's loads of a ring stage have landed, then for every
+// wave of the workgroup to get there (so the stage is complete and the stage
+// read before it is no longer read by anyone).  VMEM operations complete in
+// issue order, so with VM loads outstanding issued after the stage's own,
+// the stage's loads are complete when at most VM remain.  Inline asm: the
+// compiler, not knowing which LDS DMA an LDS read depends on, would wait
+// for all of them, and a plain barrier would also wait for all loads.
+template <int VM>
+__device__ __forceinline__ void sync_stage() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(VM) : "memory");
+}
+
+// Reads this lane's B operand bytes of a complete ring stage (inline asm for
+// the same reason; the block waits for its own reads).
 //
 // ds_read_b64_tr_b8 transposes bytes within each group of 16 lanes: lane j
 // of the group receives, in byte m, byte j % 8 of the 8-byte row addressed by
 // lane j / 8 + 2m of the group.  Lane (G, j) addresses plane 16G + 8k + j / 2
-// (k = 0, 1) of key segment 2X + (j & 1) (X = 0, 1; a segment is 64 keys, two
-// words), so it receives octet j % 8 of segment 2X + j / 8 for planes
+// (k = 0, 1) of the wave's key segment 2X + (j & 1) (X = 0, 1; a segment is
+// 64 keys, two words), so it receives octet j % 8 of segment 2X + j / 8 for planes
 // 16G + 8k .. + 7, one plane per byte: t[4X + 2k + h] holds planes
 // 16G + 8k + 4h .. + 3 in bytes 0..3, bit e of each byte being key 8 (j % 8)
 // + e of the segment.  The block also reads the lane's A operand (16 bytes
 // at a_addr), which the compiler would otherwise fence the same way.
-template <int VM>
 __device__ __forceinline__ void read_stage(uint32_t addr, uint32_t a_addr, uint32_t (&t)[8], v4i& A) {
   v2u r0, r1, r2, r3;
+  // plane 16G + 8k + j / 2 sits in row 2G + k of DMA load j / 2 (128 bytes
+  // per row), so k adds 128 bytes and X, two segments, 16
   asm volatile(
-      "s_waitcnt vmcnt(%5)\n\t"
-      "ds_read_b128 %4, %7\n\t"
-      "ds_read_b64_tr_b8 %0, %6\n\t"
-      "ds_read_b64_tr_b8 %1, %6 offset:512\n\t"
-      "ds_read_b64_tr_b8 %2, %6 offset:16\n\t"
-      "ds_read_b64_tr_b8 %3, %6 offset:528\n\t"
+      "ds_read_b128 %4, %6\n\t"
+      "ds_read_b64_tr_b8 %0, %5\n\t"
+      "ds_read_b64_tr_b8 %1, %5 offset:128\n\t"
+      "ds_read_b64_tr_b8 %2, %5 offset:16\n\t"
+      "ds_read_b64_tr_b8 %3, %5 offset:144\n\t"
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(A)
-      : "n"(VM), "v"(addr), "v"(a_addr)
+      : "v"(addr), "v"(a_addr)
       : "memory");
   t[0] = r0.x;
   t[1] = r0.y;
@@ -781,7 +791,7 @@ __device__ __forceinline__ uint32_t row_incl_sum(uint32_t v) {
 template <int GQ>
 __global__ __launch_bounds__(kMainThreads, kMainWgPerCu) void scan_main_kernel(ScanArgs a) {
   __shared__ ChunkTable T;
-  __shared__ uint32_t ring[kMainWaves][kMainStages][kStageDwords];
+  __shared__ uint32_t ring[kMainStages][kStageDwords];
   __shared__ uint2 cbuf[kMainWaves][4][kWaveCand];   // candidates per (wave, query)
   __shared__ uint32_t wkept[kMainWaves][4];
   __shared__ uint32_t wbase_s[kMainWaves][4];
@@ -826,9 +836,11 @@ __global__ __launch_bounds__(kMainThreads, kMainWgPerCu) void scan_main_kernel(S
   const int tile_end = min(a.tiles, tile_begin + a.tiles_per_wg);
   const int nsteps = max(0, tile_end - tile_begin) * nblk;   // (tile, block) steps of this workgroup
 
-  // Loads.  Stage half j, lane l: ring row r = l >> 1 (plane 16 (2j + (r & 1))
-  // + (r >> 1) of the block), words 4 (l & 1) .. + 3 of the wave's 8.  The
-  // buffer's size bounds the reads: words past the head's last plane row
+  // Loads.  DMA load q = 2 wave + j (j = 0, 1) of a stage, lane l: row
+  // l >> 3 holds plane q + 8 (l >> 3) of the block, bytes 16 (l & 7) .. + 15
+  // of the tile's 128.  (The eight planes a transpose read gathers then sit
+  // in eight different loads, whose padding spreads them over the banks.)
+  // The buffer's size bounds the reads: words past the head's last plane row
   // read as zero (past a row's end they read the next row; such keys are
   // masked out).
   const char* head = reinterpret_cast<const char*>(a.planes + int64_t(h) * kD * kPlanes * a.ldw);
@@ -836,28 +848,26 @@ __global__ __launch_bounds__(kMainThreads, kMainWgPerCu) void scan_main_kernel(S
   const uint32_t nrec = head_bytes > int64_t(0xffffffff) ? 0xffffffffu : static_cast<uint32_t>(head_bytes);
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<char*>(head), static_cast<short>(0), static_cast<int>(nrec), 0x00020000);
-  const int r = lane >> 1;
-  const int dma_plane0 = 16 * (r & 1) + (r >> 1);   // plane of row r in half 0; half 1 adds 32
-  const uint32_t dma_lane_off = 16u * static_cast<uint32_t>(lane & 1);
+  const uint32_t dma_lane_off = 16u * static_cast<uint32_t>(lane & 7);
   int it_tile = tile_begin, it_b = 0, it_slot = 0, issued = 0;   // next step to load (uniform)
   auto issue = [&]() {
     if (issued < nsteps) {
-      const uint32_t woff = static_cast<uint32_t>(it_tile * kTileWords + wave * kWaveWords) * 4u;
-      uint32_t* dst = &ring[wave][it_slot][0];
+      const uint32_t woff = static_cast<uint32_t>(it_tile * kTileWords) * 4u;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const uint32_t vo = T.rowoff[it_b * kBlockPlanes + 32 * j + dma_plane0] + dma_lane_off + woff;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst + j * kStageHalfDwords, 16, vo, 0, 0, 0);
+        const int q = 2 * wave + j;
+        const uint32_t vo = T.rowoff[it_b * kBlockPlanes + q + 8 * (lane >> 3)] + dma_lane_off + woff;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, &ring[it_slot][q * kDmaDwords], 16, vo, 0, 0, 0);
       }
       ++issued;
       if (++it_b == nblk) { it_b = 0; ++it_tile; }
       it_slot = it_slot + 1 == kMainStages ? 0 : it_slot + 1;
     }
   };
-  // transpose-read address of lane (G, col): plane 16G + col / 2 of segment
-  // col & 1 (ring row 2 (col / 2) + (G & 1) of stage half G / 2)
-  const uint32_t ring_lane = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&ring[wave][0][0])) +
-                             static_cast<uint32_t>((G >> 1) * kStageHalfDwords + (2 * (col >> 1) + (G & 1)) * kWaveWords) * 4u +
+  // transpose-read address of lane (G, col): plane 16G + col / 2 (row 2G of
+  // DMA load col / 2) of the wave's segment col & 1
+  const uint32_t ring_lane = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&ring[0][0])) +
+                             static_cast<uint32_t>((col >> 1) * kDmaDwords + 2 * G * kTileWords + wave * kWaveWords) * 4u +
                              8u * static_cast<uint32_t>(col & 1);
   const uint32_t a_lane = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&T.A[0][G][col]));
 #pragma unroll
@@ -868,17 +878,18 @@ __global__ __launch_bounds__(kMainThreads, kMainWgPerCu) void scan_main_kernel(S
   for (int tile = tile_begin; tile < tile_end; ++tile) {
     v4i acc[16];
     auto step = [&](auto first, int b) {
-      issue();
+      // the last steps have fewer loads behind them: wait for all
+      if (step_i + kMainStages - 2 < nsteps) {
+        sync_stage<2 * (kMainStages - 2)>();
+      } else {
+        sync_stage<0>();
+      }
+      issue();   // into the slot every wave has finished reading
       uint32_t x[8];
       const uint32_t addr = ring_lane + static_cast<uint32_t>(slot * kStageDwords) * 4u;
-      // the last steps have fewer loads behind them: wait for all
       const uint32_t a_addr = a_lane + static_cast<uint32_t>(b * 4 * 16 * 16);
       v4i A;
-      if (step_i + kMainStages - 1 < nsteps) {
-        read_stage<2 * (kMainStages - 1)>(addr, a_addr, x, A);
-      } else {
-        read_stage<0>(addr, a_addr, x, A);
-      }
+      read_stage(addr, a_addr, x, A);
       ++step_i;
       slot = slot + 1 == kMainStages ? 0 : slot + 1;
       mfma_block<decltype(first)::value>(x, A, acc);
