@@ -12,8 +12,9 @@
 //   C_q    = sum_c q_c (lo_c + step_c 2^(3-b_qc))      (bin-centre offsets).
 //
 // Launch sequence per call (all on the caller's stream):
-//   1. scan_sample_kernel    scores of up to 8 sampled 1024-key blocks per KV
-//                            head (lane = key, planes staged through LDS);
+//   1. scan_sample_kernel    builds each chunk's table and scores up to 8
+//                            sampled 1024-key blocks per KV head, the way
+//                            the main kernel does;
 //   2. scan_threshold_kernel per query, a radix select on the sample picks a
 //                            score theta expected to leave ~2k keys above it;
 //   3. scan_main_kernel      every key of every head, see below; keys scoring
@@ -69,8 +70,6 @@ constexpr int kMainStages = 3;
 constexpr int kDmaDwords = 8 * kTileWords + 8;           // one DMA load (8 planes x 32 words) + bank padding
 constexpr int kStageDwords = 8 * kDmaDwords;
 constexpr int kWaveCand = 32;                  // candidates per (wave, query) buffered in LDS
-constexpr int kSampleThreads = 256;            // lane = key
-constexpr int kSampleWgPerBlock = kSampleBlockKeys / kSampleThreads;
 constexpr int kSelectThreads = 1024;
 constexpr int kSelectWaves = kSelectThreads / 64;
 
@@ -296,94 +295,24 @@ __device__ void build_union(const ScanArgs& a, int h, int q0, UnionLds<GQ>& s) {
   __syncthreads();
 }
 
-// Builds the main kernel's table of this (KV head, query chunk) and stores it
-// in the workspace.  Needs blockDim.x >= 64; contains barriers.
+// Builds the main kernel's table of this (KV head, query chunk) in T and,
+// if store is set, stores it in the workspace.  Needs blockDim.x >= 64; contains barriers.
 template <int GQ>
 __device__ void build_limbs(const UnionLds<GQ>& s, ChunkTable& T, double (&wsum)[4], int nblk);
 
 template <int GQ>
-__device__ void write_chunk_table(const ScanArgs& a, const UnionLds<GQ>& s, ChunkTable& T, double (&wsum)[4]) {
+__device__ void write_chunk_table(const ScanArgs& a, const UnionLds<GQ>& s, ChunkTable& T, double (&wsum)[4],
+                                  bool store) {
   const int U = s.U;
   const int nblk = nblocks_of(U);
   for (int i = threadIdx.x; i < kMaxUnion + kPadPlanes; i += blockDim.x) T.rowoff[i] = i < U ? s.rowoff[i] : 0u;
   if (threadIdx.x < 4) T.C[threadIdx.x] = static_cast<int>(threadIdx.x) < GQ ? s.C[threadIdx.x] : 0.0f;
   if (threadIdx.x == 0) T.U = U;
   build_limbs<GQ>(s, T, wsum, nblk);   // ends with a barrier
+  if (!store) return;
   uint4* dst = reinterpret_cast<uint4*>(static_cast<char*>(a.tables) + size_t(chunk_index(a)) * kChunkTableBytes);
   const uint4* src = reinterpret_cast<const uint4*>(&T);
   for (int i = threadIdx.x; i < static_cast<int>(sizeof(ChunkTable) / 16); i += blockDim.x) dst[i] = src[i];
-}
-
-// ------------------------------------------------------------------ sample
-
-// Workgroup = (quarter of a sampled 1024-key block, KV head, query chunk):
-// the union plane words of its 256 keys are staged in LDS, then thread = key.
-// One more workgroup per chunk writes the chunk's main-kernel table.
-template <int GQ>
-__global__ __launch_bounds__(kSampleThreads) void scan_sample_kernel(ScanArgs a) {
-  constexpr int kWords = kSampleThreads / 32;
-  __shared__ UnionLds<GQ> s;
-  __shared__ uint32_t stage[kMaxUnion][kWords];
-  __shared__ ChunkTable T;
-  __shared__ double wsum[4];
-  const int h = blockIdx.y / a.cph;
-  const int q0 = h * a.group + a.qoff + (blockIdx.y % a.cph) * kQueryChunk;
-  build_union<GQ>(a, h, q0, s);
-  // the last workgroup of each chunk builds the main kernel's table instead
-  // of sampling, in parallel with the sampling workgroups
-  if (blockIdx.x == gridDim.x - 1) {   // uniform per workgroup
-    write_chunk_table<GQ>(a, s, T, wsum);
-    return;
-  }
-
-  const int sbi = blockIdx.x / kSampleWgPerBlock;
-  const int part = blockIdx.x % kSampleWgPerBlock;
-  const int64_t word0 = int64_t(sbi) * a.sample_stride * (kSampleBlockKeys / 32) + part * kWords;
-  const char* head = reinterpret_cast<const char*>(a.planes + int64_t(h) * kD * kPlanes * a.ldw);
-  const int U = s.U;
-  // Every thread issues all of its staging loads before the first store, and
-  // no load is conditional (a load under a branch makes the compiler wait for
-  // it before the branch ends, turning the batch into a chain of round trips):
-  // entries past the union read row 0 and words past the row read its last
-  // word; both are ignored later.
-  constexpr int kPer = (kMaxUnion * kWords + kSampleThreads - 1) / kSampleThreads;
-  static_assert(kPer * kSampleThreads == kMaxUnion * kWords, "staging covers the stage exactly");
-  uint32_t tmp[kPer];
-#pragma unroll
-  for (int r = 0; r < kPer; ++r) {
-    const int i = threadIdx.x + r * kSampleThreads;
-    const int p = i / kWords, wd = i % kWords;
-    const int64_t w = min<int64_t>(word0 + wd, a.ldw - 1);
-    const uint32_t ro = p < U ? s.rowoff[p] : 0u;
-    tmp[r] = *reinterpret_cast<const uint32_t*>(head + ro + w * 4);
-  }
-#pragma unroll
-  for (int r = 0; r < kPer; ++r) {
-    const int i = threadIdx.x + r * kSampleThreads;
-    stage[i / kWords][i % kWords] = tmp[r];
-  }
-  __syncthreads();
-  const int64_t key = word0 * 32 + threadIdx.x;
-  const bool valid = key < a.n;
-  const int sh = threadIdx.x & 31, wsel = threadIdx.x >> 5;
-  float acc[GQ];
-#pragma unroll
-  for (int g = 0; g < GQ; ++g) acc[g] = 0.0f;
-  // branch-free: a query that skips plane p has weight 0 there, and a
-  // uniform branch per plane would serialize the LDS reads of the loop
-#pragma unroll 8
-  for (int p = 0; p < U; ++p) {
-    const float f = static_cast<float>((stage[p][wsel] >> sh) & 1u);
-    const float4 w = *reinterpret_cast<const float4*>(&s.w[p][0]);
-    const float wg[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-    for (int g = 0; g < GQ; ++g) acc[g] = fmaf(f, wg[g], acc[g]);
-  }
-  const int local = part * kSampleThreads + threadIdx.x;   // 0..1023 within the block
-#pragma unroll
-  for (int g = 0; g < GQ; ++g)
-    a.sample[int64_t(q0 + g) * kSampleMaxKeys + sbi * kSampleBlockKeys + local] =
-        valid ? acc[g] + s.C[g] : -INFINITY;
 }
 
 // ----------------------------------------------------------- block select
@@ -391,6 +320,7 @@ __global__ __launch_bounds__(kSampleThreads) void scan_sample_kernel(ScanArgs a)
 struct SelectLds {
   uint32_t hist[kSelectWaves][256];
   uint32_t total[256];
+  uint32_t wmm[3][kSelectWaves];   // per-wave max, min, count (block_max_min)
   uint32_t sel;
   uint32_t rem;
 };
@@ -478,21 +408,17 @@ __device__ uint3 block_max_min(const uint32_t (&v)[PT], uint32_t pm, SelectLds& 
   const uint2 w = wave_max_min(mx, mn);
   const uint32_t c = read_lane(wave_incl_sum(static_cast<uint32_t>(__popc(pm))), 63);
   if (lane == 0) {
-    L.hist[wave][0] = w.x;
-    L.hist[wave][1] = w.y;
-    L.hist[wave][2] = c;
+    L.wmm[0][wave] = w.x;
+    L.wmm[1][wave] = w.y;
+    L.wmm[2][wave] = c;
   }
   __syncthreads();
-  mx = 0u;
-  mn = 0xffffffffu;
-  uint32_t cnt = 0;
-  for (int ww = 0; ww < static_cast<int>(blockDim.x >> 6); ++ww) {
-    mx = max(mx, L.hist[ww][0]);
-    mn = min(mn, L.hist[ww][1]);
-    cnt += L.hist[ww][2];
-  }
+  // every wave combines the per-wave results, one per lane
+  const bool ok = lane < static_cast<int>(blockDim.x >> 6);
+  const uint2 b = wave_max_min(ok ? L.wmm[0][lane] : 0u, ok ? L.wmm[1][lane] : 0xffffffffu);
+  const uint32_t cnt = read_lane(wave_incl_sum(ok ? L.wmm[2][lane] : 0u), 63);
   __syncthreads();
-  return make_uint3(mx, mn, cnt);
+  return make_uint3(b.x, b.y, cnt);
 }
 
 // r-th largest (1-based, r <= number present) of the present ordered keys
@@ -564,8 +490,9 @@ __device__ void digit_scan(DigitLds& D, uint32_t r) {
   const uint32_t incl = wave_incl_sum(own);
   if (lane == 63) D.wave_total[wave] = incl;
   __syncthreads();
-  uint32_t base = 0;
-  for (int w = 0; w < wave; ++w) base += D.wave_total[w];
+  // totals of the waves before this one: one per lane, prefix-summed
+  const uint32_t wt = wave_incl_sum(lane < kSelectWaves ? D.wave_total[lane] : 0u);
+  const uint32_t base = wave == 0 ? 0u : read_lane(wt, wave - 1);
   const uint32_t excl = base + incl - own;
   D.start[bh] = excl;
   D.start[bl] = excl + ch;
@@ -788,6 +715,112 @@ __device__ __forceinline__ uint32_t row_incl_sum(uint32_t v) {
   return v;
 }
 
+// Scores tiles first_tile + i * tile_stride (i < ntiles) of KV head h with
+// the chunk table T, and calls epi(tile, acc) for each: acc[8X + e] holds,
+// for lane (G, col), query G's limb sums of key 8X + e of the lane's column
+// (see the epilogues).  Plane words stream through the LDS ring by DMA,
+// kMainStages - 1 (tile, block) steps ahead.  All waves of the workgroup
+// call it with the same arguments (it contains barriers).
+template <class Epi>
+__device__ void scan_tiles(const ScanArgs& a, const ChunkTable& T, uint32_t (&ring)[kMainStages][kStageDwords], int h,
+                           int first_tile, int tile_stride, int ntiles, Epi&& epi) {
+  const int nblk = nblocks_of(T.U);
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+  const int lane = threadIdx.x & 63;
+  const int col = lane & 15;
+  const int G = lane >> 4;
+  const int nsteps = max(0, ntiles) * nblk;   // (tile, block) steps
+
+  // Loads.  DMA load q = 2 wave + j (j = 0, 1) of a stage, lane l: row
+  // l >> 3 holds plane q + 8 (l >> 3) of the block, bytes 16 (l & 7) .. + 15
+  // of the tile's 128.  (The eight planes a transpose read gathers then sit
+  // in eight different loads, whose padding spreads them over the banks.)
+  // The buffer's size bounds the reads: words past the head's last plane row
+  // read as zero (past a row's end they read the next row; such keys are
+  // masked out).
+  const char* head = reinterpret_cast<const char*>(a.planes + int64_t(h) * kD * kPlanes * a.ldw);
+  const int64_t head_bytes = int64_t(kD) * kPlanes * a.ldw * 4;
+  const uint32_t nrec = head_bytes > int64_t(0xffffffff) ? 0xffffffffu : static_cast<uint32_t>(head_bytes);
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(head), static_cast<short>(0), static_cast<int>(nrec), 0x00020000);
+  const uint32_t dma_lane_off = 16u * static_cast<uint32_t>(lane & 7);
+  int it_tile = first_tile, it_b = 0, it_slot = 0, issued = 0;   // next step to load (uniform)
+  auto issue = [&]() {
+    if (issued < nsteps) {
+      const uint32_t woff = static_cast<uint32_t>(it_tile * kTileWords) * 4u;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int q = 2 * wave + j;
+        const uint32_t vo = T.rowoff[it_b * kBlockPlanes + q + 8 * (lane >> 3)] + dma_lane_off + woff;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, &ring[it_slot][q * kDmaDwords], 16, vo, 0, 0, 0);
+      }
+      ++issued;
+      if (++it_b == nblk) {
+        it_b = 0;
+        it_tile += tile_stride;
+      }
+      it_slot = it_slot + 1 == kMainStages ? 0 : it_slot + 1;
+    }
+  };
+  // transpose-read address of lane (G, col): plane 16G + col / 2 (row 2G of
+  // DMA load col / 2) of the wave's segment col & 1
+  const uint32_t ring_lane = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&ring[0][0])) +
+                             static_cast<uint32_t>((col >> 1) * kDmaDwords + 2 * G * kTileWords + wave * kWaveWords) * 4u +
+                             8u * static_cast<uint32_t>(col & 1);
+  const uint32_t a_lane = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&T.A[0][G][col]));
+#pragma unroll
+  for (int i = 0; i < kMainStages - 1; ++i) issue();
+
+  int step_i = 0, slot = 0;
+  for (int ti = 0, tile = first_tile; ti < ntiles; ++ti, tile += tile_stride) {
+    v4i acc[16];
+    auto step = [&](auto first, int b) {
+      // the last steps have fewer loads behind them: wait for all
+      if (step_i + kMainStages - 2 < nsteps) {
+        sync_stage<2 * (kMainStages - 2)>();
+      } else {
+        sync_stage<0>();
+      }
+      issue();   // into the slot every wave has finished reading
+      uint32_t x[8];
+      const uint32_t addr = ring_lane + static_cast<uint32_t>(slot * kStageDwords) * 4u;
+      const uint32_t a_addr = a_lane + static_cast<uint32_t>(b * 4 * 16 * 16);
+      v4i A;
+      read_stage(addr, a_addr, x, A);
+      ++step_i;
+      slot = slot + 1 == kMainStages ? 0 : slot + 1;
+      mfma_block<decltype(first)::value>(x, A, acc);
+    };
+    step(std::true_type{}, 0);   // nblk >= 1: an empty union is one block of zero weights
+    for (int b = 1; b < nblk; ++b) step(std::false_type{}, b);
+    epi(tile, acc);
+  }
+}
+
+// Exact limb sums t of the 16 keys of a lane's column (see scan_tiles): key
+// 8X + e comes out scaled by 2^e (-128 for e = 7).  Unscaling limb j is a
+// shift by 8j - e, exact (the sums are multiples of 2^e), and t = l0 + 2^8 l1
+// + 2^16 l2 + 2^24 l3 is exact in wrapping int32 arithmetic because
+// |t| < 2^31.  Keys with e = 7 give -t, which t_of undoes.
+__device__ __forceinline__ void limb_sums(const v4i (&acc)[16], int (&tv)[16]) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int e = i & 7;
+    // (empty asm: keeps the Horner form, which needs one op per limb)
+    uint32_t z = (static_cast<uint32_t>(acc[i].w) << 8) + static_cast<uint32_t>(acc[i].z);
+    asm("" : "+v"(z));
+    uint32_t y = (z << 8) + static_cast<uint32_t>(acc[i].y);   // 2^e (l1 + 2^8 l2 + 2^16 l3)
+    asm("" : "+v"(y));
+    tv[i] = static_cast<int>((y << (8 - e)) + static_cast<uint32_t>(acc[i].x >> e));
+  }
+}
+
+// First key of the 8 keys 8X .. 8X + 7 of lane (G, col)'s column in a tile
+// (the wave's segments are 64 keys; X picks the second pair of segments).
+__device__ __forceinline__ int64_t column_key(int tile, int wave, int col, int X) {
+  return (int64_t(tile) * kTileWords + wave * kWaveWords) * 32 + (col >> 3) * 64 + 8 * (col & 7) + 128 * X;
+}
+
 template <int GQ>
 __global__ __launch_bounds__(kMainThreads, kMainWgPerCu) void scan_main_kernel(ScanArgs a) {
   __shared__ ChunkTable T;
@@ -806,7 +839,6 @@ __global__ __launch_bounds__(kMainThreads, kMainWgPerCu) void scan_main_kernel(S
     if (threadIdx.x < 4) theta_s[threadIdx.x] = static_cast<int>(threadIdx.x) < GQ ? a.theta[q0 + threadIdx.x] : 0.0f;
   }
   __syncthreads();
-  const int nblk = nblocks_of(T.U);
 
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int lane = threadIdx.x & 63;
@@ -834,105 +866,27 @@ __global__ __launch_bounds__(kMainThreads, kMainWgPerCu) void scan_main_kernel(S
 
   const int tile_begin = blockIdx.x * a.tiles_per_wg;
   const int tile_end = min(a.tiles, tile_begin + a.tiles_per_wg);
-  const int nsteps = max(0, tile_end - tile_begin) * nblk;   // (tile, block) steps of this workgroup
-
-  // Loads.  DMA load q = 2 wave + j (j = 0, 1) of a stage, lane l: row
-  // l >> 3 holds plane q + 8 (l >> 3) of the block, bytes 16 (l & 7) .. + 15
-  // of the tile's 128.  (The eight planes a transpose read gathers then sit
-  // in eight different loads, whose padding spreads them over the banks.)
-  // The buffer's size bounds the reads: words past the head's last plane row
-  // read as zero (past a row's end they read the next row; such keys are
-  // masked out).
-  const char* head = reinterpret_cast<const char*>(a.planes + int64_t(h) * kD * kPlanes * a.ldw);
-  const int64_t head_bytes = int64_t(kD) * kPlanes * a.ldw * 4;
-  const uint32_t nrec = head_bytes > int64_t(0xffffffff) ? 0xffffffffu : static_cast<uint32_t>(head_bytes);
-  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<char*>(head), static_cast<short>(0), static_cast<int>(nrec), 0x00020000);
-  const uint32_t dma_lane_off = 16u * static_cast<uint32_t>(lane & 7);
-  int it_tile = tile_begin, it_b = 0, it_slot = 0, issued = 0;   // next step to load (uniform)
-  auto issue = [&]() {
-    if (issued < nsteps) {
-      const uint32_t woff = static_cast<uint32_t>(it_tile * kTileWords) * 4u;
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int q = 2 * wave + j;
-        const uint32_t vo = T.rowoff[it_b * kBlockPlanes + q + 8 * (lane >> 3)] + dma_lane_off + woff;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, &ring[it_slot][q * kDmaDwords], 16, vo, 0, 0, 0);
-      }
-      ++issued;
-      if (++it_b == nblk) { it_b = 0; ++it_tile; }
-      it_slot = it_slot + 1 == kMainStages ? 0 : it_slot + 1;
-    }
-  };
-  // transpose-read address of lane (G, col): plane 16G + col / 2 (row 2G of
-  // DMA load col / 2) of the wave's segment col & 1
-  const uint32_t ring_lane = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&ring[0][0])) +
-                             static_cast<uint32_t>((col >> 1) * kDmaDwords + 2 * G * kTileWords + wave * kWaveWords) * 4u +
-                             8u * static_cast<uint32_t>(col & 1);
-  const uint32_t a_lane = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&T.A[0][G][col]));
-#pragma unroll
-  for (int i = 0; i < kMainStages - 1; ++i) issue();
-
   uint32_t wc0 = 0, wc1 = 0, wc2 = 0, wc3 = 0;   // this wave's candidates per query so far (uniform)
-  int step_i = 0, slot = 0;
-  for (int tile = tile_begin; tile < tile_end; ++tile) {
-    v4i acc[16];
-    auto step = [&](auto first, int b) {
-      // the last steps have fewer loads behind them: wait for all
-      if (step_i + kMainStages - 2 < nsteps) {
-        sync_stage<2 * (kMainStages - 2)>();
-      } else {
-        sync_stage<0>();
-      }
-      issue();   // into the slot every wave has finished reading
-      uint32_t x[8];
-      const uint32_t addr = ring_lane + static_cast<uint32_t>(slot * kStageDwords) * 4u;
-      const uint32_t a_addr = a_lane + static_cast<uint32_t>(b * 4 * 16 * 16);
-      v4i A;
-      read_stage(addr, a_addr, x, A);
-      ++step_i;
-      slot = slot + 1 == kMainStages ? 0 : slot + 1;
-      mfma_block<decltype(first)::value>(x, A, acc);
-    };
-    step(std::true_type{}, 0);   // nblk >= 1: an empty union is one block of zero weights
-    for (int b = 1; b < nblk; ++b) step(std::false_type{}, b);
-
-    // epilogue: this lane holds query G's four limb sums l0..l3 for the 16
-    // keys of its column, key i = 8X + e scaled by 2^e (-128 for e = 7).
-    // Unscaling limb j is a shift by 8j - e, exact (the sums are multiples of
-    // 2^e), and t = l0 + 2^8 l1 + 2^16 l2 + 2^24 l3 is exact in wrapping
-    // int32 arithmetic because |t| < 2^31.  Keys with e = 7 give -t.
-    // key 8X + e of the column: key_of(X) + e
-    const int64_t kbase = (int64_t(tile) * kTileWords + wave * kWaveWords) * 32 + (col >> 3) * 64 + 8 * (col & 7);
-    auto key_of = [&](int X) { return kbase + 128 * X; };
-    auto nvalid_of = [&](int X) {
-      return qvalid ? static_cast<int>(max<int64_t>(0, min<int64_t>(8, a.n - key_of(X)))) : 0;
-    };
-    const int nv0 = nvalid_of(0), nv1 = nvalid_of(1);
+  scan_tiles(a, T, ring, h, tile_begin, 1, tile_end - tile_begin, [&](int tile, const v4i (&acc)[16]) {
+    const int64_t key0 = column_key(tile, wave, col, 0), key1 = column_key(tile, wave, col, 1);
+    auto key_of = [&](int i) { return (i < 8 ? key0 : key1) + (i & 7); };
+    const int nv0 = qvalid ? static_cast<int>(max<int64_t>(0, min<int64_t>(8, a.n - key0))) : 0;
+    const int nv1 = qvalid ? static_cast<int>(max<int64_t>(0, min<int64_t>(8, a.n - key1))) : 0;
     int tv[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int e = i & 7;
-      // (empty asm: keeps the Horner form, which needs one op per limb)
-      uint32_t z = (static_cast<uint32_t>(acc[i].w) << 8) + static_cast<uint32_t>(acc[i].z);
-      asm("" : "+v"(z));
-      uint32_t y = (z << 8) + static_cast<uint32_t>(acc[i].y);   // 2^e (l1 + 2^8 l2 + 2^16 l3)
-      asm("" : "+v"(y));
-      tv[i] = static_cast<int>((y << (8 - e)) + static_cast<uint32_t>(acc[i].x >> e));
-    }
+    limb_sums(acc, tv);
     auto t_of = [&](int i) { return (i & 7) == 7 ? -tv[i] : tv[i]; };
     // (scale and offset re-read from LDS: only candidates need them)
     auto score_of = [&](int i) { return fmaf(static_cast<float>(t_of(i)), T.sigma[G], T.C[G]); };
     if (a.all_scores) {
 #pragma unroll
       for (int i = 0; i < 16; ++i)
-        if ((i & 7) < (i < 8 ? nv0 : nv1)) a.all_scores[int64_t(q0 + G) * a.n + key_of(i >> 3) + (i & 7)] = score_of(i);
+        if ((i & 7) < (i < 8 ? nv0 : nv1)) a.all_scores[int64_t(q0 + G) * a.n + key_of(i)] = score_of(i);
     }
     uint32_t bits = 0;
 #pragma unroll
     for (int i = 0; i < 16; ++i) bits |= t_of(i) >= theta_i ? (1u << i) : 0u;
     bits &= ((1u << nv0) - 1u) | (((1u << nv1) - 1u) << 8);
-    if (__ballot(bits != 0) == 0) continue;   // uniform
+    if (__ballot(bits != 0) == 0) return;   // uniform
     // Candidates go to this wave's LDS buffer of their query: a DPP row holds
     // one query (lanes 16G..16G+15) and a row prefix sum orders its lanes.
     // Slots past the buffer spill to the global list, reserved with one
@@ -967,7 +921,7 @@ __global__ __launch_bounds__(kMainThreads, kMainWgPerCu) void scan_main_kernel(S
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         if (bits & (1u << i)) {
-          const uint2 e = make_uint2(__float_as_uint(score_of(i)), static_cast<uint32_t>(key_of(i >> 3) + (i & 7)));
+          const uint2 e = make_uint2(__float_as_uint(score_of(i)), static_cast<uint32_t>(key_of(i)));
           if (slot_c < cap) {
             cbuf[wave][G][slot_c] = e;
           } else {
@@ -978,7 +932,7 @@ __global__ __launch_bounds__(kMainThreads, kMainWgPerCu) void scan_main_kernel(S
         }
       }
     }
-  }
+  });
   // flush: one global atomic per query reserves the buffered candidates'
   // slots, in wave order
   if (lane == 0) {
@@ -1007,6 +961,43 @@ __global__ __launch_bounds__(kMainThreads, kMainWgPerCu) void scan_main_kernel(S
     for (uint32_t i = lane; i < kept; i += 64)
       if (b0 + i < static_cast<uint32_t>(kCandCap)) a.cand[int64_t(q0 + g) * kCandCap + b0 + i] = cbuf[wave][g][i];
   }
+}
+
+// ------------------------------------------------------------------ sample
+
+// Workgroup = (sampled 1024-key block, KV head, query chunk): builds the
+// chunk's table in LDS (workgroup 0 also stores it for the main kernel) and
+// scores the block's keys exactly as the main kernel does.
+template <int GQ>
+__global__ __launch_bounds__(kMainThreads) void scan_sample_kernel(ScanArgs a) {
+  __shared__ UnionLds<GQ> s;
+  __shared__ ChunkTable T;
+  __shared__ double wsum[4];
+  __shared__ uint32_t ring[kMainStages][kStageDwords];
+  const int h = blockIdx.y / a.cph;
+  const int q0 = h * a.group + a.qoff + (blockIdx.y % a.cph) * kQueryChunk;
+  build_union<GQ>(a, h, q0, s);
+  write_chunk_table<GQ>(a, s, T, wsum, blockIdx.x == 0);
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+  const int lane = threadIdx.x & 63;
+  const int col = lane & 15;
+  const int G = lane >> 4;
+  const int sbi = blockIdx.x;
+  const int tile = sbi * a.sample_stride;   // a sampled block is one tile
+  scan_tiles(a, T, ring, h, tile, 0, 1, [&](int tile_, const v4i (&acc)[16]) {
+    if (G >= GQ) return;
+    int tv[16];
+    limb_sums(acc, tv);
+    const float sigma = T.sigma[G], Cq = T.C[G];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int64_t key = column_key(tile_, wave, col, i >> 3) + (i & 7);
+      const int t = (i & 7) == 7 ? -tv[i] : tv[i];
+      const float sc = fmaf(static_cast<float>(t), sigma, Cq);
+      const int local = static_cast<int>(key - int64_t(tile_) * kTileWords * 32);
+      a.sample[int64_t(q0 + G) * kSampleMaxKeys + sbi * kSampleBlockKeys + local] = key < a.n ? sc : -INFINITY;
+    }
+  });
 }
 
 // ------------------------------------------------------------------- merge
@@ -1303,9 +1294,7 @@ template <int GQ>
 void launch_chunk_class(const ScanArgs& a, int H, int nsb, bool sample_phase, hipEvent_t ev_start,
                         hipEvent_t ev_stop, hipStream_t stream) {
   if (sample_phase) {
-    // one extra workgroup per chunk builds its table
-    hipLaunchKernelGGL(scan_sample_kernel<GQ>, dim3(nsb * kSampleWgPerBlock + 1, H * a.cph),
-                       dim3(kSampleThreads), 0, stream, a);
+    hipLaunchKernelGGL(scan_sample_kernel<GQ>, dim3(nsb, H * a.cph), dim3(kMainThreads), 0, stream, a);
   } else {
     const int wgs = (a.tiles + a.tiles_per_wg - 1) / a.tiles_per_wg;
     hipExtLaunchKernelGGL(scan_main_kernel<GQ>, dim3(wgs, H * a.cph), dim3(kMainThreads), 0, stream,
