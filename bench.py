@@ -148,9 +148,10 @@ def main():
     scan_ws = fa.alloc_workspace(fa.workspace_bytes(fa.FATHOM_OP_SCAN, store, Q, k), dev)
 
     def step_fn(i):
-        fa.allocate(qd, var, G, budget, store, out=alloc)
-        fa.scan_topk(copies[i % len(copies)], lo, step, store, qd, alloc, G, k, workspace=scan_ws,
-                     out_idx=out_idx, out_score=out_score)
+        # allocation and scan + top-k in one call (the allocation is computed
+        # inside the scan's first kernel)
+        fa.allocate_scan_topk(copies[i % len(copies)], lo, step, var, store, qd, G, budget, k,
+                              workspace=scan_ws, alloc=alloc, out_idx=out_idx, out_score=out_score)
 
     if not args.no_kernel_timing:
         fa.timing_enable(True)    # creates the event pool outside the timed region

@@ -124,6 +124,17 @@ int fathom_scan_topk(const uint32_t* planes, const float* lo, const float* step,
                      int32_t num_q, int32_t group, int32_t k, int32_t* out_idx, float* out_score,
                      float* all_scores, void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/* Allocation and scan in one call: the same results as fathom_allocate
+ * (budget_bits, var) followed by fathom_scan_topk with that allocation, which
+ * is also written to alloc (uint8 [num_q][d]).  The allocation is computed
+ * inside the scan's first kernel (one wavefront per query of each KV-head
+ * chunk), so the pair costs one kernel launch less.  Arguments as in the two
+ * calls; no all_scores output. */
+int fathom_allocate_scan_topk(const uint32_t* planes, const float* lo, const float* step, const float* var,
+                              const fathom_store_desc* store, const float* q, int32_t num_q, int32_t group,
+                              int32_t budget_bits, int32_t k, uint8_t* alloc, int32_t* out_idx,
+                              float* out_score, void* workspace, size_t workspace_bytes, void* hip_stream);
+
 /* Device-visible address of pinned host memory (allocated with hipHostMalloc
  * or torch pin_memory), for a plane store kept in host RAM ([Art] para 1;
  * [Abs] s1: the index lives in host memory).  Not for registered memory. */

@@ -98,6 +98,66 @@ constexpr size_t kMaxTimed = 4096;
 
 }  // namespace
 
+namespace {
+
+int scan_impl(const char* where, const uint32_t* planes, const float* lo, const float* step,
+              const fathom_store_desc* store, const float* q, const uint8_t* alloc, int32_t num_q,
+              int32_t group, int32_t k, int32_t* out_idx, float* out_score, float* all_scores,
+              void* workspace, size_t workspace_bytes, void* hip_stream, const float* var, int32_t budget_bits,
+              uint8_t* alloc_out) {
+  int st = check_store(store);
+  if (st != FATHOM_OK) return st;
+  if (!planes || !lo || !step || !q || !out_idx || !out_score)
+    return fail(FATHOM_ERR_INVALID_ARG, "planes, lo, step, q, out_idx and out_score must be non-NULL");
+  if (var) {
+    if (!alloc_out) return fail(FATHOM_ERR_INVALID_ARG, "alloc must be non-NULL");
+    if (budget_bits < 0 || budget_bits > kPlanes * kD)
+      return fail(FATHOM_ERR_INVALID_ARG, "budget_bits = %d outside [0, %d]", budget_bits, kPlanes * kD);
+    if (!aligned(q, 8) || !aligned(var, 8) || !aligned(alloc_out, 2))
+      return fail(FATHOM_ERR_INVALID_ARG, "q and var must be 8-byte aligned, alloc 2-byte aligned");
+  } else if (!alloc) {
+    return fail(FATHOM_ERR_INVALID_ARG, "alloc must be non-NULL");
+  }
+  if (num_q < 1 || group < 1) return fail(FATHOM_ERR_INVALID_ARG, "num_q and group must be >= 1");
+  if (static_cast<int64_t>(store->num_kv_heads) * group != num_q)
+    return fail(FATHOM_ERR_INVALID_ARG, "num_q = %d must equal num_kv_heads (%d) * group (%d)", num_q,
+                store->num_kv_heads, group);
+  if (k < 1 || k > store->n) return fail(FATHOM_ERR_INVALID_ARG, "k = %d outside [1, n]", k);
+  if (k > FATHOM_MAX_K) return fail(FATHOM_ERR_UNSUPPORTED, "k = %d exceeds FATHOM_MAX_K (%d)", k, FATHOM_MAX_K);
+  if (!aligned(planes, 16)) return fail(FATHOM_ERR_INVALID_ARG, "planes must be 16-byte aligned");
+  if (!aligned(lo, 4) || !aligned(step, 4) || !aligned(q, 4) || !aligned(out_idx, 4) ||
+      !aligned(out_score, 4) || (all_scores && !aligned(all_scores, 4)))
+    return fail(FATHOM_ERR_INVALID_ARG, "float and int32 arrays must be 4-byte aligned");
+  const ScanLayout L = scan_layout(num_q);
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < L.total)
+    return fail(FATHOM_ERR_WORKSPACE, "scan needs a 256-byte aligned workspace of %zu bytes (got %zu)",
+                L.total, workspace_bytes);
+  char* w = static_cast<char*>(workspace);
+  ScanWorkspace ws{reinterpret_cast<float*>(w + L.theta), reinterpret_cast<uint32_t*>(w + L.count),
+                   reinterpret_cast<float*>(w + L.sample), reinterpret_cast<uint2*>(w + L.cand),
+                   static_cast<void*>(w + L.tables)};
+
+  ScanTiming timing;
+  bool timed = false;
+  {
+    std::lock_guard<std::mutex> lock(g_timing_mu);
+    if (g_timing_on && g_events_used < g_events.size()) {
+      timing.start = g_events[g_events_used].first;
+      timing.stop = g_events[g_events_used].second;
+      ++g_events_used;
+      timed = true;
+    }
+  }
+  hipError_t e = launch_scan_topk(planes, lo, step, store->num_kv_heads, store->n, store->ldw, q, alloc,
+                                  num_q, group, k, out_idx, out_score, all_scores, ws,
+                                  timed ? &timing : nullptr, static_cast<hipStream_t>(hip_stream), var,
+                                  budget_bits, alloc_out);
+  if (e != hipSuccess) return hip_fail(e, where);
+  return ok();
+}
+
+}  // namespace
+
 extern "C" {
 
 int64_t fathom_plane_ldw(int64_t n) {
@@ -168,45 +228,17 @@ int fathom_scan_topk(const uint32_t* planes, const float* lo, const float* step,
                      const fathom_store_desc* store, const float* q, const uint8_t* alloc,
                      int32_t num_q, int32_t group, int32_t k, int32_t* out_idx, float* out_score,
                      float* all_scores, void* workspace, size_t workspace_bytes, void* hip_stream) {
-  int st = check_store(store);
-  if (st != FATHOM_OK) return st;
-  if (!planes || !lo || !step || !q || !alloc || !out_idx || !out_score)
-    return fail(FATHOM_ERR_INVALID_ARG, "planes, lo, step, q, alloc, out_idx and out_score must be non-NULL");
-  if (num_q < 1 || group < 1) return fail(FATHOM_ERR_INVALID_ARG, "num_q and group must be >= 1");
-  if (static_cast<int64_t>(store->num_kv_heads) * group != num_q)
-    return fail(FATHOM_ERR_INVALID_ARG, "num_q = %d must equal num_kv_heads (%d) * group (%d)", num_q,
-                store->num_kv_heads, group);
-  if (k < 1 || k > store->n) return fail(FATHOM_ERR_INVALID_ARG, "k = %d outside [1, n]", k);
-  if (k > FATHOM_MAX_K) return fail(FATHOM_ERR_UNSUPPORTED, "k = %d exceeds FATHOM_MAX_K (%d)", k, FATHOM_MAX_K);
-  if (!aligned(planes, 16)) return fail(FATHOM_ERR_INVALID_ARG, "planes must be 16-byte aligned");
-  if (!aligned(lo, 4) || !aligned(step, 4) || !aligned(q, 4) || !aligned(out_idx, 4) ||
-      !aligned(out_score, 4) || (all_scores && !aligned(all_scores, 4)))
-    return fail(FATHOM_ERR_INVALID_ARG, "float and int32 arrays must be 4-byte aligned");
-  const ScanLayout L = scan_layout(num_q);
-  if (!workspace || !aligned(workspace, 256) || workspace_bytes < L.total)
-    return fail(FATHOM_ERR_WORKSPACE, "scan needs a 256-byte aligned workspace of %zu bytes (got %zu)",
-                L.total, workspace_bytes);
-  char* w = static_cast<char*>(workspace);
-  ScanWorkspace ws{reinterpret_cast<float*>(w + L.theta), reinterpret_cast<uint32_t*>(w + L.count),
-                   reinterpret_cast<float*>(w + L.sample), reinterpret_cast<uint2*>(w + L.cand),
-                   static_cast<void*>(w + L.tables)};
+  return scan_impl("fathom_scan_topk launch", planes, lo, step, store, q, alloc, num_q, group, k, out_idx,
+                   out_score, all_scores, workspace, workspace_bytes, hip_stream, nullptr, 0, nullptr);
+}
 
-  ScanTiming timing;
-  bool timed = false;
-  {
-    std::lock_guard<std::mutex> lock(g_timing_mu);
-    if (g_timing_on && g_events_used < g_events.size()) {
-      timing.start = g_events[g_events_used].first;
-      timing.stop = g_events[g_events_used].second;
-      ++g_events_used;
-      timed = true;
-    }
-  }
-  hipError_t e = launch_scan_topk(planes, lo, step, store->num_kv_heads, store->n, store->ldw, q, alloc,
-                                  num_q, group, k, out_idx, out_score, all_scores, ws,
-                                  timed ? &timing : nullptr, static_cast<hipStream_t>(hip_stream));
-  if (e != hipSuccess) return hip_fail(e, "fathom_scan_topk launch");
-  return ok();
+int fathom_allocate_scan_topk(const uint32_t* planes, const float* lo, const float* step, const float* var,
+                              const fathom_store_desc* store, const float* q, int32_t num_q, int32_t group,
+                              int32_t budget_bits, int32_t k, uint8_t* alloc, int32_t* out_idx,
+                              float* out_score, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  if (!var) return fail(FATHOM_ERR_INVALID_ARG, "var must be non-NULL");
+  return scan_impl("fathom_allocate_scan_topk launch", planes, lo, step, store, q, nullptr, num_q, group, k,
+                   out_idx, out_score, nullptr, workspace, workspace_bytes, hip_stream, var, budget_bits, alloc);
 }
 
 int fathom_host_device_pointer(void* pinned_host, void** device_ptr) {

@@ -61,6 +61,7 @@ hipError_t launch_scan_topk(const uint32_t* planes, const float* lo, const float
                             int64_t n, int64_t ldw, const float* q, const uint8_t* alloc, int num_q,
                             int group, int k, int32_t* out_idx, float* out_score,
                             float* all_scores, const ScanWorkspace& ws, const ScanTiming* timing,
-                            hipStream_t stream);
+                            hipStream_t stream, const float* var = nullptr, int budget = 0,
+                            uint8_t* alloc_out = nullptr);
 
 }  // namespace fathom

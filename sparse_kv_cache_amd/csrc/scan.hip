@@ -46,6 +46,7 @@
 #include <climits>
 #include <type_traits>
 
+#include "allocate_wave.h"
 #include "fathom_internal.h"
 
 namespace fathom {
@@ -79,6 +80,9 @@ struct ScanArgs {
   const float* step;
   const float* q;
   const uint8_t* alloc;
+  const float* var;     // non-null: the sample kernel computes the allocations itself
+  int budget;           //   (budget bits) and writes them to alloc_out, which alloc then names
+  uint8_t* alloc_out;
   int64_t n;
   int64_t ldw;
   int nwords;         // ceil(n / 32)
@@ -222,10 +226,11 @@ __device__ inline double pow2_3_minus(int b) {
 
 
 // Builds the union plane list of a query chunk (queries q0 .. q0+GQ-1 on
-// KV head h), the per-plane weights and the score offsets C_q.
+// KV head h, allocation of query q0 + g at ab[g * kD ..]), the per-plane
+// weights and the score offsets C_q.
 // Needs blockDim.x >= kD; ends with __syncthreads().
 template <int GQ>
-__device__ void build_union(const ScanArgs& a, int h, int q0, UnionLds<GQ>& s) {
+__device__ void build_union(const ScanArgs& a, int h, int q0, const uint8_t* ab, UnionLds<GQ>& s) {
   const int t = threadIdx.x;
   int u = 0, bq[4] = {0, 0, 0, 0};
   float qv[4] = {0.0f, 0.0f, 0.0f, 0.0f}, st = 0.0f;
@@ -235,7 +240,7 @@ __device__ void build_union(const ScanArgs& a, int h, int q0, UnionLds<GQ>& s) {
     double cp[GQ];
 #pragma unroll
     for (int g = 0; g < GQ; ++g) {
-      bq[g] = min(static_cast<int>(a.alloc[int64_t(q0 + g) * kD + t]), kPlanes);
+      bq[g] = min(static_cast<int>(ab[g * kD + t]), kPlanes);
       qv[g] = a.q[int64_t(q0 + g) * kD + t];
       u = max(u, bq[g]);
       cp[g] = static_cast<double>(qv[g]) *
@@ -967,19 +972,33 @@ __global__ __launch_bounds__(kMainThreads, kMainWgPerCu) void scan_main_kernel(S
 
 // Workgroup = (sampled 1024-key block, KV head, query chunk): builds the
 // chunk's table in LDS (workgroup 0 also stores it for the main kernel) and
-// scores the block's keys exactly as the main kernel does.
+// scores the block's keys exactly as the main kernel does.  With a.var set,
+// wavefront g first computes the allocation of query q0 + g (workgroup 0
+// also stores it in a.alloc_out).
 template <int GQ>
 __global__ __launch_bounds__(kMainThreads) void scan_sample_kernel(ScanArgs a) {
   __shared__ UnionLds<GQ> s;
   __shared__ ChunkTable T;
   __shared__ double wsum[4];
   __shared__ uint32_t ring[kMainStages][kStageDwords];
+  __shared__ uint16_t s_alloc[4][kD / 2];
   const int h = blockIdx.y / a.cph;
   const int q0 = h * a.group + a.qoff + (blockIdx.y % a.cph) * kQueryChunk;
-  build_union<GQ>(a, h, q0, s);
-  write_chunk_table<GQ>(a, s, T, wsum, blockIdx.x == 0);
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int lane = threadIdx.x & 63;
+  const uint8_t* ab = a.alloc + int64_t(q0) * kD;
+  if (a.var) {   // uniform
+    if (wave < GQ) {
+      const uint2 b = allocate_query_wave(a.q + int64_t(q0 + wave) * kD, a.var + int64_t(h) * kD, a.budget);
+      const uint16_t pair = static_cast<uint16_t>(b.x | (b.y << 8));
+      s_alloc[wave][lane] = pair;
+      if (blockIdx.x == 0) *reinterpret_cast<uint16_t*>(a.alloc_out + int64_t(q0 + wave) * kD + 2 * lane) = pair;
+    }
+    __syncthreads();
+    ab = reinterpret_cast<const uint8_t*>(&s_alloc[0][0]);
+  }
+  build_union<GQ>(a, h, q0, ab, s);
+  write_chunk_table<GQ>(a, s, T, wsum, blockIdx.x == 0);
   const int col = lane & 15;
   const int G = lane >> 4;
   const int sbi = blockIdx.x;
@@ -1318,13 +1337,18 @@ hipError_t launch_scan_topk(const uint32_t* planes, const float* lo, const float
                             int64_t n, int64_t ldw, const float* q, const uint8_t* alloc, int num_q,
                             int group, int k, int32_t* out_idx, float* out_score,
                             float* all_scores, const ScanWorkspace& ws, const ScanTiming* timing,
-                            hipStream_t stream) {
+                            hipStream_t stream, const float* var, int budget, uint8_t* alloc_out) {
   ScanArgs a{};
   a.planes = planes;
   a.lo = lo;
   a.step = step;
   a.q = q;
-  a.alloc = alloc;
+  // fused allocation: the sample kernel writes alloc_out, which later
+  // kernels read as the allocation
+  a.alloc = var ? alloc_out : alloc;
+  a.var = var;
+  a.budget = budget;
+  a.alloc_out = alloc_out;
   a.n = n;
   a.ldw = ldw;
   a.nwords = static_cast<int>((n + 31) / 32);

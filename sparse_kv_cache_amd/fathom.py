@@ -31,6 +31,7 @@ EXPORTS = (
     "fathom_pack_planes",
     "fathom_allocate",
     "fathom_scan_topk",
+    "fathom_allocate_scan_topk",
     "fathom_host_device_pointer",
     "fathom_status_string",
     "fathom_last_error",
@@ -70,6 +71,7 @@ def _load():
         "fathom_pack_planes": (ctypes.c_int, [P, i64, i64, SD, P, P, P, P, P, sz, P]),
         "fathom_allocate": (ctypes.c_int, [P, i32, i32, P, SD, i32, P, P]),
         "fathom_scan_topk": (ctypes.c_int, [P, P, P, SD, P, P, i32, i32, i32, P, P, P, P, sz, P]),
+        "fathom_allocate_scan_topk": (ctypes.c_int, [P, P, P, P, SD, P, i32, i32, i32, i32, P, P, P, P, sz, P]),
         "fathom_host_device_pointer": (ctypes.c_int, [P, ctypes.POINTER(P)]),
         "fathom_status_string": (ctypes.c_char_p, [i32]),
         "fathom_last_error": (ctypes.c_char_p, []),
@@ -180,6 +182,30 @@ def scan_topk(planes: torch.Tensor, lo: torch.Tensor, step: torch.Tensor, store:
                               _ptr(workspace), workspace.numel(), _stream(stream))
     _check(st, "fathom_scan_topk")
     return out_idx, out_score
+
+
+def allocate_scan_topk(planes: torch.Tensor, lo: torch.Tensor, step: torch.Tensor, var: torch.Tensor,
+                       store: StoreDesc, q: torch.Tensor, group: int, budget: int, k: int, *,
+                       workspace: Optional[torch.Tensor] = None, alloc: Optional[torch.Tensor] = None,
+                       out_idx: Optional[torch.Tensor] = None, out_score: Optional[torch.Tensor] = None,
+                       planes_ptr: Optional[int] = None, stream=None):
+    """allocate() then scan_topk() in one call: (alloc uint8 [Q, d], idx, score)."""
+    Q, d = q.shape
+    dev = q.device
+    if alloc is None:
+        alloc = torch.empty((Q, d), dtype=torch.uint8, device=dev)
+    if out_idx is None:
+        out_idx = torch.empty((Q, k), dtype=torch.int32, device=dev)
+    if out_score is None:
+        out_score = torch.empty((Q, k), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = alloc_workspace(workspace_bytes(FATHOM_OP_SCAN, store, Q, k), dev)
+    pp = ctypes.c_void_p(planes_ptr) if planes_ptr is not None else _ptr(planes)
+    st = lib.fathom_allocate_scan_topk(pp, _ptr(lo), _ptr(step), _ptr(var), ctypes.byref(store), _ptr(q),
+                                       Q, group, budget, k, _ptr(alloc), _ptr(out_idx), _ptr(out_score),
+                                       _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(st, "fathom_allocate_scan_topk")
+    return alloc, out_idx, out_score
 
 
 def host_device_pointer(pinned: torch.Tensor) -> int:

@@ -256,6 +256,33 @@ def test_allocation_sweep():
         assert np.array_equal(got, ref), B
 
 
+@pytest.mark.parametrize("n,H,group,budget,k", [
+    (1, 1, 1, 92, 1),
+    (5017, 2, 6, 136, 257),
+    (70000, 1, 5, 92, 4000),
+    (40000, 2, 3, 0, 300),
+    (50000, 2, 4, 512, 1000),
+])
+def test_fused_allocate_scan_matches_two_calls(n, H, group, budget, k):
+    """fathom_allocate_scan_topk computes the allocation inside the scan's
+    first kernel (chunks of 4 query heads, and a smaller last chunk when the
+    group is not a multiple of 4): allocation, indices and scores are
+    identical to fathom_allocate followed by fathom_scan_topk, and the
+    allocation to the oracle's."""
+    say("fused", n, H, group, budget, k)
+    keys, q = synth.make_inputs(101 + n, H, n, H * group)
+    planes, lo, step, var = gpu_pack(keys)
+    store = fa.store_desc(H, n, 128)
+    qd = dev(q)
+    alloc = fa.allocate(qd, var, group, budget, store)
+    idx, val = fa.scan_topk(planes, lo, step, store, qd, alloc, group, k)
+    f_alloc, f_idx, f_val = fa.allocate_scan_topk(planes, lo, step, var, store, qd, group, budget, k)
+    assert np.array_equal(host(f_alloc), host(alloc))
+    assert np.array_equal(host(f_alloc), O.allocate_all(q, host(var), group, budget))
+    assert np.array_equal(host(f_idx), host(idx))
+    assert np.array_equal(host(f_val), host(val))
+
+
 def test_host_resident_store_matches_device():
     """The store read zero-copy from pinned host memory gives the same
     result as the HBM-resident store."""
@@ -312,6 +339,11 @@ def test_qwen3_8b_1m_full_size():
     assert np.array_equal(host(alloc), alloc_ref)
     idx, val = fa.scan_topk(planes, lo, step, store, qd, alloc, G, w.k)
     idx, val = host(idx), host(val)
+    # the fused call the benchmark times gives the same allocation and top-k
+    f_alloc, f_idx, f_val = fa.allocate_scan_topk(planes, lo, step, var, store, qd, G, 92, w.k)
+    assert np.array_equal(host(f_alloc), alloc_ref)
+    assert np.array_equal(host(f_idx), idx)
+    assert np.array_equal(host(f_val), val)
     for i in range(w.num_q):
         l, s, _, codes = heads[i // G]
         ref_sel = O.scores_from_codes(codes[idx[i]], l, s, q[i], alloc_ref[i])
