@@ -305,15 +305,25 @@ __device__ void build_union(const ScanArgs& a, int h, int q0, const uint8_t* ab,
 template <int GQ>
 __device__ void build_limbs(const UnionLds<GQ>& s, ChunkTable& T, double (&wsum)[4], int nblk);
 
+// Workgroup barrier for LDS data only: unlike __syncthreads() it does not
+// wait for outstanding global loads, so LDS DMA loads issued before it stay
+// in flight.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory"); }
+
+// First part: rows, offsets and union size (a barrier must follow).
 template <int GQ>
-__device__ void write_chunk_table(const ScanArgs& a, const UnionLds<GQ>& s, ChunkTable& T, double (&wsum)[4],
-                                  bool store) {
+__device__ void table_rows(const UnionLds<GQ>& s, ChunkTable& T) {
   const int U = s.U;
-  const int nblk = nblocks_of(U);
   for (int i = threadIdx.x; i < kMaxUnion + kPadPlanes; i += blockDim.x) T.rowoff[i] = i < U ? s.rowoff[i] : 0u;
   if (threadIdx.x < 4) T.C[threadIdx.x] = static_cast<int>(threadIdx.x) < GQ ? s.C[threadIdx.x] : 0.0f;
   if (threadIdx.x == 0) T.U = U;
-  build_limbs<GQ>(s, T, wsum, nblk);   // ends with a barrier
+}
+
+// Second part: the A operands and scales, then the store.
+template <int GQ>
+__device__ void table_limbs(const ScanArgs& a, const UnionLds<GQ>& s, ChunkTable& T, double (&wsum)[4],
+                            bool store) {
+  build_limbs<GQ>(s, T, wsum, nblocks_of(s.U));   // ends with a barrier
   if (!store) return;
   uint4* dst = reinterpret_cast<uint4*>(static_cast<char*>(a.tables) + size_t(chunk_index(a)) * kChunkTableBytes);
   const uint4* src = reinterpret_cast<const uint4*>(&T);
@@ -622,7 +632,7 @@ __device__ void build_limbs(const UnionLds<GQ>& s, ChunkTable& T, double (&wsum)
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
   for (int i = t; i < P * 4; i += blockDim.x) {
     const int p = i >> 2, g = i & 3;
     const double ws = wsum[g];
@@ -636,7 +646,7 @@ __device__ void build_limbs(const UnionLds<GQ>& s, ChunkTable& T, double (&wsum)
       v = (v - d) >> 8;
     }
   }
-  __syncthreads();
+  lds_barrier();
 }
 
 typedef uint32_t v2u __attribute__((ext_vector_type(2)));
@@ -721,36 +731,55 @@ __device__ __forceinline__ uint32_t row_incl_sum(uint32_t v) {
 }
 
 // Scores tiles first_tile + i * tile_stride (i < ntiles) of KV head h with
-// the chunk table T, and calls epi(tile, acc) for each: acc[8X + e] holds,
-// for lane (G, col), query G's limb sums of key 8X + e of the lane's column
-// (see the epilogues).  Plane words stream through the LDS ring by DMA,
-// kMainStages - 1 (tile, block) steps ahead.  All waves of the workgroup
-// call it with the same arguments (it contains barriers).
-template <class Epi>
-__device__ void scan_tiles(const ScanArgs& a, const ChunkTable& T, uint32_t (&ring)[kMainStages][kStageDwords], int h,
-                           int first_tile, int tile_stride, int ntiles, Epi&& epi) {
-  const int nblk = nblocks_of(T.U);
-  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
-  const int lane = threadIdx.x & 63;
-  const int col = lane & 15;
-  const int G = lane >> 4;
-  const int nsteps = max(0, ntiles) * nblk;   // (tile, block) steps
+// the chunk table T: run(epi) calls epi(tile, acc) for each, where acc[8X + e]
+// holds, for lane (G, col), query G's limb sums of key 8X + e of the lane's
+// column (see the epilogues).  Plane words stream through the LDS ring by
+// DMA, kMainStages - 1 (tile, block) steps ahead; prologue() issues the first
+// of those loads and needs only T.U and T.rowoff, so the caller may still be
+// building the rest of T.  All waves of the workgroup make the same calls
+// (run contains barriers).
+struct TileScanner {
+  const ScanArgs& a;
+  const ChunkTable& T;
+  uint32_t (*ring)[kStageDwords];
+  int first_tile, tile_stride, ntiles;
+  int nblk, wave, lane, col, G, nsteps;
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t dma_lane_off, ring_lane, a_lane;
+  int it_tile, it_b = 0, it_slot = 0, issued = 0;   // next step to load (uniform)
 
-  // Loads.  DMA load q = 2 wave + j (j = 0, 1) of a stage, lane l: row
-  // l >> 3 holds plane q + 8 (l >> 3) of the block, bytes 16 (l & 7) .. + 15
-  // of the tile's 128.  (The eight planes a transpose read gathers then sit
-  // in eight different loads, whose padding spreads them over the banks.)
-  // The buffer's size bounds the reads: words past the head's last plane row
-  // read as zero (past a row's end they read the next row; such keys are
-  // masked out).
-  const char* head = reinterpret_cast<const char*>(a.planes + int64_t(h) * kD * kPlanes * a.ldw);
-  const int64_t head_bytes = int64_t(kD) * kPlanes * a.ldw * 4;
-  const uint32_t nrec = head_bytes > int64_t(0xffffffff) ? 0xffffffffu : static_cast<uint32_t>(head_bytes);
-  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<char*>(head), static_cast<short>(0), static_cast<int>(nrec), 0x00020000);
-  const uint32_t dma_lane_off = 16u * static_cast<uint32_t>(lane & 7);
-  int it_tile = first_tile, it_b = 0, it_slot = 0, issued = 0;   // next step to load (uniform)
-  auto issue = [&]() {
+  __device__ TileScanner(const ScanArgs& a_, const ChunkTable& T_, uint32_t (&ring_)[kMainStages][kStageDwords], int h,
+                         int first_tile_, int tile_stride_, int ntiles_)
+      : a(a_), T(T_), ring(ring_), first_tile(first_tile_), tile_stride(tile_stride_), ntiles(ntiles_) {
+    nblk = nblocks_of(T.U);
+    wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+    lane = threadIdx.x & 63;
+    col = lane & 15;
+    G = lane >> 4;
+    nsteps = max(0, ntiles) * nblk;   // (tile, block) steps
+    it_tile = first_tile;
+    // Loads.  DMA load q = 2 wave + j (j = 0, 1) of a stage, lane l: row
+    // l >> 3 holds plane q + 8 (l >> 3) of the block, bytes 16 (l & 7) .. + 15
+    // of the tile's 128.  (The eight planes a transpose read gathers then sit
+    // in eight different loads, whose padding spreads them over the banks.)
+    // The buffer's size bounds the reads: words past the head's last plane
+    // row read as zero (past a row's end they read the next row; such keys
+    // are masked out).
+    const char* head = reinterpret_cast<const char*>(a.planes + int64_t(h) * kD * kPlanes * a.ldw);
+    const int64_t head_bytes = int64_t(kD) * kPlanes * a.ldw * 4;
+    const uint32_t nrec = head_bytes > int64_t(0xffffffff) ? 0xffffffffu : static_cast<uint32_t>(head_bytes);
+    rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(head), static_cast<short>(0),
+                                             static_cast<int>(nrec), 0x00020000);
+    dma_lane_off = 16u * static_cast<uint32_t>(lane & 7);
+    // transpose-read address of lane (G, col): plane 16G + col / 2 (row 2G
+    // of DMA load col / 2) of the wave's segment col & 1
+    ring_lane = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&ring[0][0])) +
+                static_cast<uint32_t>((col >> 1) * kDmaDwords + 2 * G * kTileWords + wave * kWaveWords) * 4u +
+                8u * static_cast<uint32_t>(col & 1);
+    a_lane = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&T.A[0][G][col]));
+  }
+
+  __device__ void issue() {
     if (issued < nsteps) {
       const uint32_t woff = static_cast<uint32_t>(it_tile * kTileWords) * 4u;
 #pragma unroll
@@ -766,40 +795,48 @@ __device__ void scan_tiles(const ScanArgs& a, const ChunkTable& T, uint32_t (&ri
       }
       it_slot = it_slot + 1 == kMainStages ? 0 : it_slot + 1;
     }
-  };
-  // transpose-read address of lane (G, col): plane 16G + col / 2 (row 2G of
-  // DMA load col / 2) of the wave's segment col & 1
-  const uint32_t ring_lane = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&ring[0][0])) +
-                             static_cast<uint32_t>((col >> 1) * kDmaDwords + 2 * G * kTileWords + wave * kWaveWords) * 4u +
-                             8u * static_cast<uint32_t>(col & 1);
-  const uint32_t a_lane = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&T.A[0][G][col]));
-#pragma unroll
-  for (int i = 0; i < kMainStages - 1; ++i) issue();
-
-  int step_i = 0, slot = 0;
-  for (int ti = 0, tile = first_tile; ti < ntiles; ++ti, tile += tile_stride) {
-    v4i acc[16];
-    auto step = [&](auto first, int b) {
-      // the last steps have fewer loads behind them: wait for all
-      if (step_i + kMainStages - 2 < nsteps) {
-        sync_stage<2 * (kMainStages - 2)>();
-      } else {
-        sync_stage<0>();
-      }
-      issue();   // into the slot every wave has finished reading
-      uint32_t x[8];
-      const uint32_t addr = ring_lane + static_cast<uint32_t>(slot * kStageDwords) * 4u;
-      const uint32_t a_addr = a_lane + static_cast<uint32_t>(b * 4 * 16 * 16);
-      v4i A;
-      read_stage(addr, a_addr, x, A);
-      ++step_i;
-      slot = slot + 1 == kMainStages ? 0 : slot + 1;
-      mfma_block<decltype(first)::value>(x, A, acc);
-    };
-    step(std::true_type{}, 0);   // nblk >= 1: an empty union is one block of zero weights
-    for (int b = 1; b < nblk; ++b) step(std::false_type{}, b);
-    epi(tile, acc);
   }
+
+  __device__ void prologue() {
+#pragma unroll
+    for (int i = 0; i < kMainStages - 1; ++i) issue();
+  }
+
+  template <class Epi>
+  __device__ void run(Epi&& epi) {
+    int step_i = 0, slot = 0;
+    for (int ti = 0, tile = first_tile; ti < ntiles; ++ti, tile += tile_stride) {
+      v4i acc[16];
+      auto step = [&](auto first, int b) {
+        // the last steps have fewer loads behind them: wait for all
+        if (step_i + kMainStages - 2 < nsteps) {
+          sync_stage<2 * (kMainStages - 2)>();
+        } else {
+          sync_stage<0>();
+        }
+        issue();   // into the slot every wave has finished reading
+        uint32_t x[8];
+        const uint32_t addr = ring_lane + static_cast<uint32_t>(slot * kStageDwords) * 4u;
+        const uint32_t a_addr = a_lane + static_cast<uint32_t>(b * 4 * 16 * 16);
+        v4i A;
+        read_stage(addr, a_addr, x, A);
+        ++step_i;
+        slot = slot + 1 == kMainStages ? 0 : slot + 1;
+        mfma_block<decltype(first)::value>(x, A, acc);
+      };
+      step(std::true_type{}, 0);   // nblk >= 1: an empty union is one block of zero weights
+      for (int b = 1; b < nblk; ++b) step(std::false_type{}, b);
+      epi(tile, acc);
+    }
+  }
+};
+
+template <class Epi>
+__device__ void scan_tiles(const ScanArgs& a, const ChunkTable& T, uint32_t (&ring)[kMainStages][kStageDwords], int h,
+                           int first_tile, int tile_stride, int ntiles, Epi&& epi) {
+  TileScanner sc(a, T, ring, h, first_tile, tile_stride, ntiles);
+  sc.prologue();
+  sc.run(static_cast<Epi&&>(epi));
 }
 
 // Exact limb sums t of the 16 keys of a lane's column (see scan_tiles): key
@@ -998,12 +1035,16 @@ __global__ __launch_bounds__(kMainThreads) void scan_sample_kernel(ScanArgs a) {
     ab = reinterpret_cast<const uint8_t*>(&s_alloc[0][0]);
   }
   build_union<GQ>(a, h, q0, ab, s);
-  write_chunk_table<GQ>(a, s, T, wsum, blockIdx.x == 0);
+  table_rows<GQ>(s, T);
+  __syncthreads();
   const int col = lane & 15;
   const int G = lane >> 4;
   const int sbi = blockIdx.x;
   const int tile = sbi * a.sample_stride;   // a sampled block is one tile
-  scan_tiles(a, T, ring, h, tile, 0, 1, [&](int tile_, const v4i (&acc)[16]) {
+  TileScanner sc(a, T, ring, h, tile, 0, 1);
+  sc.prologue();   // the block's plane words load while the limbs are built
+  table_limbs<GQ>(a, s, T, wsum, blockIdx.x == 0);
+  sc.run([&](int tile_, const v4i (&acc)[16]) {
     if (G >= GQ) return;
     int tv[16];
     limb_sums(acc, tv);
