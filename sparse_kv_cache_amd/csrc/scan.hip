@@ -225,23 +225,42 @@ __device__ inline double pow2_3_minus(int b) {
 }
 
 
-// Builds the union plane list of a query chunk (queries q0 .. q0+GQ-1 on
-// KV head h, allocation of query q0 + g at ab[g * kD ..]), the per-plane
-// weights and the score offsets C_q.
+// Per-channel inputs of build_union (thread t < kD holds channel t), loaded
+// ahead so their latency overlaps other work.
+struct UnionInputs {
+  float lo, st, q[4];
+};
+
+template <int GQ>
+__device__ inline UnionInputs load_union_inputs(const ScanArgs& a, int h, int q0) {
+  UnionInputs in{0.0f, 0.0f, {0.0f, 0.0f, 0.0f, 0.0f}};
+  const int t = threadIdx.x;
+  if (t < kD) {
+    in.lo = a.lo[h * kD + t];
+    in.st = a.step[h * kD + t];
+#pragma unroll
+    for (int g = 0; g < GQ; ++g) in.q[g] = a.q[int64_t(q0 + g) * kD + t];
+  }
+  return in;
+}
+
+// Builds the union plane list of a query chunk (queries q0 .. q0+GQ-1 on one
+// KV head, channel inputs in `in`, allocation of query q0 + g at
+// ab[g * kD ..]), the per-plane weights and the score offsets C_q.
 // Needs blockDim.x >= kD; ends with __syncthreads().
 template <int GQ>
-__device__ void build_union(const ScanArgs& a, int h, int q0, const uint8_t* ab, UnionLds<GQ>& s) {
+__device__ void build_union(const ScanArgs& a, const UnionInputs& in, const uint8_t* ab, UnionLds<GQ>& s) {
   const int t = threadIdx.x;
   int u = 0, bq[4] = {0, 0, 0, 0};
   float qv[4] = {0.0f, 0.0f, 0.0f, 0.0f}, st = 0.0f;
   if (t < kD) {
-    const float lo = a.lo[h * kD + t];
-    st = a.step[h * kD + t];
+    const float lo = in.lo;
+    st = in.st;
     double cp[GQ];
 #pragma unroll
     for (int g = 0; g < GQ; ++g) {
       bq[g] = min(static_cast<int>(ab[g * kD + t]), kPlanes);
-      qv[g] = a.q[int64_t(q0 + g) * kD + t];
+      qv[g] = in.q[g];
       u = max(u, bq[g]);
       cp[g] = static_cast<double>(qv[g]) *
               (static_cast<double>(lo) + static_cast<double>(st) * pow2_3_minus(bq[g]));
@@ -1023,6 +1042,7 @@ __global__ __launch_bounds__(kMainThreads) void scan_sample_kernel(ScanArgs a) {
   const int q0 = h * a.group + a.qoff + (blockIdx.y % a.cph) * kQueryChunk;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int lane = threadIdx.x & 63;
+  const UnionInputs in = load_union_inputs<GQ>(a, h, q0);   // in flight during the allocation
   const uint8_t* ab = a.alloc + int64_t(q0) * kD;
   if (a.var) {   // uniform
     if (wave < GQ) {
@@ -1034,7 +1054,7 @@ __global__ __launch_bounds__(kMainThreads) void scan_sample_kernel(ScanArgs a) {
     __syncthreads();
     ab = reinterpret_cast<const uint8_t*>(&s_alloc[0][0]);
   }
-  build_union<GQ>(a, h, q0, ab, s);
+  build_union<GQ>(a, in, ab, s);
   table_rows<GQ>(s, T);
   __syncthreads();
   const int col = lane & 15;

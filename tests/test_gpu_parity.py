@@ -161,6 +161,8 @@ def test_single_head_long(budget):
     (5017, 2, 6, 136, 257, 0),
     (4096, 3, 4, 300, 4096, 8),
     (70000, 1, 5, 92, 4000, 0),
+    (200000, 1, 4, 92, 1024, 0),
+    (300000, 2, 6, 136, 512, 4),
 ])
 def test_ragged_shapes(n, H, group, budget, k, pad):
     say("ragged", n, H, group, budget, k, pad)
