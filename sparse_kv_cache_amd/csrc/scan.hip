@@ -59,7 +59,7 @@ constexpr int kMaxBlocks = kMaxUnion / kBlockPlanes;
 constexpr int kPadPlanes = kBlockPlanes;
 constexpr int kMainThreads = 256;              // 4 wavefronts
 constexpr int kMainWaves = kMainThreads / 64;
-constexpr int kMainWgPerCu = 3;                // LDS budget: 3 resident workgroups per CU
+constexpr int kMainWgPerCu = 4;                // 4 resident workgroups per CU: <= 128 VGPRs, <= 40 KB of LDS
 constexpr int kWaveWords = 8;                  // 16 MFMA columns = 8 words x 2 halves
 constexpr int kTileWords = kMainWaves * kWaveWords;   // 32 words = 1024 keys
 // Workgroup LDS ring of plane words: a stage holds one K block of the
@@ -881,6 +881,12 @@ __device__ __forceinline__ void limb_sums(const v4i (&acc)[16], int (&tv)[16]) {
 __device__ __forceinline__ int64_t column_key(int tile, int wave, int col, int X) {
   return (int64_t(tile) * kTileWords + wave * kWaveWords) * 32 + (col >> 3) * 64 + 8 * (col & 7) + 128 * X;
 }
+
+// kMainWgPerCu workgroups share a CU's 160 KB of LDS (the small arrays fit
+// in the 512 bytes left over)
+static_assert(sizeof(ChunkTable) + sizeof(uint32_t) * kMainStages * kStageDwords + sizeof(uint2) * kMainWaves * 4 * kWaveCand +
+                      512 <= 160 * 1024 / kMainWgPerCu,
+              "main-kernel LDS fits kMainWgPerCu workgroups per CU");
 
 template <int GQ>
 __global__ __launch_bounds__(kMainThreads, kMainWgPerCu) void scan_main_kernel(ScanArgs a) {
