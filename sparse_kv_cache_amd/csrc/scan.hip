@@ -105,14 +105,10 @@ template <int GQ>
 struct UnionLds {
   float w[kMaxUnion + kPadPlanes][4];        // W_qcj per union plane; 0 where the query skips it
   uint32_t rowoff[kMaxUnion + kPadPlanes];   // byte offset of the plane row (c*4 + j) in the head
-  uint8_t mask[kMaxUnion + kPadPlanes];      // bit g: query g of the chunk reads the plane
   int off[kPlanes][kD];
   int u[kD];
   double cpart[2][GQ];
   float C[GQ];
-  float theta[GQ];
-  uint32_t tally[4];    // candidates of the current tile per query (main kernel)
-  uint32_t base[4];     // their first slot in the candidate list
   int U;
 };
 
@@ -275,10 +271,8 @@ __device__ void build_union(const ScanArgs& a, const UnionInputs& in, const uint
   }
   __syncthreads();
   // Union plane list in (plane j asc, channel c asc) order: plane j of
-  // channel c is present when j < u_c.  Listing one plane level across many
-  // channels makes the 8 bits of a LUT index come from 8 different channels,
-  // which keeps the index distribution (and so the LDS bank spread) close to
-  // uniform; the order is free because the score is a plain sum.
+  // channel c is present when j < u_c (any order would do: the score is a
+  // plain sum).
   // cnt[j] = #channels with u > j; exclusive prefix over channels per level.
   if (t < 64) {
     int base = 0;
@@ -297,24 +291,20 @@ __device__ void build_union(const ScanArgs& a, const UnionInputs& in, const uint
   if (t < kD) {
     for (int j = 0; j < u; ++j) {
       const int o = s.off[j][t];
-      uint32_t m = 0;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const bool on = g < GQ && j < bq[g];
-        m |= on ? (1u << g) : 0u;
         s.w[o][g] = on ? __fmul_rn(qv[g], st) * static_cast<float>(8 >> j) : 0.0f;
       }
       s.rowoff[o] = static_cast<uint32_t>((t * kPlanes + j) * a.ldw * 4);
-      s.mask[o] = static_cast<uint8_t>(m);
     }
   }
-  // padding up to whole groups of 4 LUT chunks: row 0, weight 0
+  // padding up to whole 64-plane blocks: row 0, weight 0
   const int U = s.U;
   const int pad = (kPadPlanes - U % kPadPlanes) % kPadPlanes;
   if (t < pad) {
     s.w[U + t][0] = s.w[U + t][1] = s.w[U + t][2] = s.w[U + t][3] = 0.0f;
     s.rowoff[U + t] = 0u;
-    s.mask[U + t] = 0u;
   }
   __syncthreads();
 }
