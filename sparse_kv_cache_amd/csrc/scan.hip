@@ -973,20 +973,39 @@ __global__ __launch_bounds__(kMainThreads, kMainWgPerCu) void scan_main_kernel(S
       }
     }
     if (bits != 0) {
-      uint32_t slot_c = slot0;
-      // static key index: a computed index into tv would move it to scratch
+      // Lanes pass few keys: walk the set bits only.  The key's t is picked
+      // from the registers by a select tree on the bits of its index (a
+      // computed index into tv would move it to scratch).
+      const float sig = T.sigma[G], cq = T.C[G];
+      int tn[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        if (bits & (1u << i)) {
-          const uint2 e = make_uint2(__float_as_uint(score_of(i)), static_cast<uint32_t>(key_of(i)));
-          if (slot_c < cap) {
-            cbuf[wave][G][slot_c] = e;
-          } else {
-            if (gpos < static_cast<uint32_t>(kCandCap)) a.cand[int64_t(q0 + G) * kCandCap + gpos] = e;
-            ++gpos;
-          }
-          ++slot_c;
+      for (int i = 0; i < 16; ++i) tn[i] = t_of(i);
+      uint32_t slot_c = slot0;
+      uint32_t rem = bits;
+      while (rem != 0u) {
+        const int i = __ffs(static_cast<int>(rem)) - 1;
+        rem &= rem - 1u;
+        // (bit masks rather than selects, which the compiler would turn
+        // back into an indexed array)
+        const int m0 = -(i & 1), m1 = -((i >> 1) & 1), m2 = -((i >> 2) & 1), m3 = -((i >> 3) & 1);
+        int t8[8], t4[4], t2[2];
+#pragma unroll
+        for (int m = 0; m < 8; ++m) t8[m] = tn[2 * m] ^ ((tn[2 * m] ^ tn[2 * m + 1]) & m0);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) t4[m] = t8[2 * m] ^ ((t8[2 * m] ^ t8[2 * m + 1]) & m1);
+#pragma unroll
+        for (int m = 0; m < 2; ++m) t2[m] = t4[2 * m] ^ ((t4[2 * m] ^ t4[2 * m + 1]) & m2);
+        const int t = t2[0] ^ ((t2[0] ^ t2[1]) & m3);
+        const float sc = fmaf(static_cast<float>(t), sig, cq);
+        const uint32_t key = static_cast<uint32_t>(((i & 8) ? key1 : key0) + (i & 7));
+        const uint2 e = make_uint2(__float_as_uint(sc), key);
+        if (slot_c < cap) {
+          cbuf[wave][G][slot_c] = e;
+        } else {
+          if (gpos < static_cast<uint32_t>(kCandCap)) a.cand[int64_t(q0 + G) * kCandCap + gpos] = e;
+          ++gpos;
         }
+        ++slot_c;
       }
     }
   });
