@@ -866,6 +866,13 @@ __device__ __forceinline__ void limb_sums(const v4i (&acc)[16], int (&tv)[16]) {
   }
 }
 
+// b where the lane's bit of mask is set, else a (v_cndmask with a lane mask).
+__device__ __forceinline__ int lane_select(int a, int b, uint64_t mask) {
+  int r;
+  asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "s"(mask));
+  return r;
+}
+
 // First key of the 8 keys 8X .. 8X + 7 of lane (G, col)'s column in a tile
 // (the wave's segments are 64 keys; X picks the second pair of segments).
 __device__ __forceinline__ int64_t column_key(int tile, int wave, int col, int X) {
@@ -985,17 +992,18 @@ __global__ __launch_bounds__(kMainThreads, kMainWgPerCu) void scan_main_kernel(S
       while (rem != 0u) {
         const int i = __ffs(static_cast<int>(rem)) - 1;
         rem &= rem - 1u;
-        // (bit masks rather than selects, which the compiler would turn
-        // back into an indexed array)
-        const int m0 = -(i & 1), m1 = -((i >> 1) & 1), m2 = -((i >> 2) & 1), m3 = -((i >> 3) & 1);
+        // (lane-mask selects written out: as plain selects the compiler
+        // would turn them back into an indexed array)
+        const uint64_t m0 = __ballot((i & 1) != 0), m1 = __ballot((i & 2) != 0);
+        const uint64_t m2 = __ballot((i & 4) != 0), m3 = __ballot((i & 8) != 0);
         int t8[8], t4[4], t2[2];
 #pragma unroll
-        for (int m = 0; m < 8; ++m) t8[m] = tn[2 * m] ^ ((tn[2 * m] ^ tn[2 * m + 1]) & m0);
+        for (int m = 0; m < 8; ++m) t8[m] = lane_select(tn[2 * m], tn[2 * m + 1], m0);
 #pragma unroll
-        for (int m = 0; m < 4; ++m) t4[m] = t8[2 * m] ^ ((t8[2 * m] ^ t8[2 * m + 1]) & m1);
+        for (int m = 0; m < 4; ++m) t4[m] = lane_select(t8[2 * m], t8[2 * m + 1], m1);
 #pragma unroll
-        for (int m = 0; m < 2; ++m) t2[m] = t4[2 * m] ^ ((t4[2 * m] ^ t4[2 * m + 1]) & m2);
-        const int t = t2[0] ^ ((t2[0] ^ t2[1]) & m3);
+        for (int m = 0; m < 2; ++m) t2[m] = lane_select(t4[2 * m], t4[2 * m + 1], m2);
+        const int t = lane_select(t2[0], t2[1], m3);
         const float sc = fmaf(static_cast<float>(t), sig, cq);
         const uint32_t key = static_cast<uint32_t>(((i & 8) ? key1 : key0) + (i & 7));
         const uint2 e = make_uint2(__float_as_uint(sc), key);
