@@ -13,7 +13,7 @@
 // the B-th largest ordering key bits(w_c) - j 2^24, channel c takes every
 // plane whose key exceeds theta, and the candidates equal to theta (at most
 // one per channel) are filled in ascending channel order until sum b_c = B.
-// theta is found by bisection on the int32 key with wavefront ballot counts.
+// theta is found by a search on the int32 key with wavefront counts.
 #ifndef FATHOM_ALLOCATE_WAVE_H
 #define FATHOM_ALLOCATE_WAVE_H
 
@@ -25,6 +25,18 @@ namespace alloc_detail {
 constexpr int kKeyStep = 1 << 24;
 
 __device__ inline int wave_count(bool pred) { return __popcll(__ballot(pred)); }
+
+// Sum over the wavefront's 64 lanes, returned to every lane (DPP row shifts
+// give each row's inclusive prefix, row broadcasts carry it across rows).
+__device__ inline uint32_t wave_sum_u32(uint32_t v) {
+  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x111, 0xf, 0xf, false));
+  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x112, 0xf, 0xf, false));
+  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x114, 0xf, 0xf, false));
+  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x118, 0xf, 0xf, false));
+  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x142, 0xa, 0xf, false));
+  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x143, 0xc, 0xf, false));
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
+}
 
 __device__ inline int lanes_below(uint64_t mask) {
   const int lane = threadIdx.x & 63;
@@ -48,27 +60,46 @@ __device__ inline uint2 allocate_query_wave(const float* __restrict__ q_row, con
   const float w1 = __fmul_rn(__fmul_rn(qv.y, qv.y), vv.y);
   const int k0 = __float_as_int(w0);       // w >= 0, so the bit pattern orders like the value
   const int k1 = __float_as_int(w1);
-  // count of candidates with key >= t
-  auto count_ge = [&](long long t) {
-    int cnt = 0;
-#pragma unroll
-    for (int j = 0; j < kPlanes; ++j) {
-      cnt += wave_count(static_cast<long long>(k0) - j * kKeyStep >= t);
-      cnt += wave_count(static_cast<long long>(k1) - j * kKeyStep >= t);
-    }
-    return cnt;
-  };
+  // The search runs on u = key - kKeyLo, which is >= 0 for every candidate
+  // key and below 2^32, so all of it is 32-bit unsigned arithmetic.
+  // Candidates of channel c with u >= t: the keys k_c - j 2^24 (j = 0..3)
+  // are evenly spaced, so that is min(4, (u_c - t) / 2^24 + 1) when u_c >= t.
+  constexpr uint32_t kKeyLo = static_cast<uint32_t>(-3 * kKeyStep);   // -3 2^24 as a bit pattern
+  const uint32_t u0 = static_cast<uint32_t>(k0) - kKeyLo, u1 = static_cast<uint32_t>(k1) - kKeyLo;
+  auto cnt1 = [](uint32_t u, uint32_t t) -> uint32_t { return u >= t ? min(4u, ((u - t) >> 24) + 1u) : 0u; };
   int b0 = 0, b1 = 0;
   if (budget >= kPlanes * kD) {
     b0 = b1 = kPlanes;
   } else if (budget > 0) {
-    long long lo = -3ll * kKeyStep;        // count_ge(lo) = 4d >= budget
-    long long hi = 0x7f800001ll;           // above every finite key: count_ge(hi) = 0
-    while (hi - lo > 1) {
-      const long long mid = lo + (hi - lo) / 2;
-      if (count_ge(mid) >= budget) lo = mid; else hi = mid;
+    // Search for the budget-th largest key with three probes per round:
+    // their counts (each <= 4d = 512 < 2^10) are packed into one word, so one
+    // wavefront sum serves all three.  Invariant: count(lo) >= budget >
+    // count(hi).
+    uint32_t lo = 0u;                                      // key -3 2^24: count = 4d >= budget
+    uint32_t hi = 0x7f800001u - kKeyLo;                    // above every finite key: count = 0
+    const uint32_t B = static_cast<uint32_t>(budget);
+    while (hi - lo > 1u) {
+      const uint32_t step = max(1u, (hi - lo) / 4u);
+      const uint32_t t1 = min(lo + step, hi - 1u);
+      const uint32_t t2 = min(t1 + step, hi - 1u);
+      const uint32_t t3 = min(t2 + step, hi - 1u);
+      uint32_t packed = (cnt1(u0, t1) + cnt1(u1, t1)) | ((cnt1(u0, t2) + cnt1(u1, t2)) << 10) |
+                        ((cnt1(u0, t3) + cnt1(u1, t3)) << 20);
+      packed = wave_sum_u32(packed);
+      const uint32_t c1 = packed & 1023u, c2 = (packed >> 10) & 1023u, c3 = packed >> 20;
+      if (c3 >= B) {
+        lo = t3;
+      } else if (c2 >= B) {
+        lo = t2;
+        hi = t3;
+      } else if (c1 >= B) {
+        lo = t1;
+        hi = t2;
+      } else {
+        hi = t1;
+      }
     }
-    const long long theta = lo;            // the budget-th largest key
+    const long long theta = static_cast<long long>(static_cast<int>(lo + kKeyLo));   // the budget-th largest key
     int gt0 = 0, gt1 = 0;
     bool tie0 = false, tie1 = false;
 #pragma unroll
