@@ -71,6 +71,7 @@ constexpr int kMainStages = 3;
 constexpr int kDmaDwords = 8 * kTileWords + 8;           // one DMA load (8 planes x 32 words) + bank padding
 constexpr int kStageDwords = 8 * kDmaDwords;
 constexpr int kWaveCand = 32;                  // candidates per (wave, query) buffered in LDS
+constexpr int kTopR = 64;                      // largest sample rank served by per-block lane maxima
 constexpr int kSelectThreads = 1024;
 constexpr int kSelectWaves = kSelectThreads / 64;
 
@@ -97,6 +98,8 @@ struct ScanArgs {
   uint2* cand;
   float* all_scores;
   int sample_stride;  // distance between sampled blocks, in 1024-key blocks
+  int rsel;           // sample rank of the threshold
+  int top_lists;      // rsel <= kTopR: sampled blocks store their lane maxima only
   int chunks_per_head;
   void* tables;       // [H * chunks_per_head] ChunkTable, written by the sample kernel
 };
@@ -150,7 +153,9 @@ __device__ inline int lanes_below(uint64_t mask) {
 // row_bcast:15 / row_bcast:31 (rows are 16 lanes).
 constexpr int kDppXor1 = 0xB1;          // quad_perm [1,0,3,2]
 constexpr int kDppXor2 = 0x4E;          // quad_perm [2,3,0,1]
-constexpr int kDppRowShr = 0x110;       // + n: row_shr:n
+constexpr int kDppRowShl = 0x100;       // + n: row_shl:n (lane reads lane + n of its row)
+constexpr int kDppRowShr = 0x110;       // + n: row_shr:n (lane reads lane - n of its row)
+constexpr int kDppRowRor = 0x120;       // + n: row_ror:n
 constexpr int kDppRowMirror = 0x140;
 constexpr int kDppRowHalfMirror = 0x141;
 constexpr int kDppRowBcast15 = 0x142;
@@ -608,6 +613,148 @@ __global__ __launch_bounds__(kSelectThreads) void scan_threshold_kernel(
     th = prefix;   // lowest value of the bucket: the low bits are zero
   }
   if (tid == 0) {
+    theta[q] = ordered_to_float(th);
+    count[q] = 0u;
+  }
+}
+
+// ------------------------------------------------ per-block lane maxima
+// For rsel <= kTopR the sample kernel stores, per sampled block and query,
+// only the maxima of the 64 groups of 16 keys that one lane scores (as
+// ordered keys, in the block's slot of kTopR words at the front of the
+// query's sample row).  The rsel-th largest of these maxima never exceeds
+// the rsel-th largest sampled score and, while the best rsel scores fall in
+// distinct groups, equals it; the threshold then selects from at most
+// kSampleMaxBlocks * 64 values instead of the whole sample.
+static_assert(kTopR == kMainWaves * 16, "a block's list holds one maximum per (wavefront, column)");
+
+// v of lane (lane ^ J): DPP for J < 16, lane shuffle otherwise.
+template <int J>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
+  if constexpr (J == 1) {
+    return dpp_u32<kDppXor1>(v, v);
+  } else if constexpr (J == 2) {
+    return dpp_u32<kDppXor2>(v, v);
+  } else if constexpr (J == 4) {
+    const uint32_t up = dpp_u32<kDppRowShl + 4>(v, v);   // lane + 4 (used where bit 2 is clear)
+    const uint32_t dn = dpp_u32<kDppRowShr + 4>(v, v);   // lane - 4 (used where it is set)
+    return (threadIdx.x & 4) ? dn : up;
+  } else if constexpr (J == 8) {
+    return dpp_u32<kDppRowRor + 8>(v, v);               // rotation by half a row
+  } else {
+    return static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), J, 64));
+  }
+}
+
+// One compare-exchange step of a bitonic network: merge size K, distance J.
+template <int K, int J>
+__device__ __forceinline__ uint32_t bitonic_step(uint32_t v) {
+  const uint32_t p = xor_lane<J>(v);
+  const int lane = threadIdx.x & 63;
+  const bool keep_max = ((lane & J) == 0) == ((lane & K) == 0);
+  return keep_max ? max(v, p) : min(v, p);
+}
+
+// The wavefront's 64 values (one per lane) in descending order across the lanes.
+__device__ inline uint32_t wave_sort_desc(uint32_t v) {
+  v = bitonic_step<2, 1>(v);
+  v = bitonic_step<4, 2>(v);
+  v = bitonic_step<4, 1>(v);
+  v = bitonic_step<8, 4>(v);
+  v = bitonic_step<8, 2>(v);
+  v = bitonic_step<8, 1>(v);
+  v = bitonic_step<16, 8>(v);
+  v = bitonic_step<16, 4>(v);
+  v = bitonic_step<16, 2>(v);
+  v = bitonic_step<16, 1>(v);
+  v = bitonic_step<32, 16>(v);
+  v = bitonic_step<32, 8>(v);
+  v = bitonic_step<32, 4>(v);
+  v = bitonic_step<32, 2>(v);
+  v = bitonic_step<32, 1>(v);
+  v = bitonic_step<64, 32>(v);
+  v = bitonic_step<64, 16>(v);
+  v = bitonic_step<64, 8>(v);
+  v = bitonic_step<64, 4>(v);
+  v = bitonic_step<64, 2>(v);
+  v = bitonic_step<64, 1>(v);
+  return v;
+}
+
+// r-th largest (1 <= r <= number of values) of the ordered keys v[m] of the
+// wavefront's lanes: bisection on the key with three probes per round, whose
+// counts (each < 2^10, so 64 M < 1024) share one packed wavefront sum.
+template <int M>
+__device__ uint32_t wave_rth_search(const uint32_t (&v)[M], uint32_t r) {
+  static_assert(64 * M < 1024, "counts fit 10-bit fields");
+  auto cnt = [&](uint32_t t) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int m = 0; m < M; ++m) c += v[m] >= t ? 1u : 0u;
+    return c;
+  };
+  // invariant: count(>= lo) >= r > count(>= hi); no ordered score is 2^32 - 1
+  uint32_t lo = 0u, hi = 0xffffffffu;
+  while (hi - lo > 1u) {
+    const uint32_t step = max(1u, (hi - lo) / 4u);
+    const uint32_t t1 = min(lo + step, hi - 1u);
+    const uint32_t t2 = min(t1 + step, hi - 1u);
+    const uint32_t t3 = min(t2 + step, hi - 1u);
+    uint32_t packed = cnt(t1) | (cnt(t2) << 10) | (cnt(t3) << 20);
+    packed = read_lane(wave_incl_sum(packed), 63);
+    if ((packed >> 20) >= r) {
+      lo = t3;
+    } else if (((packed >> 10) & 1023u) >= r) {
+      lo = t2;
+      hi = t3;
+    } else if ((packed & 1023u) >= r) {
+      lo = t1;
+      hi = t2;
+    } else {
+      hi = t1;
+    }
+  }
+  return lo;
+}
+
+// Per query (one wavefront): theta = the rsel-th largest of the sampled
+// blocks' lane maxima.  The rsel-th largest per-lane maximum L has at least
+// rsel values at or above it; when at most 64 do, they are compacted one
+// per lane and sorted, otherwise a search finds the rank directly.
+__global__ __launch_bounds__(64) void scan_threshold_lists_kernel(const float* __restrict__ sample, int nsb,
+                                                                  uint32_t rsel, float* __restrict__ theta,
+                                                                  uint32_t* __restrict__ count) {
+  __shared__ uint32_t scratch[64];
+  const int q = blockIdx.x;
+  const int lane = threadIdx.x;
+  const uint32_t* row = reinterpret_cast<const uint32_t*>(sample) + int64_t(q) * kSampleMaxKeys;
+  uint32_t v[kSampleMaxBlocks];
+  // absent lists read as 0, below every ordered score
+#pragma unroll
+  for (int m = 0; m < kSampleMaxBlocks; ++m) v[m] = m < nsb ? row[m * kTopR + lane] : 0u;
+  uint32_t mx = 0u;
+#pragma unroll
+  for (int m = 0; m < kSampleMaxBlocks; ++m) mx = max(mx, v[m]);
+  const uint32_t L = read_lane(wave_sort_desc(mx), static_cast<int>(rsel) - 1);
+  uint32_t c = 0;
+#pragma unroll
+  for (int m = 0; m < kSampleMaxBlocks; ++m) c += static_cast<uint32_t>(__popcll(__ballot(v[m] >= L)));
+  uint32_t th;
+  if (c <= 64u) {   // uniform
+    uint32_t base = 0;
+#pragma unroll
+    for (int m = 0; m < kSampleMaxBlocks; ++m) {
+      const bool in = v[m] >= L;
+      const uint64_t bal = __ballot(in);
+      if (in) scratch[base + lanes_below(bal)] = v[m];
+      base += static_cast<uint32_t>(__popcll(bal));
+    }
+    __syncthreads();
+    th = read_lane(wave_sort_desc(static_cast<uint32_t>(lane) < c ? scratch[lane] : 0u), static_cast<int>(rsel) - 1);
+  } else {
+    th = wave_rth_search<kSampleMaxBlocks>(v, rsel);
+  }
+  if (lane == 0) {
     theta[q] = ordered_to_float(th);
     count[q] = 0u;
   }
@@ -1092,14 +1239,19 @@ __global__ __launch_bounds__(kMainThreads) void scan_sample_kernel(ScanArgs a) {
     int tv[16];
     limb_sums(acc, tv);
     const float sigma = T.sigma[G], Cq = T.C[G];
+    uint32_t mx = 0u;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int64_t key = column_key(tile_, wave, col, i >> 3) + (i & 7);
       const int t = (i & 7) == 7 ? -tv[i] : tv[i];
       const float sc = fmaf(static_cast<float>(t), sigma, Cq);
       const int local = static_cast<int>(key - int64_t(tile_) * kTileWords * 32);
-      a.sample[int64_t(q0 + G) * kSampleMaxKeys + sbi * kSampleBlockKeys + local] = key < a.n ? sc : -INFINITY;
+      const float score = key < a.n ? sc : -INFINITY;
+      mx = max(mx, float_to_ordered(score));
+      if (!a.top_lists) a.sample[int64_t(q0 + G) * kSampleMaxKeys + sbi * kSampleBlockKeys + local] = score;
     }
+    if (a.top_lists)
+      reinterpret_cast<uint32_t*>(a.sample)[int64_t(q0 + G) * kSampleMaxKeys + sbi * kTopR + wave * 16 + col] = mx;
   });
 }
 
@@ -1240,10 +1392,11 @@ __global__ __launch_bounds__(kSelectThreads) void scan_merge_kernel(ScanArgs a, 
     const uint2* cand = a.cand + int64_t(q) * kCandCap;
     static_assert(PT * kSelectThreads == kCandCap, "one register per candidate slot");
     uint32_t v[PT], id[PT];
-    // unconditional loads (the list is allocated to its capacity), masked after
+    // only the cnt filled slots are read (cnt is known before any load issues)
 #pragma unroll
     for (int j = 0; j < PT; ++j) {
-      const uint2 e = cand[tid + j * kSelectThreads];
+      uint2 e = make_uint2(0u, 0u);
+      if (tid + j * kSelectThreads < static_cast<int>(cnt)) e = cand[tid + j * kSelectThreads];
       v[j] = e.x;
       id[j] = e.y;
     }
@@ -1462,6 +1615,8 @@ hipError_t launch_scan_topk(const uint32_t* planes, const float* lo, const float
   const int64_t rmin = svalid < 16 ? svalid : 16;
   if (rsel < rmin) rsel = rmin;
   if (rsel > svalid) rsel = svalid;
+  a.rsel = static_cast<int>(rsel);
+  a.top_lists = rsel <= kTopR ? 1 : 0;
 
   // main-kernel work split: kMainWgPerCu resident workgroups per CU, each
   // taking a contiguous run of tiles of one (head, query chunk)
@@ -1491,7 +1646,10 @@ hipError_t launch_scan_topk(const uint32_t* planes, const float* lo, const float
       b.qoff = full * kQueryChunk;
       launch_class(rest, b, H, nsb, sample_phase, full > 0 ? nullptr : ev_start, ev_stop, stream);
     }
-    if (sample_phase) {
+    if (sample_phase && a.top_lists) {
+      hipLaunchKernelGGL(scan_threshold_lists_kernel, dim3(num_q), dim3(64), 0, stream, ws.sample, nsb,
+                         static_cast<uint32_t>(rsel), ws.theta, ws.count);
+    } else if (sample_phase) {
       hipLaunchKernelGGL(scan_threshold_kernel, dim3(num_q), dim3(kSelectThreads), 0, stream, ws.sample,
                          nsb * kSampleBlockKeys, static_cast<uint32_t>(rsel), ws.theta, ws.count);
     }
