@@ -116,6 +116,7 @@ struct UnionLds {
 };
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef unsigned int v2u32 __attribute__((ext_vector_type(2)));
 
 // What the main kernel needs of a (KV head, query chunk): the union rows, the
 // MFMA A operands (int8 limbs of the fixed-point plane weights), the scales
@@ -423,13 +424,14 @@ __device__ inline uint32_t present_below(uint32_t count) {
 
 // Block-wide max, min and number of the present values (ordered keys;
 // value j of a thread is present when bit j of pm is set).
+// Slots j >= nj (uniform per wavefront) hold nothing and are skipped.
 template <int PT>
-__device__ uint3 block_max_min(const uint32_t (&v)[PT], uint32_t pm, SelectLds& L) {
+__device__ uint3 block_max_min(const uint32_t (&v)[PT], uint32_t pm, SelectLds& L, int nj = PT) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint32_t mx = 0u, mn = 0xffffffffu;
 #pragma unroll
   for (int j = 0; j < PT; ++j) {
-    if ((pm >> j) & 1u) {
+    if (j < nj && ((pm >> j) & 1u)) {
       mx = max(mx, v[j]);
       mn = min(mn, v[j]);
     }
@@ -1384,22 +1386,42 @@ __global__ __launch_bounds__(kSelectThreads) void scan_merge_kernel(ScanArgs a, 
   const int q = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
+  static_assert(PT * kSelectThreads == kCandCap, "one register per candidate slot");
+  // The first kSpecSlots slots of the list load at once, before the count
+  // arrives (the list is allocated to its capacity; slots past the count
+  // are masked later), so the two memory round trips overlap.  Slots beyond
+  // them are bounded by the count: a lane past it reads 0 without a memory
+  // access, so those loads issue unconditionally too (a load under a branch
+  // would wait for its data inside the branch).
+  constexpr int kSpecSlots = 6;
+  uint32_t v[PT], id[PT];
+  {
+    const __amdgpu_buffer_rsrc_t cand = __builtin_amdgcn_make_buffer_rsrc(
+        a.cand + int64_t(q) * kCandCap, static_cast<short>(0), kSpecSlots * kSelectThreads * 8, 0x00020000);
+#pragma unroll
+    for (int j = 0; j < kSpecSlots; ++j) {
+      const v2u32 e = __builtin_amdgcn_raw_buffer_load_b64(cand, (tid + j * kSelectThreads) * 8, 0, 0);
+      v[j] = e.x;
+      id[j] = e.y;
+    }
+  }
   const uint32_t cnt = a.count[q];
   unsigned kept = 0;
   bool fast = false;   // uniform
 
   if (cnt >= static_cast<uint32_t>(k) && cnt <= static_cast<uint32_t>(kCandCap)) {
-    const uint2* cand = a.cand + int64_t(q) * kCandCap;
-    static_assert(PT * kSelectThreads == kCandCap, "one register per candidate slot");
-    uint32_t v[PT], id[PT];
-    // only the cnt filled slots are read (cnt is known before any load issues)
+    const __amdgpu_buffer_rsrc_t cand = __builtin_amdgcn_make_buffer_rsrc(
+        a.cand + int64_t(q) * kCandCap, static_cast<short>(0), static_cast<int>(cnt * 8u), 0x00020000);
 #pragma unroll
-    for (int j = 0; j < PT; ++j) {
-      uint2 e = make_uint2(0u, 0u);
-      if (tid + j * kSelectThreads < static_cast<int>(cnt)) e = cand[tid + j * kSelectThreads];
-      v[j] = e.x;
+    for (int j = kSpecSlots; j < PT; ++j) {
+      const v2u32 e = __builtin_amdgcn_raw_buffer_load_b64(cand, (tid + j * kSelectThreads) * 8, 0, 0);
+      v[j] = float_to_ordered(__uint_as_float(e.x));
       id[j] = e.y;
     }
+    // slots j < nj of this wavefront hold candidates; the others are left
+    // out (their pm bit stays clear, and every later use tests pm)
+    const int wbase = __builtin_amdgcn_readfirstlane(tid & ~63);
+    const int nj = min(PT, max(0, (static_cast<int>(cnt) - wbase + kSelectThreads - 1) / kSelectThreads));
     // The scan's filter may also pass keys just below theta; only candidates
     // scoring >= theta count, and the list is complete for the top k exactly
     // when at least k of them do.
@@ -1407,13 +1429,15 @@ __global__ __launch_bounds__(kSelectThreads) void scan_merge_kernel(ScanArgs a, 
     uint32_t pm = 0;
 #pragma unroll
     for (int j = 0; j < PT; ++j) {
-      const uint32_t i = tid + j * kSelectThreads;
-      v[j] = i < cnt ? float_to_ordered(__uint_as_float(v[j])) : 0u;
-      pm |= (i < cnt && v[j] >= theta_o) ? (1u << j) : 0u;
+      if (j < nj) {   // uniform
+        const uint32_t i = tid + j * kSelectThreads;
+        v[j] = i < cnt ? (j < kSpecSlots ? float_to_ordered(__uint_as_float(v[j])) : v[j]) : 0u;
+        pm |= (i < cnt && v[j] >= theta_o) ? (1u << j) : 0u;
+      }
     }
     DigitLds& D = *reinterpret_cast<DigitLds*>(keys + kFastKept);
     digit_clear(D);
-    const uint3 mm = block_max_min<PT>(v, pm, L);
+    const uint3 mm = block_max_min<PT>(v, pm, L, nj);
     if (mm.z >= static_cast<uint32_t>(k)) {
       fast = true;
       // Fast path: one digit pass puts the candidates into ordered buckets;
@@ -1426,7 +1450,8 @@ __global__ __launch_bounds__(kSelectThreads) void scan_merge_kernel(ScanArgs a, 
         const int width = min(kDigitBits, hi), shift = hi - width;
         const uint32_t dmask = (1u << width) - 1u;
 #pragma unroll
-        for (int j = 0; j < PT; ++j) hist_add(D.hist, (pm >> j) & 1u, (v[j] >> shift) & dmask);
+        for (int j = 0; j < PT; ++j)
+          if (j < nj) hist_add(D.hist, (pm >> j) & 1u, (v[j] >> shift) & dmask);
         __syncthreads();
         digit_scan(D, static_cast<uint32_t>(k) - 1u);
         if (D.big == 0u) {
@@ -1435,15 +1460,22 @@ __global__ __launch_bounds__(kSelectThreads) void scan_merge_kernel(ScanArgs a, 
 #pragma unroll
           for (int j = 0; j < PT; ++j) {
             const uint32_t d = (v[j] >> shift) & dmask;
-            if (((pm >> j) & 1u) && d >= bstar) keys[D.start[d] + atomicAdd(&D.cursor[d], 1u)] = sort_key(v[j], id[j]);
+            if (j < nj && ((pm >> j) & 1u) && d >= bstar)
+              keys[D.start[d] + atomicAdd(&D.cursor[d], 1u)] = sort_key(v[j], id[j]);
           }
           __syncthreads();
           for (uint32_t p = tid; p < nkeep; p += kSelectThreads) {
             const unsigned long long key = keys[p];
             const uint32_t d = (static_cast<uint32_t>(key >> 32) >> shift) & dmask;
             const uint32_t b0 = D.start[d], c = D.hist[d];
-            uint32_t rank = 0;
-            for (uint32_t i = 0; i < c; ++i) rank += keys[b0 + i] > key ? 1u : 0u;
+            // (four independent reads per round keep several LDS reads in flight)
+            uint32_t rank = 0, i = 0;
+            for (; i + 4 <= c; i += 4) {
+              const unsigned long long k0 = keys[b0 + i], k1 = keys[b0 + i + 1];
+              const unsigned long long k2 = keys[b0 + i + 2], k3 = keys[b0 + i + 3];
+              rank += (k0 > key ? 1u : 0u) + (k1 > key ? 1u : 0u) + (k2 > key ? 1u : 0u) + (k3 > key ? 1u : 0u);
+            }
+            for (; i < c; ++i) rank += keys[b0 + i] > key ? 1u : 0u;
             const uint32_t pos = b0 + rank;
             if (pos < static_cast<uint32_t>(k)) {
               out_idx[int64_t(q) * k + pos] = static_cast<int32_t>(~static_cast<uint32_t>(key));
@@ -1476,6 +1508,10 @@ __global__ __launch_bounds__(kSelectThreads) void scan_merge_kernel(ScanArgs a, 
     }
   }
   if (!fast) {
+    // (the early loads are consumed on this path too, so the compiler keeps
+    // them ahead of the count test instead of sinking them into the fast path)
+#pragma unroll
+    for (int j = 0; j < kSpecSlots; ++j) asm volatile("" : : "v"(v[j]), "v"(id[j]));
     // exact fallback: radix select over recomputed scores
     const int h = q / a.group;
     const uint32_t* head_planes = a.planes + int64_t(h) * kD * kPlanes * a.ldw;
