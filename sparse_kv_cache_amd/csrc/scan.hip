@@ -99,7 +99,9 @@ struct ScanArgs {
   float* all_scores;
   int sample_stride;  // distance between sampled blocks, in 1024-key blocks
   int rsel;           // sample rank of the threshold
-  int top_lists;      // rsel <= kTopR: sampled blocks store their lane maxima only
+  int top_lists;      // rsel <= kTopR: sampled blocks store their lane maxima only,
+                      //   and the main kernel selects theta from them
+  int nsb;            // sampled blocks per head
   int chunks_per_head;
   void* tables;       // [H * chunks_per_head] ChunkTable, written by the sample kernel
 };
@@ -233,16 +235,16 @@ struct UnionInputs {
   float lo, st, q[4];
 };
 
+// Every thread loads (threads past kD re-read channel kD - 1 and ignore it):
+// loads under a branch would be waited for inside it.
 template <int GQ>
 __device__ inline UnionInputs load_union_inputs(const ScanArgs& a, int h, int q0) {
   UnionInputs in{0.0f, 0.0f, {0.0f, 0.0f, 0.0f, 0.0f}};
-  const int t = threadIdx.x;
-  if (t < kD) {
-    in.lo = a.lo[h * kD + t];
-    in.st = a.step[h * kD + t];
+  const int t = min(static_cast<int>(threadIdx.x), kD - 1);
+  in.lo = a.lo[h * kD + t];
+  in.st = a.step[h * kD + t];
 #pragma unroll
-    for (int g = 0; g < GQ; ++g) in.q[g] = a.q[int64_t(q0 + g) * kD + t];
-  }
+  for (int g = 0; g < GQ; ++g) in.q[g] = a.q[int64_t(q0 + g) * kD + t];
   return in;
 }
 
@@ -719,47 +721,32 @@ __device__ uint32_t wave_rth_search(const uint32_t (&v)[M], uint32_t r) {
   return lo;
 }
 
-// Per query (one wavefront): theta = the rsel-th largest of the sampled
-// blocks' lane maxima.  The rsel-th largest per-lane maximum L has at least
-// rsel values at or above it; when at most 64 do, they are compacted one
-// per lane and sorted, otherwise a search finds the rank directly.
-__global__ __launch_bounds__(64) void scan_threshold_lists_kernel(const float* __restrict__ sample, int nsb,
-                                                                  uint32_t rsel, float* __restrict__ theta,
-                                                                  uint32_t* __restrict__ count) {
-  __shared__ uint32_t scratch[64];
-  const int q = blockIdx.x;
-  const int lane = threadIdx.x;
-  const uint32_t* row = reinterpret_cast<const uint32_t*>(sample) + int64_t(q) * kSampleMaxKeys;
-  uint32_t v[kSampleMaxBlocks];
-  // absent lists read as 0, below every ordered score
-#pragma unroll
-  for (int m = 0; m < kSampleMaxBlocks; ++m) v[m] = m < nsb ? row[m * kTopR + lane] : 0u;
+// The r-th largest (1 <= r <= 64) of the wavefront's ordered keys v[m]
+// (m < M; 0 marks an absent key).  The r-th largest per-lane maximum L has
+// at least r keys at or above it; when at most 64 do, they are compacted one
+// per lane through `scratch` (64 words of LDS private to the wavefront) and
+// sorted, otherwise a search finds the rank directly.
+template <int M>
+__device__ uint32_t wave_rth_largest(const uint32_t (&v)[M], uint32_t r, uint32_t* scratch) {
+  const int lane = threadIdx.x & 63;
   uint32_t mx = 0u;
 #pragma unroll
-  for (int m = 0; m < kSampleMaxBlocks; ++m) mx = max(mx, v[m]);
-  const uint32_t L = read_lane(wave_sort_desc(mx), static_cast<int>(rsel) - 1);
+  for (int m = 0; m < M; ++m) mx = max(mx, v[m]);
+  const uint32_t L = read_lane(wave_sort_desc(mx), static_cast<int>(r) - 1);
   uint32_t c = 0;
 #pragma unroll
-  for (int m = 0; m < kSampleMaxBlocks; ++m) c += static_cast<uint32_t>(__popcll(__ballot(v[m] >= L)));
-  uint32_t th;
-  if (c <= 64u) {   // uniform
-    uint32_t base = 0;
+  for (int m = 0; m < M; ++m) c += static_cast<uint32_t>(__popcll(__ballot(v[m] >= L)));
+  if (c > 64u) return wave_rth_search<M>(v, r);   // uniform
+  uint32_t base = 0;
 #pragma unroll
-    for (int m = 0; m < kSampleMaxBlocks; ++m) {
-      const bool in = v[m] >= L;
-      const uint64_t bal = __ballot(in);
-      if (in) scratch[base + lanes_below(bal)] = v[m];
-      base += static_cast<uint32_t>(__popcll(bal));
-    }
-    __syncthreads();
-    th = read_lane(wave_sort_desc(static_cast<uint32_t>(lane) < c ? scratch[lane] : 0u), static_cast<int>(rsel) - 1);
-  } else {
-    th = wave_rth_search<kSampleMaxBlocks>(v, rsel);
+  for (int m = 0; m < M; ++m) {
+    const bool in = v[m] >= L;
+    const uint64_t bal = __ballot(in);
+    if (in) scratch[base + lanes_below(bal)] = v[m];
+    base += static_cast<uint32_t>(__popcll(bal));
   }
-  if (lane == 0) {
-    theta[q] = ordered_to_float(th);
-    count[q] = 0u;
-  }
+  __builtin_amdgcn_wave_barrier();
+  return read_lane(wave_sort_desc(static_cast<uint32_t>(lane) < c ? scratch[lane] : 0u), static_cast<int>(r) - 1);
 }
 
 // -------------------------------------------------------------------- main
@@ -1044,17 +1031,53 @@ __global__ __launch_bounds__(kMainThreads, kMainWgPerCu) void scan_main_kernel(S
   __shared__ float theta_s[4];
   const int h = blockIdx.y / a.cph;
   const int q0 = h * a.group + a.qoff + (blockIdx.y % a.cph) * kQueryChunk;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+  const int lane = threadIdx.x & 63;
+  // With per-block lists, wavefront g selects theta of query q0 + g itself
+  // (every workgroup of the chunk gets the same value): its lanes load entry
+  // `lane` of each sampled block's list together with the table.
+  uint32_t lv[kSampleMaxBlocks];
+  if (a.top_lists && wave < GQ) {   // uniform
+    const uint32_t* row = reinterpret_cast<const uint32_t*>(a.sample) + int64_t(q0 + wave) * kSampleMaxKeys;
+#pragma unroll
+    for (int m = 0; m < kSampleMaxBlocks; ++m) lv[m] = m < a.nsb ? row[m * kTopR + lane] : 0u;
+  }
   {
+    // (read unconditionally, with the table, and used only without lists)
+    const float theta_in = a.theta[q0 + min(static_cast<int>(threadIdx.x) & 3, GQ - 1)];
     const uint4* src = reinterpret_cast<const uint4*>(static_cast<const char*>(a.tables) +
                                                       size_t(chunk_index(a)) * kChunkTableBytes);
     uint4* dst = reinterpret_cast<uint4*>(&T);
-    for (int i = threadIdx.x; i < static_cast<int>(sizeof(ChunkTable) / 16); i += blockDim.x) dst[i] = src[i];
-    if (threadIdx.x < 4) theta_s[threadIdx.x] = static_cast<int>(threadIdx.x) < GQ ? a.theta[q0 + threadIdx.x] : 0.0f;
+    // all of a thread's loads issue before any store (a loop would wait for
+    // each load in turn); indexes past the table copy its last piece again
+    constexpr int kPieces = static_cast<int>(sizeof(ChunkTable) / 16);
+    constexpr int kPer = (kPieces + kMainThreads - 1) / kMainThreads;
+    uint4 piece[kPer];
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) piece[r] = src[min(static_cast<int>(threadIdx.x) + r * kMainThreads, kPieces - 1)];
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) dst[min(static_cast<int>(threadIdx.x) + r * kMainThreads, kPieces - 1)] = piece[r];
+    // (every thread stores, the same value per slot: a store under a branch
+    // would pull the load into it)
+    theta_s[threadIdx.x & 3] = (a.top_lists || static_cast<int>(threadIdx.x & 3) >= GQ) ? 0.0f : theta_in;
   }
   __syncthreads();
+  const int tile_begin = blockIdx.x * a.tiles_per_wg;
+  const int tile_end = min(a.tiles, tile_begin + a.tiles_per_wg);
+  TileScanner scanner(a, T, ring, h, tile_begin, 1, tile_end - tile_begin);
+  scanner.prologue();   // the first plane loads are in flight during the selection
+  if (a.top_lists) {   // uniform
+    if (wave < GQ) {
+      const float th = ordered_to_float(
+          wave_rth_largest<kSampleMaxBlocks>(lv, static_cast<uint32_t>(a.rsel), reinterpret_cast<uint32_t*>(&cbuf[wave][0][0])));
+      if (lane == 0) {
+        theta_s[wave] = th;
+        if (blockIdx.x == 0) a.theta[q0 + wave] = th;
+      }
+    }
+    lds_barrier();
+  }
 
-  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
-  const int lane = threadIdx.x & 63;
   const int col = lane & 15;            // MFMA column: octet col & 7 of key segments 2X + (col >> 3)
   const int G = lane >> 4;              // K slice; in the result, the query of the lane
   const bool qvalid = G < GQ;
@@ -1077,10 +1100,8 @@ __global__ __launch_bounds__(kMainThreads, kMainWgPerCu) void scan_main_kernel(S
     theta_i = tt <= -0x1p31 ? INT_MIN : tt >= 0x1p31 ? INT_MAX : static_cast<int>(ceil(tt));
   }
 
-  const int tile_begin = blockIdx.x * a.tiles_per_wg;
-  const int tile_end = min(a.tiles, tile_begin + a.tiles_per_wg);
   uint32_t wc0 = 0, wc1 = 0, wc2 = 0, wc3 = 0;   // this wave's candidates per query so far (uniform)
-  scan_tiles(a, T, ring, h, tile_begin, 1, tile_end - tile_begin, [&](int tile, const v4i (&acc)[16]) {
+  scanner.run([&](int tile, const v4i (&acc)[16]) {
     const int64_t key0 = column_key(tile, wave, col, 0), key1 = column_key(tile, wave, col, 1);
     auto key_of = [&](int i) { return (i < 8 ? key0 : key1) + (i & 7); };
     const int nv0 = qvalid ? static_cast<int>(max<int64_t>(0, min<int64_t>(8, a.n - key0))) : 0;
@@ -1216,6 +1237,9 @@ __global__ __launch_bounds__(kMainThreads) void scan_sample_kernel(ScanArgs a) {
   const int lane = threadIdx.x & 63;
   const UnionInputs in = load_union_inputs<GQ>(a, h, q0);   // in flight during the allocation
   const uint8_t* ab = a.alloc + int64_t(q0) * kD;
+  // the main kernel's candidate counts start at 0 (on the path without
+  // per-block lists the threshold kernel resets them)
+  if (a.top_lists && blockIdx.x == 0 && static_cast<int>(threadIdx.x) < GQ) a.count[q0 + threadIdx.x] = 0u;
   if (a.var) {   // uniform
     if (wave < GQ) {
       const uint2 b = allocate_query_wave(a.q + int64_t(q0 + wave) * kD, a.var + int64_t(h) * kD, a.budget);
@@ -1389,10 +1413,9 @@ __global__ __launch_bounds__(kSelectThreads) void scan_merge_kernel(ScanArgs a, 
   static_assert(PT * kSelectThreads == kCandCap, "one register per candidate slot");
   // The first kSpecSlots slots of the list load at once, before the count
   // arrives (the list is allocated to its capacity; slots past the count
-  // are masked later), so the two memory round trips overlap.  Slots beyond
-  // them are bounded by the count: a lane past it reads 0 without a memory
-  // access, so those loads issue unconditionally too (a load under a branch
-  // would wait for its data inside the branch).
+  // are masked later), so the two memory round trips overlap.  The rest load
+  // only for a longer list, bounded by the count (a lane past it reads 0
+  // without a memory access).
   constexpr int kSpecSlots = 6;
   uint32_t v[PT], id[PT];
   {
@@ -1410,13 +1433,15 @@ __global__ __launch_bounds__(kSelectThreads) void scan_merge_kernel(ScanArgs a, 
   bool fast = false;   // uniform
 
   if (cnt >= static_cast<uint32_t>(k) && cnt <= static_cast<uint32_t>(kCandCap)) {
-    const __amdgpu_buffer_rsrc_t cand = __builtin_amdgcn_make_buffer_rsrc(
-        a.cand + int64_t(q) * kCandCap, static_cast<short>(0), static_cast<int>(cnt * 8u), 0x00020000);
+    if (cnt > static_cast<uint32_t>(kSpecSlots * kSelectThreads)) {   // uniform
+      const __amdgpu_buffer_rsrc_t cand = __builtin_amdgcn_make_buffer_rsrc(
+          a.cand + int64_t(q) * kCandCap, static_cast<short>(0), static_cast<int>(cnt * 8u), 0x00020000);
 #pragma unroll
-    for (int j = kSpecSlots; j < PT; ++j) {
-      const v2u32 e = __builtin_amdgcn_raw_buffer_load_b64(cand, (tid + j * kSelectThreads) * 8, 0, 0);
-      v[j] = float_to_ordered(__uint_as_float(e.x));
-      id[j] = e.y;
+      for (int j = kSpecSlots; j < PT; ++j) {
+        const v2u32 e = __builtin_amdgcn_raw_buffer_load_b64(cand, (tid + j * kSelectThreads) * 8, 0, 0);
+        v[j] = float_to_ordered(__uint_as_float(e.x));
+        id[j] = e.y;
+      }
     }
     // slots j < nj of this wavefront hold candidates; the others are left
     // out (their pm bit stays clear, and every later use tests pm)
@@ -1653,6 +1678,7 @@ hipError_t launch_scan_topk(const uint32_t* planes, const float* lo, const float
   if (rsel > svalid) rsel = svalid;
   a.rsel = static_cast<int>(rsel);
   a.top_lists = rsel <= kTopR ? 1 : 0;
+  a.nsb = nsb;
 
   // main-kernel work split: kMainWgPerCu resident workgroups per CU, each
   // taking a contiguous run of tiles of one (head, query chunk)
@@ -1682,10 +1708,7 @@ hipError_t launch_scan_topk(const uint32_t* planes, const float* lo, const float
       b.qoff = full * kQueryChunk;
       launch_class(rest, b, H, nsb, sample_phase, full > 0 ? nullptr : ev_start, ev_stop, stream);
     }
-    if (sample_phase && a.top_lists) {
-      hipLaunchKernelGGL(scan_threshold_lists_kernel, dim3(num_q), dim3(64), 0, stream, ws.sample, nsb,
-                         static_cast<uint32_t>(rsel), ws.theta, ws.count);
-    } else if (sample_phase) {
+    if (sample_phase && !a.top_lists) {
       hipLaunchKernelGGL(scan_threshold_kernel, dim3(num_q), dim3(kSelectThreads), 0, stream, ws.sample,
                          nsb * kSampleBlockKeys, static_cast<uint32_t>(rsel), ws.theta, ws.count);
     }
