@@ -18,6 +18,7 @@
 #define FATHOM_ALLOCATE_WAVE_H
 
 #include "fathom_internal.h"
+#include "wave_ops.h"
 
 namespace fathom {
 namespace alloc_detail {
@@ -74,10 +75,19 @@ __device__ inline uint2 allocate_query_wave(const float* __restrict__ q_row, con
     // Search for the budget-th largest key with three probes per round:
     // their counts (each <= 4d = 512 < 2^10) are packed into one word, so one
     // wavefront sum serves all three.  Invariant: count(lo) >= budget >
-    // count(hi).
-    uint32_t lo = 0u;                                      // key -3 2^24: count = 4d >= budget
-    uint32_t hi = 0x7f800001u - kKeyLo;                    // above every finite key: count = 0
+    // count(hi).  The start bracket comes from the lanes' larger keys in
+    // descending order, M_1 >= M_2 >= ...: with r = ceil(budget / 4), the r
+    // lanes whose larger key is >= M_r each have a channel with all four
+    // candidates >= M_r - 3 2^24, so that key counts >= 4r >= budget; and
+    // fewer than r' = ceil(r / 2) lanes hold a key above M_r', at most two
+    // channels each, so M_r' + 1 counts <= 8 (r' - 1) < budget.
     const uint32_t B = static_cast<uint32_t>(budget);
+    const int r = (budget + 3) / 4, r2 = (r + 1) / 2;   // r in 1..128, r2 in 1..64
+    const uint32_t msort = wave_sort_desc(static_cast<uint32_t>(max(k0, k1)));   // keys are >= 0
+    const uint32_t m_r = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(msort), min(r, 64) - 1));
+    const uint32_t m_r2 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(msort), r2 - 1));
+    uint32_t lo = r <= 64 ? m_r : 0u;                      // key M_r - 3 2^24 (else -3 2^24: count 4d)
+    uint32_t hi = m_r2 + 1u - kKeyLo;                      // key M_r' + 1
     while (hi - lo > 1u) {
       const uint32_t step = max(1u, (hi - lo) / 4u);
       const uint32_t t1 = min(lo + step, hi - 1u);
