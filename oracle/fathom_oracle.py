@@ -224,6 +224,57 @@ def distortion(w: np.ndarray, b: np.ndarray) -> float:
 
 
 # --------------------------------------------------------------------------
+# Fixed-depth control reads  [Art findings bullets 1-2; Abs s4]
+# --------------------------------------------------------------------------
+
+CONTROL_UNIFORM = 0
+CONTROL_TOP_CHANNELS = 1
+
+
+def channel_order(q: np.ndarray) -> np.ndarray:
+    """Channel indices by |q_c| descending (fp32 magnitudes), ties to the
+    lower channel index."""
+    a = np.abs(np.asarray(q, dtype=np.float32)).astype(np.float64)
+    return np.lexsort((np.arange(a.shape[0]), -a))
+
+
+def control_allocation(q: np.ndarray, budget: int, mode: int) -> np.ndarray:
+    """Plane counts of a query-independent-depth read with the same budget.
+
+    The pages compare Fathom with scans that read every key at a fixed width
+    (136 and 68 bits).  READING(Z16): two such reads through the same scan:
+
+    * CONTROL_UNIFORM: every channel reads floor(B/d) planes; the B mod d
+      leftover planes go one each to the channels first in channel_order.
+    * CONTROL_TOP_CHANNELS: the floor(B/4) channels first in channel_order
+      read all 4 planes; the B mod 4 leftover planes go to the next one.
+
+    uint8 [d], sum = budget.
+    """
+    q = np.asarray(q, dtype=np.float32)
+    d = q.shape[0]
+    if not 0 <= budget <= PLANES * d:
+        raise ValueError("budget must be in [0, 4d]")
+    rank = np.empty(d, dtype=np.int64)
+    rank[channel_order(q)] = np.arange(d)
+    if mode == CONTROL_UNIFORM:
+        base, rem = divmod(budget, d)
+        b = base + (rank < rem)
+    elif mode == CONTROL_TOP_CHANNELS:
+        r, rem = divmod(budget, PLANES)
+        b = np.where(rank < r, PLANES, np.where(rank == r, rem, 0))
+    else:
+        raise ValueError("unknown control mode")
+    return b.astype(np.uint8)
+
+
+def control_allocation_all(q: np.ndarray, budget: int, mode: int) -> np.ndarray:
+    """control_allocation for every query row: uint8 [Q, d]."""
+    q = np.asarray(q, dtype=np.float32)
+    return np.stack([control_allocation(q[i], budget, mode) for i in range(q.shape[0])])
+
+
+# --------------------------------------------------------------------------
 # Scores and top-k  [Art para 1, 2; Abs s1, s2]
 # --------------------------------------------------------------------------
 
