@@ -1,12 +1,16 @@
 """Benchmark of the Fathom decode-step hot path on one MI355X.
 
-One step = per-query allocation (fathom_allocate) + plane-prefix scan with
-fused top-k (fathom_scan_topk) over every KV head of the workload, inputs
+One step = per-query allocation + plane-prefix scan with fused top-k over
+every KV head of the workload, in one call (fathom_allocate_scan_topk), inputs
 resident in HBM.  The default workload is the 1M-token Qwen3-8B-shaped decode
 step: 8 KV heads x 1,048,576 keys x 128 channels, 32 query heads (GQA 4),
 budget B = 92 bits, k = 2048.  Synthetic seeded keys (no model weights are
 available).  Several copies of the plane store are rotated so that
 consecutive steps never find their planes in the 256 MB Infinity Cache.
+
+The same scan is also timed on the fixed-width reads the pages compare with
+(136 and 68 bits per key: uniform depth, or whole 4-bit channels by |q|), as
+control allocation + scan per step ("controls").
 
 Prints one JSON line (see the repository's design notes for the fields).
 """
@@ -92,6 +96,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true",
                     help="leave the main-kernel timing events off (for traces of the bare step)")
+    ap.add_argument("--control-steps", type=int, default=50,
+                    help="steps per fixed-width control read (0: skip the controls)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this size (for counter calibration)")
     args = ap.parse_args()
@@ -193,6 +199,34 @@ def main():
     gkeys = H * n / (ms_per_step * 1e-3) / 1e9
     achieved = alg_bytes / (main_ms * 1e-3) / 1e9
 
+    # fixed-width control reads through the same scan (after the timed region)
+    controls = {}
+    if args.control_steps > 0:
+        ctrl_alloc = torch.empty((Q, d), dtype=torch.uint8, device=dev)
+        for name, mode, width in (("top_channels_136", fa.FATHOM_CONTROL_TOP_CHANNELS, 136),
+                                  ("uniform_136", fa.FATHOM_CONTROL_UNIFORM, 136),
+                                  ("top_channels_68", fa.FATHOM_CONTROL_TOP_CHANNELS, 68)):
+            def ctrl_step(i):
+                fa.control_allocate(qd, mode, width, out=ctrl_alloc)
+                fa.scan_topk(copies[i % len(copies)], lo, step, store, qd, ctrl_alloc, G, k,
+                             workspace=scan_ws, out_idx=out_idx, out_score=out_score)
+            for i in range(5):
+                ctrl_step(i)
+            torch.cuda.synchronize()
+            c0 = time.perf_counter()
+            for i in range(args.control_steps):
+                ctrl_step(i)
+            torch.cuda.synchronize()
+            c_ms = (time.perf_counter() - c0) * 1e3 / args.control_steps
+            c_bytes = union_bytes(ctrl_alloc.cpu().numpy(), G, store.ldw)
+            controls[name] = {
+                "ms_per_step": round(c_ms, 4),
+                "gkeys_per_s": round(H * n / (c_ms * 1e-3) / 1e9, 3),
+                "union_bits_per_key": round(c_bytes * 8 / (H * store.ldw * 32), 2),
+                "fathom_speedup": round(c_ms / ms_per_step, 3),
+            }
+            log(f"control {name}: {c_ms * 1e3:.1f} us/step")
+
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
@@ -237,6 +271,7 @@ def main():
         "main_kernel_ms": round(main_ms, 4),
         "step_gbs": round(alg_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "pack_ms": round(pack_ms, 3),
+        "controls": controls,
         "kernel_source": source_digest(),
     }
     print(json.dumps(rec), flush=True)

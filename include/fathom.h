@@ -58,6 +58,9 @@ enum {
 /* Operation selector for fathom_workspace_bytes. */
 enum { FATHOM_OP_PACK = 0, FATHOM_OP_SCAN = 1 };
 
+/* Control-read modes of fathom_control_allocate. */
+enum { FATHOM_CONTROL_UNIFORM = 0, FATHOM_CONTROL_TOP_CHANNELS = 1 };
+
 /* Largest k accepted by fathom_scan_topk. */
 #define FATHOM_MAX_K 4096
 
@@ -106,6 +109,21 @@ int fathom_pack_planes(const float* keys, int64_t stride_head, int64_t stride_to
 int fathom_allocate(const float* q, int32_t num_q, int32_t group, const float* var,
                     const fathom_store_desc* store, int32_t budget_bits, uint8_t* alloc,
                     void* hip_stream);
+
+/* Fixed-depth control allocations: the read widths the pages compare Fathom
+ * with (fixed 136- and 68-bit scans; [Art] findings bullets 1-2; [Abs] s4),
+ * as allocations that fathom_scan_topk reads like any other.
+ * q: float32 [num_q][d] (d = 128, 8-byte aligned); budget_bits B in [0, 4d];
+ * alloc: uint8 [num_q][d] (2-byte aligned).  Channels are ranked by |q_c|
+ * descending, ties to the lower channel index.
+ *   FATHOM_CONTROL_UNIFORM: every channel reads floor(B/d) planes, and the
+ *     first B mod d channels in rank order one more.
+ *   FATHOM_CONTROL_TOP_CHANNELS: the first floor(B/4) channels read all 4
+ *     planes and the next one B mod 4.
+ * Every row sums to B.  Returns FATHOM_ERR_INVALID_ARG for a bad mode,
+ * budget, count or alignment (nothing is launched). */
+int fathom_control_allocate(const float* q, int32_t num_q, int32_t mode, int32_t budget_bits, uint8_t* alloc,
+                            void* hip_stream);
 
 /* Plane-prefix scan with fused top-k ([Art] paras 1-2; [Abs] s1-s3).
  * For every query q (KV head h = q / group) and key i < n:

@@ -224,6 +224,21 @@ int fathom_allocate(const float* q, int32_t num_q, int32_t group, const float* v
   return ok();
 }
 
+int fathom_control_allocate(const float* q, int32_t num_q, int32_t mode, int32_t budget_bits, uint8_t* alloc,
+                            void* hip_stream) {
+  if (!q || !alloc) return fail(FATHOM_ERR_INVALID_ARG, "q and alloc must be non-NULL");
+  if (num_q < 1) return fail(FATHOM_ERR_INVALID_ARG, "num_q must be >= 1");
+  if (mode != FATHOM_CONTROL_UNIFORM && mode != FATHOM_CONTROL_TOP_CHANNELS)
+    return fail(FATHOM_ERR_INVALID_ARG, "unknown control mode %d", mode);
+  if (budget_bits < 0 || budget_bits > kPlanes * kD)
+    return fail(FATHOM_ERR_INVALID_ARG, "budget_bits = %d outside [0, %d]", budget_bits, kPlanes * kD);
+  if (!aligned(q, 8) || !aligned(alloc, 2))
+    return fail(FATHOM_ERR_INVALID_ARG, "q must be 8-byte aligned, alloc 2-byte aligned");
+  hipError_t e = launch_control_allocate(q, num_q, mode, budget_bits, alloc, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return hip_fail(e, "fathom_control_allocate launch");
+  return ok();
+}
+
 int fathom_scan_topk(const uint32_t* planes, const float* lo, const float* step,
                      const fathom_store_desc* store, const float* q, const uint8_t* alloc,
                      int32_t num_q, int32_t group, int32_t k, int32_t* out_idx, float* out_score,

@@ -44,6 +44,9 @@ hipError_t launch_pack(const float* keys, int64_t stride_head, int64_t stride_to
 hipError_t launch_allocate(const float* q, int num_q, int group, const float* var, int budget,
                            uint8_t* alloc, hipStream_t stream);
 
+hipError_t launch_control_allocate(const float* q, int num_q, int mode, int budget, uint8_t* alloc,
+                                   hipStream_t stream);
+
 struct ScanWorkspace {
   float* theta;      // [Q] candidate threshold per query
   uint32_t* count;   // [Q] candidates seen per query

@@ -319,10 +319,14 @@ __device__ void table_rows(const UnionLds<GQ>& s, ChunkTable& T) {
 
 // Second part: the A operands and scales, then the store.
 template <int GQ>
-__device__ void table_limbs(const ScanArgs& a, const UnionLds<GQ>& s, ChunkTable& T, double (&wsum)[4],
-                            bool store) {
+__device__ void table_limbs(const UnionLds<GQ>& s, ChunkTable& T, double (&wsum)[4]) {
   build_limbs<GQ>(s, T, wsum, nblocks_of(s.U));   // ends with a barrier
-  if (!store) return;
+}
+
+// Stores the finished table T for the main kernel.  (Issued at the end of
+// the sample kernel: a barrier or stage wait after a store waits for its
+// write to complete.)
+__device__ void store_table(const ScanArgs& a, const ChunkTable& T) {
   uint4* dst = reinterpret_cast<uint4*>(static_cast<char*>(a.tables) + size_t(chunk_index(a)) * kChunkTableBytes);
   const uint4* src = reinterpret_cast<const uint4*>(&T);
   for (int i = threadIdx.x; i < static_cast<int>(sizeof(ChunkTable) / 16); i += blockDim.x) dst[i] = src[i];
@@ -999,10 +1003,7 @@ __global__ __launch_bounds__(kMainThreads, kMainWgPerCu) void scan_main_kernel(S
     if (wave < GQ) {
       const float th = ordered_to_float(
           wave_rth_largest<kSampleMaxBlocks>(lv, static_cast<uint32_t>(a.rsel), reinterpret_cast<uint32_t*>(&cbuf[wave][0][0])));
-      if (lane == 0) {
-        theta_s[wave] = th;
-        if (blockIdx.x == 0) a.theta[q0 + wave] = th;
-      }
+      if (lane == 0) theta_s[wave] = th;   // (workgroup 0 stores it at the end)
     }
     lds_barrier();
   }
@@ -1144,6 +1145,8 @@ __global__ __launch_bounds__(kMainThreads, kMainWgPerCu) void scan_main_kernel(S
     for (uint32_t i = lane; i < kept; i += 64)
       if (b0 + i < static_cast<uint32_t>(kCandCap)) a.cand[int64_t(q0 + g) * kCandCap + b0 + i] = cbuf[wave][g][i];
   }
+  // the threshold of each query, for the merge
+  if (a.top_lists && blockIdx.x == 0 && static_cast<int>(threadIdx.x) < GQ) a.theta[q0 + threadIdx.x] = theta_s[threadIdx.x];
 }
 
 // ------------------------------------------------------------------ sample
@@ -1174,7 +1177,6 @@ __global__ __launch_bounds__(kMainThreads) void scan_sample_kernel(ScanArgs a) {
       const uint2 b = allocate_query_wave(a.q + int64_t(q0 + wave) * kD, a.var + int64_t(h) * kD, a.budget);
       const uint16_t pair = static_cast<uint16_t>(b.x | (b.y << 8));
       s_alloc[wave][lane] = pair;
-      if (blockIdx.x == 0) *reinterpret_cast<uint16_t*>(a.alloc_out + int64_t(q0 + wave) * kD + 2 * lane) = pair;
     }
     __syncthreads();
     ab = reinterpret_cast<const uint8_t*>(&s_alloc[0][0]);
@@ -1188,7 +1190,7 @@ __global__ __launch_bounds__(kMainThreads) void scan_sample_kernel(ScanArgs a) {
   const int tile = sbi * a.sample_stride;   // a sampled block is one tile
   TileScanner sc(a, T, ring, h, tile, 0, 1);
   sc.prologue();   // the block's plane words load while the limbs are built
-  table_limbs<GQ>(a, s, T, wsum, blockIdx.x == 0);
+  table_limbs<GQ>(s, T, wsum);
   sc.run([&](int tile_, const v4i (&acc)[16]) {
     if (G >= GQ) return;
     int tv[16];
@@ -1208,6 +1210,12 @@ __global__ __launch_bounds__(kMainThreads) void scan_sample_kernel(ScanArgs a) {
     if (a.top_lists)
       reinterpret_cast<uint32_t*>(a.sample)[int64_t(q0 + G) * kSampleMaxKeys + sbi * kTopR + wave * 16 + col] = mx;
   });
+  // workgroup 0 of the chunk stores its table and the allocations last
+  if (blockIdx.x == 0) {
+    store_table(a, T);
+    if (a.var && wave < GQ)
+      *reinterpret_cast<uint16_t*>(a.alloc_out + int64_t(q0 + wave) * kD + 2 * lane) = s_alloc[wave][lane];
+  }
 }
 
 // ------------------------------------------------------------------- merge

@@ -23,6 +23,8 @@ FATHOM_ERR_WORKSPACE = -3
 FATHOM_ERR_HIP = -4
 FATHOM_OP_PACK = 0
 FATHOM_OP_SCAN = 1
+FATHOM_CONTROL_UNIFORM = 0
+FATHOM_CONTROL_TOP_CHANNELS = 1
 MAX_K = 4096
 
 EXPORTS = (
@@ -30,6 +32,7 @@ EXPORTS = (
     "fathom_workspace_bytes",
     "fathom_pack_planes",
     "fathom_allocate",
+    "fathom_control_allocate",
     "fathom_scan_topk",
     "fathom_allocate_scan_topk",
     "fathom_host_device_pointer",
@@ -70,6 +73,7 @@ def _load():
         "fathom_workspace_bytes": (sz, [i32, SD, i32, i32]),
         "fathom_pack_planes": (ctypes.c_int, [P, i64, i64, SD, P, P, P, P, P, sz, P]),
         "fathom_allocate": (ctypes.c_int, [P, i32, i32, P, SD, i32, P, P]),
+        "fathom_control_allocate": (ctypes.c_int, [P, i32, i32, i32, P, P]),
         "fathom_scan_topk": (ctypes.c_int, [P, P, P, SD, P, P, i32, i32, i32, P, P, P, P, sz, P]),
         "fathom_allocate_scan_topk": (ctypes.c_int, [P, P, P, P, SD, P, i32, i32, i32, i32, P, P, P, P, sz, P]),
         "fathom_host_device_pointer": (ctypes.c_int, [P, ctypes.POINTER(P)]),
@@ -156,6 +160,16 @@ def allocate(q: torch.Tensor, var: torch.Tensor, group: int, budget: int,
     st = lib.fathom_allocate(_ptr(q), Q, group, _ptr(var), ctypes.byref(store), budget, _ptr(out),
                              _stream(stream))
     _check(st, "fathom_allocate")
+    return out
+
+
+def control_allocate(q: torch.Tensor, mode: int, budget: int, out: Optional[torch.Tensor] = None, stream=None):
+    """Fixed-depth control allocation (FATHOM_CONTROL_*): q float32 [Q, d] -> uint8 [Q, d]."""
+    Q, d = q.shape
+    if out is None:
+        out = torch.empty((Q, d), dtype=torch.uint8, device=q.device)
+    st = lib.fathom_control_allocate(_ptr(q), Q, mode, budget, _ptr(out), _stream(stream))
+    _check(st, "fathom_control_allocate")
     return out
 
 

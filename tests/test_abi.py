@@ -97,6 +97,22 @@ def test_allocate_validation():
     assert "513" in (_alloc(s, budget=513) and lib.fathom_last_error().decode())
 
 
+def _control(num_q=8, mode=0, budget=136, q=FAKE, alloc=FAKE):
+    return lib.fathom_control_allocate(q, num_q, mode, budget, alloc, None)
+
+
+def test_control_allocate_validation():
+    assert _control(mode=2) == fa.FATHOM_ERR_INVALID_ARG
+    assert _control(mode=-1) == fa.FATHOM_ERR_INVALID_ARG
+    assert _control(budget=-1) == fa.FATHOM_ERR_INVALID_ARG
+    assert _control(budget=513) == fa.FATHOM_ERR_INVALID_ARG
+    assert _control(num_q=0) == fa.FATHOM_ERR_INVALID_ARG
+    assert _control(q=None) == fa.FATHOM_ERR_INVALID_ARG
+    assert _control(q=ctypes.c_void_p(0x1004)) == fa.FATHOM_ERR_INVALID_ARG
+    assert _control(alloc=ctypes.c_void_p(0x1001)) == fa.FATHOM_ERR_INVALID_ARG
+    assert "mode" in (_control(mode=5) and lib.fathom_last_error().decode())
+
+
 def _scan(store, num_q=8, group=4, k=16, planes=FAKE, ws=FAKE, ws_bytes=1 << 30, out_idx=FAKE):
     return lib.fathom_scan_topk(planes, FAKE, FAKE, ctypes.byref(store), FAKE, FAKE, num_q, group, k,
                                 out_idx, FAKE, None, ws, ws_bytes, None)

@@ -287,6 +287,46 @@ def test_fused_allocate_scan_matches_two_calls(n, H, group, budget, k):
     assert np.array_equal(host(f_val), host(val))
 
 
+def test_control_allocation_matches_oracle():
+    """Fixed-depth control allocations (uniform depth; whole 4-bit channels
+    by |q|) are bit-identical to the oracle's, ties in |q| included."""
+    say("control allocation")
+    rng = np.random.default_rng(23)
+    q = rng.standard_normal((40, 128)).astype(np.float32)
+    q[1] = 0.0                                   # all magnitudes tie
+    q[2, 64:] = -q[2, :64]                       # pairs of equal magnitudes
+    q[3, ::3] = 0.5
+    qd = dev(q)
+    for mode in (fa.FATHOM_CONTROL_UNIFORM, fa.FATHOM_CONTROL_TOP_CHANNELS):
+        for B in (0, 1, 3, 68, 92, 127, 128, 129, 136, 300, 511, 512):
+            got = host(fa.control_allocate(qd, mode, B))
+            assert np.array_equal(got, O.control_allocation_all(q, B, mode)), (mode, B)
+
+
+@pytest.mark.parametrize("mode,budget", [(0, 136), (1, 136), (1, 68)])
+def test_control_reads_through_the_scan(mode, budget):
+    """The scan reads a control allocation like any other: scores and top-k
+    match the oracle's for that allocation."""
+    say("control scan", mode, budget)
+    n, H, group, k = 70000, 2, 4, 500
+    keys, q = synth.make_inputs(211 + mode, H, n, H * group)
+    planes, lo, step, _ = gpu_pack(keys)
+    store = fa.store_desc(H, n, 128)
+    qd = dev(q)
+    alloc = fa.control_allocate(qd, mode, budget)
+    alloc_ref = O.control_allocation_all(q, budget, mode)
+    assert np.array_equal(host(alloc), alloc_ref)
+    sc = torch.empty((H * group, n), dtype=torch.float32, device=DEV)
+    idx, val = fa.scan_topk(planes, lo, step, store, qd, alloc, group, k, all_scores=sc)
+    idx, val, sc = host(idx), host(val), host(sc)
+    heads = oracle_heads(keys)
+    for i in range(H * group):
+        _, l, s, _, codes = heads[i // group]
+        s_ref = oracle_scores(codes, l, s, q[i], alloc_ref[i])
+        check_scores(sc[i], s_ref)
+        check_topk(idx[i], val[i], s_ref, k, n)
+
+
 def test_host_resident_store_matches_device():
     """The store read zero-copy from pinned host memory gives the same
     result as the HBM-resident store."""
