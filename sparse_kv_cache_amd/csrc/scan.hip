@@ -50,6 +50,13 @@
 #include "fathom_internal.h"
 #include "wave_ops.h"
 
+#ifndef WAVE_X
+#define WAVE_X 2
+#endif
+#ifndef MAIN_STAGES
+#define MAIN_STAGES 3
+#endif
+
 namespace fathom {
 namespace {
 
@@ -58,20 +65,35 @@ constexpr int kBlockPlanes = 64;               // union planes per MFMA (its K)
 constexpr int kMaxBlocks = kMaxUnion / kBlockPlanes;
 // the union is padded with readable zero-weight rows to whole K blocks
 constexpr int kPadPlanes = kBlockPlanes;
-constexpr int kMainThreads = 256;              // 4 wavefronts
-constexpr int kMainWaves = kMainThreads / 64;
-constexpr int kMainWgPerCu = 4;                // 4 resident workgroups per CU: <= 128 VGPRs, <= 40 KB of LDS
-constexpr int kWaveWords = 8;                  // 16 MFMA columns = 8 words x 2 halves
-constexpr int kTileWords = kMainWaves * kWaveWords;   // 32 words = 1024 keys
+// A tile is 32 plane words (1024 keys).  Each wavefront takes kWaveX
+// groups of 4 words: 16 MFMA columns of 8 keys, in two 64-key segments.
+// kWaveX = 2 (4 wavefronts of 110 VGPRs, 4 workgroups per CU) measured
+// faster on the 1M-key step than kWaveX = 1 (8 wavefronts of 64-66 VGPRs,
+// 3 or 4 workgroups per CU): 45.5 against 48-50 us.
+constexpr int kTileWords = 32;
+constexpr int kWaveX = WAVE_X;
+constexpr int kWaveWords = 4 * kWaveX;
+constexpr int kWaveKeys = 8 * kWaveX;                 // keys per lane and tile (one accumulator each)
+constexpr int kMainWaves = kTileWords / kWaveWords;
+constexpr int kMainThreads = 64 * kMainWaves;
+constexpr int kDmaPerWave = 8 / kMainWaves;          // a stage is 8 DMA loads
+#ifdef MAIN_WG_PER_CU
+constexpr int kMainWgPerCu = MAIN_WG_PER_CU;
+#else
+constexpr int kMainWgPerCu = kWaveX == 2 ? 4 : 3;    // 16 or 24 wavefronts per CU
+#endif
 // Workgroup LDS ring of plane words: a stage holds one K block of the
 // workgroup's tile (64 planes x 32 words), written by eight LDS DMA loads of
 // 8 planes x 128 bytes (two per wave; whole 128-byte lines).  Loads run
 // kMainStages - 2 stages ahead of the stage being read, plus the one issued
 // while it is read.
-constexpr int kMainStages = 3;
+constexpr int kMainStages = MAIN_STAGES;
 constexpr int kDmaDwords = 8 * kTileWords + 8;           // one DMA load (8 planes x 32 words) + bank padding
 constexpr int kStageDwords = 8 * kDmaDwords;
-constexpr int kWaveCand = 32;                  // candidates per (wave, query) buffered in LDS
+#ifndef WAVE_CAND
+#define WAVE_CAND 32
+#endif
+constexpr int kWaveCand = WAVE_CAND;           // candidates per (wave, query) buffered in LDS
 constexpr int kTopR = 64;                      // largest sample rank served by per-block lane maxima
 constexpr int kSelectThreads = 1024;
 constexpr int kSelectWaves = kSelectThreads / 64;
@@ -615,7 +637,7 @@ __global__ __launch_bounds__(kSelectThreads) void scan_threshold_kernel(
 // the rsel-th largest sampled score and, while the best rsel scores fall in
 // distinct groups, equals it; the threshold then selects from at most
 // kSampleMaxBlocks * 64 values instead of the whole sample.
-static_assert(kTopR == kMainWaves * 16, "a block's list holds one maximum per (wavefront, column)");
+static_assert(kTopR * 16 == kTileWords * 32, "a block's list holds one maximum per 16 keys");
 
 
 // r-th largest (1 <= r <= number of values) of the ordered keys v[m] of the
@@ -753,28 +775,44 @@ __device__ __forceinline__ void sync_stage() {
 // 16G + 8k + 4h .. + 3 in bytes 0..3, bit e of each byte being key 8 (j % 8)
 // + e of the segment.  The block also reads the lane's A operand (16 bytes
 // at a_addr), which the compiler would otherwise fence the same way.
-__device__ __forceinline__ void read_stage(uint32_t addr, uint32_t a_addr, uint32_t (&t)[8], v4i& A) {
-  v2u r0, r1, r2, r3;
+__device__ __forceinline__ void read_stage(uint32_t addr, uint32_t a_addr, uint32_t (&t)[4 * kWaveX], v4i& A) {
   // plane 16G + 8k + j / 2 sits in row 2G + k of DMA load j / 2 (128 bytes
   // per row), so k adds 128 bytes and X, two segments, 16
-  asm volatile(
-      "ds_read_b128 %4, %6\n\t"
-      "ds_read_b64_tr_b8 %0, %5\n\t"
-      "ds_read_b64_tr_b8 %1, %5 offset:128\n\t"
-      "ds_read_b64_tr_b8 %2, %5 offset:16\n\t"
-      "ds_read_b64_tr_b8 %3, %5 offset:144\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(A)
-      : "v"(addr), "v"(a_addr)
-      : "memory");
-  t[0] = r0.x;
-  t[1] = r0.y;
-  t[2] = r1.x;
-  t[3] = r1.y;
-  t[4] = r2.x;
-  t[5] = r2.y;
-  t[6] = r3.x;
-  t[7] = r3.y;
+  if constexpr (kWaveX == 2) {
+    v2u r0, r1, r2, r3;
+    asm volatile(
+        "ds_read_b128 %4, %6\n\t"
+        "ds_read_b64_tr_b8 %0, %5\n\t"
+        "ds_read_b64_tr_b8 %1, %5 offset:128\n\t"
+        "ds_read_b64_tr_b8 %2, %5 offset:16\n\t"
+        "ds_read_b64_tr_b8 %3, %5 offset:144\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(A)
+        : "v"(addr), "v"(a_addr)
+        : "memory");
+    t[0] = r0.x;
+    t[1] = r0.y;
+    t[2] = r1.x;
+    t[3] = r1.y;
+    t[4] = r2.x;
+    t[5] = r2.y;
+    t[6] = r3.x;
+    t[7] = r3.y;
+  } else {
+    v2u r0, r1;
+    asm volatile(
+        "ds_read_b128 %2, %4\n\t"
+        "ds_read_b64_tr_b8 %0, %3\n\t"
+        "ds_read_b64_tr_b8 %1, %3 offset:128\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r0), "=&v"(r1), "=&v"(A)
+        : "v"(addr), "v"(a_addr)
+        : "memory");
+    t[0] = r0.x;
+    t[1] = r0.y;
+    t[2] = r1.x;
+    t[3] = r1.y;
+  }
 }
 
 // One K block: two sets X of 16 columns, 8 MFMAs each.  For key e of a
@@ -784,10 +822,10 @@ __device__ __forceinline__ void read_stage(uint32_t addr, uint32_t a_addr, uint3
 // so acc[8X + e] holds the key's limb sums times that scale.  The first
 // block of a tile starts from a zero accumulator.
 template <bool FIRST>
-__device__ __forceinline__ void mfma_block(const uint32_t (&t)[8], v4i A, v4i (&acc)[16]) {
+__device__ __forceinline__ void mfma_block(const uint32_t (&t)[4 * kWaveX], v4i A, v4i (&acc)[kWaveKeys]) {
   const v4i zero = {0, 0, 0, 0};
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < kWaveKeys; ++i) {
     const uint32_t m = 0x01010101u << (i & 7);
     const int X = i >> 3;
     v4i bv;
@@ -836,7 +874,7 @@ struct TileScanner {
     G = lane >> 4;
     nsteps = max(0, ntiles) * nblk;   // (tile, block) steps
     it_tile = first_tile;
-    // Loads.  DMA load q = 2 wave + j (j = 0, 1) of a stage, lane l: row
+    // Loads.  DMA load q = kDmaPerWave wave + j of a stage, lane l: row
     // l >> 3 holds plane q + 8 (l >> 3) of the block, bytes 16 (l & 7) .. + 15
     // of the tile's 128.  (The eight planes a transpose read gathers then sit
     // in eight different loads, whose padding spreads them over the banks.)
@@ -861,8 +899,8 @@ struct TileScanner {
     if (issued < nsteps) {
       const uint32_t woff = static_cast<uint32_t>(it_tile * kTileWords) * 4u;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int q = 2 * wave + j;
+      for (int j = 0; j < kDmaPerWave; ++j) {
+        const int q = kDmaPerWave * wave + j;
         const uint32_t vo = T.rowoff[it_b * kBlockPlanes + q + 8 * (lane >> 3)] + dma_lane_off + woff;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, &ring[it_slot][q * kDmaDwords], 16, vo, 0, 0, 0);
       }
@@ -884,16 +922,16 @@ struct TileScanner {
   __device__ void run(Epi&& epi) {
     int step_i = 0, slot = 0;
     for (int ti = 0, tile = first_tile; ti < ntiles; ++ti, tile += tile_stride) {
-      v4i acc[16];
+      v4i acc[kWaveKeys];
       auto step = [&](auto first, int b) {
         // the last steps have fewer loads behind them: wait for all
         if (step_i + kMainStages - 2 < nsteps) {
-          sync_stage<2 * (kMainStages - 2)>();
+          sync_stage<kDmaPerWave * (kMainStages - 2)>();
         } else {
           sync_stage<0>();
         }
         issue();   // into the slot every wave has finished reading
-        uint32_t x[8];
+        uint32_t x[4 * kWaveX];
         const uint32_t addr = ring_lane + static_cast<uint32_t>(slot * kStageDwords) * 4u;
         const uint32_t a_addr = a_lane + static_cast<uint32_t>(b * 4 * 16 * 16);
         v4i A;
@@ -922,9 +960,9 @@ __device__ void scan_tiles(const ScanArgs& a, const ChunkTable& T, uint32_t (&ri
 // shift by 8j - e, exact (the sums are multiples of 2^e), and t = l0 + 2^8 l1
 // + 2^16 l2 + 2^24 l3 is exact in wrapping int32 arithmetic because
 // |t| < 2^31.  Keys with e = 7 give -t, which t_of undoes.
-__device__ __forceinline__ void limb_sums(const v4i (&acc)[16], int (&tv)[16]) {
+__device__ __forceinline__ void limb_sums(const v4i (&acc)[kWaveKeys], int (&tv)[kWaveKeys]) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < kWaveKeys; ++i) {
     const int e = i & 7;
     // (empty asm: keeps the Horner form, which needs one op per limb)
     uint32_t z = (static_cast<uint32_t>(acc[i].w) << 8) + static_cast<uint32_t>(acc[i].z);
@@ -954,8 +992,9 @@ static_assert(sizeof(ChunkTable) + sizeof(uint32_t) * kMainStages * kStageDwords
                       512 <= 160 * 1024 / kMainWgPerCu,
               "main-kernel LDS fits kMainWgPerCu workgroups per CU");
 
+// (the second launch bound is the minimum number of wavefronts per SIMD)
 template <int GQ>
-__global__ __launch_bounds__(kMainThreads, kMainWgPerCu) void scan_main_kernel(ScanArgs a) {
+__global__ __launch_bounds__(kMainThreads, kMainWgPerCu * kMainWaves / 4) void scan_main_kernel(ScanArgs a) {
   __shared__ ChunkTable T;
   __shared__ uint32_t ring[kMainStages][kStageDwords];
   __shared__ uint2 cbuf[kMainWaves][4][kWaveCand];   // candidates per (wave, query)
@@ -1031,24 +1070,25 @@ __global__ __launch_bounds__(kMainThreads, kMainWgPerCu) void scan_main_kernel(S
   }
 
   uint32_t wc0 = 0, wc1 = 0, wc2 = 0, wc3 = 0;   // this wave's candidates per query so far (uniform)
-  scanner.run([&](int tile, const v4i (&acc)[16]) {
-    const int64_t key0 = column_key(tile, wave, col, 0), key1 = column_key(tile, wave, col, 1);
+  scanner.run([&](int tile, const v4i (&acc)[kWaveKeys]) {
+    const int64_t key0 = column_key(tile, wave, col, 0);
+    const int64_t key1 = kWaveX == 2 ? column_key(tile, wave, col, 1) : key0;
     auto key_of = [&](int i) { return (i < 8 ? key0 : key1) + (i & 7); };
     const int nv0 = qvalid ? static_cast<int>(max<int64_t>(0, min<int64_t>(8, a.n - key0))) : 0;
-    const int nv1 = qvalid ? static_cast<int>(max<int64_t>(0, min<int64_t>(8, a.n - key1))) : 0;
-    int tv[16];
+    const int nv1 = (kWaveX == 2 && qvalid) ? static_cast<int>(max<int64_t>(0, min<int64_t>(8, a.n - key1))) : 0;
+    int tv[kWaveKeys];
     limb_sums(acc, tv);
     auto t_of = [&](int i) { return (i & 7) == 7 ? -tv[i] : tv[i]; };
     // (scale and offset re-read from LDS: only candidates need them)
     auto score_of = [&](int i) { return fmaf(static_cast<float>(t_of(i)), T.sigma[G], T.C[G]); };
     if (a.all_scores) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
+      for (int i = 0; i < kWaveKeys; ++i)
         if ((i & 7) < (i < 8 ? nv0 : nv1)) a.all_scores[int64_t(q0 + G) * a.n + key_of(i)] = score_of(i);
     }
     uint32_t bits = 0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) bits |= t_of(i) >= theta_i ? (1u << i) : 0u;
+    for (int i = 0; i < kWaveKeys; ++i) bits |= t_of(i) >= theta_i ? (1u << i) : 0u;
     bits &= ((1u << nv0) - 1u) | (((1u << nv1) - 1u) << 8);
     if (__ballot(bits != 0) == 0) return;   // uniform
     // Candidates go to this wave's LDS buffer of their query: a DPP row holds
@@ -1084,9 +1124,9 @@ __global__ __launch_bounds__(kMainThreads, kMainWgPerCu) void scan_main_kernel(S
       // from the registers by a select tree on the bits of its index (a
       // computed index into tv would move it to scratch).
       const float sig = T.sigma[G], cq = T.C[G];
-      int tn[16];
+      int tn[kWaveKeys];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) tn[i] = t_of(i);
+      for (int i = 0; i < kWaveKeys; ++i) tn[i] = t_of(i);
       uint32_t slot_c = slot0;
       uint32_t rem = bits;
       while (rem != 0u) {
@@ -1095,15 +1135,21 @@ __global__ __launch_bounds__(kMainThreads, kMainWgPerCu) void scan_main_kernel(S
         // (lane-mask selects written out: as plain selects the compiler
         // would turn them back into an indexed array)
         const uint64_t m0 = __ballot((i & 1) != 0), m1 = __ballot((i & 2) != 0);
-        const uint64_t m2 = __ballot((i & 4) != 0), m3 = __ballot((i & 8) != 0);
+        const uint64_t m2 = __ballot((i & 4) != 0);
         int t8[8], t4[4], t2[2];
+        if constexpr (kWaveKeys == 16) {
+          const uint64_t m3 = __ballot((i & 8) != 0);
 #pragma unroll
-        for (int m = 0; m < 8; ++m) t8[m] = lane_select(tn[2 * m], tn[2 * m + 1], m0);
+          for (int m = 0; m < 8; ++m) t8[m] = lane_select(tn[m], tn[m + 8], m3);
+        } else {
 #pragma unroll
-        for (int m = 0; m < 4; ++m) t4[m] = lane_select(t8[2 * m], t8[2 * m + 1], m1);
+          for (int m = 0; m < 8; ++m) t8[m] = tn[m];
+        }
 #pragma unroll
-        for (int m = 0; m < 2; ++m) t2[m] = lane_select(t4[2 * m], t4[2 * m + 1], m2);
-        const int t = lane_select(t2[0], t2[1], m3);
+        for (int m = 0; m < 4; ++m) t4[m] = lane_select(t8[2 * m], t8[2 * m + 1], m0);
+#pragma unroll
+        for (int m = 0; m < 2; ++m) t2[m] = lane_select(t4[2 * m], t4[2 * m + 1], m1);
+        const int t = lane_select(t2[0], t2[1], m2);
         const float sc = fmaf(static_cast<float>(t), sig, cq);
         const uint32_t key = static_cast<uint32_t>(((i & 8) ? key1 : key0) + (i & 7));
         const uint2 e = make_uint2(__float_as_uint(sc), key);
@@ -1191,14 +1237,14 @@ __global__ __launch_bounds__(kMainThreads) void scan_sample_kernel(ScanArgs a) {
   TileScanner sc(a, T, ring, h, tile, 0, 1);
   sc.prologue();   // the block's plane words load while the limbs are built
   table_limbs<GQ>(s, T, wsum);
-  sc.run([&](int tile_, const v4i (&acc)[16]) {
+  sc.run([&](int tile_, const v4i (&acc)[kWaveKeys]) {
     if (G >= GQ) return;
-    int tv[16];
+    int tv[kWaveKeys];
     limb_sums(acc, tv);
     const float sigma = T.sigma[G], Cq = T.C[G];
     uint32_t mx = 0u;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < kWaveKeys; ++i) {
       const int64_t key = column_key(tile_, wave, col, i >> 3) + (i & 7);
       const int t = (i & 7) == 7 ? -tv[i] : tv[i];
       const float sc = fmaf(static_cast<float>(t), sigma, Cq);
@@ -1207,8 +1253,17 @@ __global__ __launch_bounds__(kMainThreads) void scan_sample_kernel(ScanArgs a) {
       mx = max(mx, float_to_ordered(score));
       if (!a.top_lists) a.sample[int64_t(q0 + G) * kSampleMaxKeys + sbi * kSampleBlockKeys + local] = score;
     }
-    if (a.top_lists)
-      reinterpret_cast<uint32_t*>(a.sample)[int64_t(q0 + G) * kSampleMaxKeys + sbi * kTopR + wave * 16 + col] = mx;
+    // one maximum per 16 keys: a lane's own, or (8 keys per lane) those of
+    // two neighbouring columns
+    if (a.top_lists) {
+      uint32_t* list = reinterpret_cast<uint32_t*>(a.sample) + int64_t(q0 + G) * kSampleMaxKeys + sbi * kTopR;
+      if constexpr (kWaveKeys == 16) {
+        list[wave * 16 + col] = mx;
+      } else {
+        mx = max(mx, dpp_u32<kDppXor1>(mx, mx));
+        if ((col & 1) == 0) list[wave * 8 + (col >> 1)] = mx;
+      }
+    }
   });
   // workgroup 0 of the chunk stores its table and the allocations last
   if (blockIdx.x == 0) {
