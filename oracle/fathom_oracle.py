@@ -367,3 +367,39 @@ def decode_step(keys: np.ndarray, q: np.ndarray, group: int, budget: int, k: int
         "idx": idx,
         "val": val,
     }
+
+
+# --------------------------------------------------------------------------
+# Attention over the selected keys  [Abs title and s1; Art findings bullet 2]
+# --------------------------------------------------------------------------
+
+def attention(k_rows: np.ndarray, v_rows: np.ndarray, q: np.ndarray, scale: float) -> np.ndarray:
+    """Softmax attention of one query over the given key/value rows.
+
+    READING(Z17): the decode step that follows the top-k selection attends
+    over the selected rows only, with the usual scaled dot-product softmax:
+        p_i = exp(scale q.k_i - max_j scale q.k_j),  o = sum_i p_i v_i / sum_i p_i
+    in float64 on the rows as stored.  k_rows, v_rows [m, d] (m >= 1) ->
+    float64 [d].
+    """
+    K = np.asarray(k_rows).astype(np.float64)
+    V = np.asarray(v_rows).astype(np.float64)
+    if K.shape[0] < 1:
+        raise ValueError("attention needs at least one row")
+    z = scale * (K @ np.asarray(q, np.float32).astype(np.float64))
+    p = np.exp(z - z.max())
+    return (p @ V) / p.sum()
+
+
+def sparse_attention(K: np.ndarray, V: np.ndarray, q: np.ndarray, idx: np.ndarray, scale: float) -> np.ndarray:
+    """attention() over the rows idx of one head's K, V [n, d]."""
+    idx = np.asarray(idx, dtype=np.int64)
+    return attention(np.asarray(K)[idx], np.asarray(V)[idx], q, scale)
+
+
+def attention_error(o_sparse: np.ndarray, o_dense: np.ndarray) -> float:
+    """READING(Z17): relative L2 error of the sparse output against dense
+    attention over all n keys."""
+    o_dense = np.asarray(o_dense, np.float64)
+    return float(np.linalg.norm(np.asarray(o_sparse, np.float64) - o_dense) / np.linalg.norm(o_dense))
+

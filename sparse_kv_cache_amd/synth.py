@@ -18,6 +18,8 @@ pages' task suites are available, so keys are drawn per KV head as
 
 and queries as N(0, 1) float32.  Generator: NumPy PCG64 via
 ``np.random.default_rng(seed)``; heads are drawn in order, then the queries.
+Value rows (for the attention over the selected keys) are N(0, 1) float32,
+drawn per head from a separate stream.
 """
 
 from __future__ import annotations
@@ -99,6 +101,13 @@ def stream_inputs(seed: int, num_kv_heads: int, n: int, num_q: int, d: int = D_D
     for h in range(num_kv_heads):
         yield "head", h, head_keys(rng, n, d)
     yield "queries", rng.standard_normal((num_q, d), dtype=np.float32)
+
+
+def head_values(seed: int, h: int, n: int, d: int = D_DEFAULT) -> np.ndarray:
+    """Value rows of KV head h for the attention step, float32 [n, d] ~ N(0, 1),
+    from a stream of their own (seed, h), so the key and query draws are
+    unchanged."""
+    return np.random.default_rng([seed, 1 << 20, h]).standard_normal((n, d), dtype=np.float32)
 
 
 def forced_tie_keys(seed: int, n: int, d: int = D_DEFAULT) -> np.ndarray:
