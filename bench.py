@@ -8,6 +8,10 @@ budget B = 92 bits, k = 2048.  Synthetic seeded keys (no model weights are
 available).  Several copies of the plane store are rotated so that
 consecutive steps never find their planes in the 256 MB Infinity Cache.
 
+After the timed region, attention over the rows the step selected (bf16 K
+and V, split over chunks of the selected rows, then combined) is timed too
+("attention").
+
 The same scan is also timed on the fixed-width reads the pages compare with
 (136 and 68 bits per key: uniform depth, or whole 4-bit channels by |q|), as
 control allocation + scan per step ("controls").
@@ -98,6 +102,8 @@ def main():
                     help="leave the main-kernel timing events off (for traces of the bare step)")
     ap.add_argument("--control-steps", type=int, default=50,
                     help="steps per fixed-width control read (0: skip the controls)")
+    ap.add_argument("--attention-steps", type=int, default=50,
+                    help="steps of attention over the selected rows (0: skip)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this size (for counter calibration)")
     args = ap.parse_args()
@@ -144,6 +150,9 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     pack_ms = e0.elapsed_time(e1)
+    # bf16 K and V rows for the attention over the selected keys (V drawn on
+    # the device from a fixed seed)
+    k_bf16 = keys.to(torch.bfloat16) if args.attention_steps > 0 else None
     del keys
     torch.cuda.empty_cache()
     copies = [planes0] + [planes0.clone() for _ in range(max(1, args.copies) - 1)]
@@ -227,6 +236,34 @@ def main():
             }
             log(f"control {name}: {c_ms * 1e3:.1f} us/step")
 
+    # attention over the rows the last step selected (after the timed region)
+    attention = None
+    if args.attention_steps > 0:
+        fa.allocate_scan_topk(copies[0], lo, step, var, store, qd, G, budget, k, workspace=scan_ws, alloc=alloc,
+                              out_idx=out_idx, out_score=out_score)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(w.seed + 7)
+        v_bf16 = torch.randn((H, n, d), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        att_ws = fa.alloc_workspace(fa.workspace_bytes(fa.FATHOM_OP_ATTEND, store, Q, k), dev)
+        att_out = torch.empty((Q, d), dtype=torch.float32, device=dev)
+        for _ in range(5):
+            fa.sparse_attention(k_bf16, v_bf16, store, qd, out_idx, G, out=att_out, workspace=att_ws)
+        torch.cuda.synchronize()
+        a0 = time.perf_counter()
+        for _ in range(args.attention_steps):
+            fa.sparse_attention(k_bf16, v_bf16, store, qd, out_idx, G, out=att_out, workspace=att_ws)
+        torch.cuda.synchronize()
+        a_ms = (time.perf_counter() - a0) * 1e3 / args.attention_steps
+        a_bytes = Q * k * 2 * d * 2 + Q * k * 4 + Q * d * 8
+        attention = {
+            "ms_per_step": round(a_ms, 4),
+            "rows_per_step": Q * k,
+            "gbs": round(a_bytes / (a_ms * 1e-3) / 1e9, 1),
+            "decode_step_ms": round(ms_per_step + a_ms, 4),
+        }
+        log(f"attention over the selected rows: {a_ms * 1e3:.1f} us/step")
+        del v_bf16, k_bf16
+
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
@@ -272,6 +309,7 @@ def main():
         "step_gbs": round(alg_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "pack_ms": round(pack_ms, 3),
         "controls": controls,
+        "attention": attention,
         "kernel_source": source_digest(),
     }
     print(json.dumps(rec), flush=True)

@@ -56,7 +56,7 @@ enum {
 };
 
 /* Operation selector for fathom_workspace_bytes. */
-enum { FATHOM_OP_PACK = 0, FATHOM_OP_SCAN = 1 };
+enum { FATHOM_OP_PACK = 0, FATHOM_OP_SCAN = 1, FATHOM_OP_ATTEND = 2 };
 
 /* Control-read modes of fathom_control_allocate. */
 enum { FATHOM_CONTROL_UNIFORM = 0, FATHOM_CONTROL_TOP_CHANNELS = 1 };
@@ -78,7 +78,8 @@ typedef struct fathom_store_desc {
 int64_t fathom_plane_ldw(int64_t n);
 
 /* Bytes of device workspace needed by an operation (FATHOM_OP_PACK: num_q and
- * k are ignored; FATHOM_OP_SCAN: the scan + top-k of num_q queries).  Returns
+ * k are ignored; FATHOM_OP_SCAN: the scan + top-k of num_q queries;
+ * FATHOM_OP_ATTEND: attention of num_q queries over k selected rows).  Returns
  * 0 for an invalid description.  The workspace pointer must be 256-byte
  * aligned. */
 size_t fathom_workspace_bytes(int32_t op, const fathom_store_desc* store, int32_t num_q, int32_t k);
@@ -156,6 +157,25 @@ int fathom_allocate_scan_topk(const uint32_t* planes, const float* lo, const flo
 /* Device-visible address of pinned host memory (allocated with hipHostMalloc
  * or torch pin_memory), for a plane store kept in host RAM ([Art] para 1;
  * [Abs] s1: the index lives in host memory).  Not for registered memory. */
+/* Attention over the selected keys: the decode step after the top-k scan
+ * ([Abs] title and s1; [Art] findings bullet 2 for its error measure).  For
+ * query q (KV head h = q / group) and its k selected rows i = idx[q][0..k):
+ *   p_i = exp(scale * q.k_i - max),  out[q] = sum_i p_i v_i / sum_i p_i,
+ * accumulated in fp32.  k_rows, v_rows: bf16 (uint16 bit patterns); row i of
+ * head h at [h * stride_head + i * stride_token], channel stride 1, d = 128;
+ * device pointers or device-visible pinned host pointers (rows then cross
+ * PCIe).  Bases 16-byte aligned, strides in elements, multiples of 8,
+ * stride_token >= d.  q: float32 [num_q][d]; idx: int32 [num_q][k] (typically
+ * fathom_scan_topk's out_idx; an index outside [0, n) is skipped); scale
+ * finite (e.g. 1/sqrt(d)); out: float32 [num_q][d] (0 for a query with no
+ * index in range).  1 <= k <= min(n, FATHOM_MAX_K).
+ * workspace: >= fathom_workspace_bytes(FATHOM_OP_ATTEND, store, num_q, k)
+ * bytes, 256-byte aligned.  Two kernel launches on hip_stream. */
+int fathom_sparse_attention(const uint16_t* k_rows, const uint16_t* v_rows, int64_t stride_head,
+                            int64_t stride_token, const fathom_store_desc* store, const float* q,
+                            const int32_t* idx, int32_t num_q, int32_t group, int32_t k, float scale,
+                            float* out, void* workspace, size_t workspace_bytes, void* hip_stream);
+
 int fathom_host_device_pointer(void* pinned_host, void** device_ptr);
 
 /* Static text for a status code. */

@@ -3,6 +3,7 @@
 // behaviour, are in include/fathom.h.  Every check below runs on the host
 // before any HIP call, so an invalid call launches nothing.
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -156,6 +157,11 @@ int scan_impl(const char* where, const uint32_t* planes, const float* lo, const 
   return ok();
 }
 
+size_t attend_bytes(int num_q, int k) {
+  const size_t b = size_t(num_q) * size_t(attend_splits(k)) * size_t(kD + 2) * sizeof(float);
+  return (b + 255) / 256 * 256;
+}
+
 }  // namespace
 
 extern "C" {
@@ -172,6 +178,10 @@ size_t fathom_workspace_bytes(int32_t op, const fathom_store_desc* store, int32_
   if (op == FATHOM_OP_SCAN) {
     if (num_q < 1 || k < 1) return 0;
     return scan_layout(num_q).total;
+  }
+  if (op == FATHOM_OP_ATTEND) {
+    if (num_q < 1 || k < 1 || k > kMaxK) return 0;
+    return attend_bytes(num_q, k);
   }
   return 0;
 }
@@ -254,6 +264,39 @@ int fathom_allocate_scan_topk(const uint32_t* planes, const float* lo, const flo
   if (!var) return fail(FATHOM_ERR_INVALID_ARG, "var must be non-NULL");
   return scan_impl("fathom_allocate_scan_topk launch", planes, lo, step, store, q, nullptr, num_q, group, k,
                    out_idx, out_score, nullptr, workspace, workspace_bytes, hip_stream, var, budget_bits, alloc);
+}
+
+int fathom_sparse_attention(const uint16_t* k_rows, const uint16_t* v_rows, int64_t stride_head,
+                            int64_t stride_token, const fathom_store_desc* store, const float* q,
+                            const int32_t* idx, int32_t num_q, int32_t group, int32_t k, float scale,
+                            float* out, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  int st = check_store(store);
+  if (st != FATHOM_OK) return st;
+  if (!k_rows || !v_rows || !q || !idx || !out)
+    return fail(FATHOM_ERR_INVALID_ARG, "k_rows, v_rows, q, idx and out must be non-NULL");
+  if (num_q < 1 || group < 1) return fail(FATHOM_ERR_INVALID_ARG, "num_q and group must be >= 1");
+  if (static_cast<int64_t>(store->num_kv_heads) * group != num_q)
+    return fail(FATHOM_ERR_INVALID_ARG, "num_q = %d must equal num_kv_heads (%d) * group (%d)", num_q,
+                store->num_kv_heads, group);
+  if (k < 1 || k > store->n) return fail(FATHOM_ERR_INVALID_ARG, "k = %d outside [1, n]", k);
+  if (k > kMaxK) return fail(FATHOM_ERR_UNSUPPORTED, "k = %d above %d", k, kMaxK);
+  if (!std::isfinite(scale)) return fail(FATHOM_ERR_INVALID_ARG, "scale must be finite");
+  if (!aligned(k_rows, 16) || !aligned(v_rows, 16))
+    return fail(FATHOM_ERR_INVALID_ARG, "k_rows and v_rows must be 16-byte aligned");
+  if (stride_token < kD || stride_token % 8 != 0)
+    return fail(FATHOM_ERR_INVALID_ARG, "stride_token must be >= d and a multiple of 8");
+  if (store->num_kv_heads > 1 && (stride_head < store->n * stride_token || stride_head % 8 != 0))
+    return fail(FATHOM_ERR_INVALID_ARG, "stride_head must be >= n * stride_token and a multiple of 8");
+  if (!aligned(q, 4) || !aligned(idx, 4) || !aligned(out, 4))
+    return fail(FATHOM_ERR_INVALID_ARG, "q, idx and out must be 4-byte aligned");
+  const size_t need = attend_bytes(num_q, k);
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < need)
+    return fail(FATHOM_ERR_WORKSPACE, "attention needs a 256-byte aligned workspace of %zu bytes (got %zu)", need,
+                workspace_bytes);
+  hipError_t e = launch_attend(k_rows, v_rows, stride_head, stride_token, store->n, q, idx, num_q, group, k, scale,
+                               static_cast<float*>(workspace), out, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return hip_fail(e, "fathom_sparse_attention launch");
+  return ok();
 }
 
 int fathom_host_device_pointer(void* pinned_host, void** device_ptr) {

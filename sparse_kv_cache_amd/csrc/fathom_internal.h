@@ -47,6 +47,13 @@ hipError_t launch_allocate(const float* q, int num_q, int group, const float* va
 hipError_t launch_control_allocate(const float* q, int num_q, int mode, int budget, uint8_t* alloc,
                                    hipStream_t stream);
 
+// Attention over selected rows: chunks per query, and the two launches
+// (partials into part [num_q][attend_splits(k)][kD + 2], then the combine).
+int attend_splits(int k);
+hipError_t launch_attend(const uint16_t* k_rows, const uint16_t* v_rows, int64_t stride_head,
+                         int64_t stride_token, int64_t n, const float* q, const int32_t* idx, int num_q,
+                         int group, int k, float scale, float* part, float* out, hipStream_t stream);
+
 struct ScanWorkspace {
   float* theta;      // [Q] candidate threshold per query
   uint32_t* count;   // [Q] candidates seen per query

@@ -23,6 +23,7 @@ FATHOM_ERR_WORKSPACE = -3
 FATHOM_ERR_HIP = -4
 FATHOM_OP_PACK = 0
 FATHOM_OP_SCAN = 1
+FATHOM_OP_ATTEND = 2
 FATHOM_CONTROL_UNIFORM = 0
 FATHOM_CONTROL_TOP_CHANNELS = 1
 MAX_K = 4096
@@ -35,6 +36,7 @@ EXPORTS = (
     "fathom_control_allocate",
     "fathom_scan_topk",
     "fathom_allocate_scan_topk",
+    "fathom_sparse_attention",
     "fathom_host_device_pointer",
     "fathom_status_string",
     "fathom_last_error",
@@ -76,6 +78,8 @@ def _load():
         "fathom_control_allocate": (ctypes.c_int, [P, i32, i32, i32, P, P]),
         "fathom_scan_topk": (ctypes.c_int, [P, P, P, SD, P, P, i32, i32, i32, P, P, P, P, sz, P]),
         "fathom_allocate_scan_topk": (ctypes.c_int, [P, P, P, P, SD, P, i32, i32, i32, i32, P, P, P, P, sz, P]),
+        "fathom_sparse_attention": (ctypes.c_int, [P, P, i64, i64, SD, P, P, i32, i32, i32, ctypes.c_float, P, P,
+                                                   sz, P]),
         "fathom_host_device_pointer": (ctypes.c_int, [P, ctypes.POINTER(P)]),
         "fathom_status_string": (ctypes.c_char_p, [i32]),
         "fathom_last_error": (ctypes.c_char_p, []),
@@ -220,6 +224,37 @@ def allocate_scan_topk(planes: torch.Tensor, lo: torch.Tensor, step: torch.Tenso
                                        _ptr(workspace), workspace.numel(), _stream(stream))
     _check(st, "fathom_allocate_scan_topk")
     return alloc, out_idx, out_score
+
+
+def sparse_attention(k_rows: torch.Tensor, v_rows: torch.Tensor, store: StoreDesc, q: torch.Tensor,
+                     idx: torch.Tensor, group: int, scale: Optional[float] = None, *,
+                     out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                     k_ptr: Optional[int] = None, v_ptr: Optional[int] = None, stream=None):
+    """Attention of each query over its selected rows: k_rows, v_rows bfloat16
+    [H, n, d] (channel stride 1; k_ptr / v_ptr override the addresses, e.g.
+    for rows in pinned host memory), q float32 [Q, d], idx int32 [Q, k] ->
+    out float32 [Q, d]."""
+    assert k_rows.dtype == torch.bfloat16 and v_rows.dtype == torch.bfloat16
+    H = k_rows.shape[0]
+    assert k_rows.shape == v_rows.shape and k_rows.stride(2) == 1 and v_rows.stride(2) == 1
+    assert k_rows.stride(1) == v_rows.stride(1) and (H == 1 or k_rows.stride(0) == v_rows.stride(0))
+    Q, d = q.shape
+    k = idx.shape[1]
+    dev = q.device
+    if scale is None:
+        scale = d ** -0.5
+    if out is None:
+        out = torch.empty((Q, d), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = alloc_workspace(workspace_bytes(FATHOM_OP_ATTEND, store, Q, k), dev)
+    kp = ctypes.c_void_p(k_ptr) if k_ptr is not None else _ptr(k_rows)
+    vp = ctypes.c_void_p(v_ptr) if v_ptr is not None else _ptr(v_rows)
+    stride_head = k_rows.stride(0) if H > 1 else k_rows.shape[1] * k_rows.stride(1)
+    st = lib.fathom_sparse_attention(kp, vp, stride_head, k_rows.stride(1), ctypes.byref(store), _ptr(q),
+                                     _ptr(idx), Q, group, k, float(scale), _ptr(out), _ptr(workspace),
+                                     workspace.numel(), _stream(stream))
+    _check(st, "fathom_sparse_attention")
+    return out
 
 
 def host_device_pointer(pinned: torch.Tensor) -> int:

@@ -132,6 +132,29 @@ def test_scan_validation():
     assert _scan(SD(2, 128, 1000, 36), ws_bytes=10) == fa.FATHOM_ERR_WORKSPACE
 
 
+def _attend(store=None, num_q=8, group=4, k=16, scale=0.088, stride_token=128, krows=FAKE, ws=FAKE,
+            ws_bytes=1 << 30):
+    store = store or SD(2, 128, 1000, 32)
+    return lib.fathom_sparse_attention(krows, FAKE, store.n * stride_token, stride_token, ctypes.byref(store),
+                                       FAKE, FAKE, num_q, group, k, ctypes.c_float(scale), FAKE, ws, ws_bytes, None)
+
+
+def test_attention_validation():
+    assert _attend(num_q=7) == fa.FATHOM_ERR_INVALID_ARG
+    assert _attend(k=0) == fa.FATHOM_ERR_INVALID_ARG
+    assert _attend(k=1001) == fa.FATHOM_ERR_INVALID_ARG
+    big = SD(1, 128, 10000, fa.plane_ldw(10000))
+    assert _attend(store=big, num_q=4, k=4097) == fa.FATHOM_ERR_UNSUPPORTED
+    assert _attend(scale=float("inf")) == fa.FATHOM_ERR_INVALID_ARG
+    assert _attend(stride_token=132) == fa.FATHOM_ERR_INVALID_ARG
+    assert _attend(stride_token=64) == fa.FATHOM_ERR_INVALID_ARG
+    assert _attend(krows=ctypes.c_void_p(0x1008)) == fa.FATHOM_ERR_INVALID_ARG
+    assert _attend(krows=None) == fa.FATHOM_ERR_INVALID_ARG
+    assert _attend(ws_bytes=16) == fa.FATHOM_ERR_WORKSPACE
+    assert _attend(store=SD(2, 256, 1000, 32)) == fa.FATHOM_ERR_UNSUPPORTED
+    assert fa.workspace_bytes(fa.FATHOM_OP_ATTEND, SD(8, 128, 1 << 20, 32768), 32, 2048) == 32 * 16 * 130 * 4
+
+
 def test_misc_validation():
     assert lib.fathom_host_device_pointer(None, None) == fa.FATHOM_ERR_INVALID_ARG
     assert lib.fathom_timing_read(None, None) == fa.FATHOM_ERR_INVALID_ARG

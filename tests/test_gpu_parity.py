@@ -327,6 +327,104 @@ def test_control_reads_through_the_scan(mode, budget):
         check_topk(idx[i], val[i], s_ref, k, n)
 
 
+def _bf16_rows(x_np):
+    """float32 [H, n, d] -> (bfloat16 device tensor, the same values as float64)."""
+    t = torch.from_numpy(np.ascontiguousarray(x_np)).to(DEV).to(torch.bfloat16)
+    return t, t.float().cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("n,H,group,k", [(3000, 1, 1, 1), (20000, 2, 4, 100), (20000, 2, 4, 128),
+                                         (50000, 2, 3, 300), (70000, 1, 4, 2048)])
+def test_sparse_attention_matches_oracle(n, H, group, k):
+    """Attention over each query's selected rows (bf16 K and V) matches the
+    oracle's float64 attention over the same rows."""
+    say("attention", n, H, group, k)
+    keys, q = synth.make_inputs(301 + n, H, n, H * group)
+    vals = np.stack([synth.head_values(301 + n, h, n) for h in range(H)])
+    kd, k64 = _bf16_rows(keys)
+    vd, v64 = _bf16_rows(vals)
+    store = fa.store_desc(H, n, 128)
+    rng = np.random.default_rng(k)
+    idx = np.stack([rng.choice(n, k, replace=False) for _ in range(H * group)]).astype(np.int32)
+    out = host(fa.sparse_attention(kd, vd, store, dev(q), dev(idx), group))
+    for i in range(H * group):
+        h = i // group
+        ref = O.sparse_attention(k64[h], v64[h], q[i], idx[i], 128 ** -0.5)
+        tol = 1e-4 * np.abs(v64[h][idx[i]]).max()
+        assert np.abs(out[i] - ref).max() <= tol, (i, np.abs(out[i] - ref).max(), tol)
+
+
+def test_sparse_attention_skips_out_of_range_rows():
+    say("attention out of range")
+    n, H, group, k = 5000, 1, 2, 200
+    keys, q = synth.make_inputs(7, H, n, H * group)
+    vals = np.stack([synth.head_values(7, 0, n)])
+    kd, k64 = _bf16_rows(keys)
+    vd, v64 = _bf16_rows(vals)
+    rng = np.random.default_rng(5)
+    idx = rng.choice(n, (H * group, k)).astype(np.int32)
+    idx[0, ::7] = -1
+    idx[1, 3::5] = n + 11
+    out = host(fa.sparse_attention(kd, vd, fa.store_desc(H, n, 128), dev(q), dev(idx), group))
+    for i in range(H * group):
+        ok = idx[i][(idx[i] >= 0) & (idx[i] < n)]
+        ref = O.sparse_attention(k64[0], v64[0], q[i], ok, 128 ** -0.5)
+        assert np.abs(out[i] - ref).max() <= 1e-4 * np.abs(v64[0][ok]).max()
+    idx[:] = -1
+    assert np.all(host(fa.sparse_attention(kd, vd, fa.store_desc(H, n, 128), dev(q), dev(idx), group)) == 0)
+
+
+def test_sparse_attention_host_rows_match_device():
+    """K and V rows read zero-copy from pinned host memory give the same
+    output as the HBM-resident rows."""
+    say("attention host rows")
+    n, H, group, k = 40000, 2, 4, 512
+    keys, q = synth.make_inputs(9, H, n, H * group)
+    vals = np.stack([synth.head_values(9, h, n) for h in range(H)])
+    kd, _ = _bf16_rows(keys)
+    vd, _ = _bf16_rows(vals)
+    store = fa.store_desc(H, n, 128)
+    idx = dev(np.stack([np.random.default_rng(i).choice(n, k, replace=False) for i in range(H * group)])
+              .astype(np.int32))
+    out_d = host(fa.sparse_attention(kd, vd, store, dev(q), idx, group))
+    kh = torch.empty(kd.shape, dtype=kd.dtype, pin_memory=True)
+    vh = torch.empty(vd.shape, dtype=vd.dtype, pin_memory=True)
+    kh.copy_(kd)
+    vh.copy_(vd)
+    torch.cuda.synchronize()
+    out_h = host(fa.sparse_attention(kd, vd, store, dev(q), idx, group,
+                                     k_ptr=fa.host_device_pointer(kh), v_ptr=fa.host_device_pointer(vh)))
+    assert np.array_equal(out_h, out_d)
+
+
+def test_decode_step_attention_error_below_random_selection():
+    """Whole decode step (pack, fused allocate + scan + top-k, attention over
+    the selected rows): its error against dense attention over all n keys is
+    below that of attending over k random keys, for every query."""
+    say("decode step attention error")
+    n, H, group, k, B = 131072, 1, 4, 1024, 92
+    keys, q = synth.make_inputs(41, H, n, H * group)
+    vals = np.stack([synth.head_values(41, 0, n)])
+    planes, lo, step, var = gpu_pack(keys)
+    store = fa.store_desc(H, n, 128)
+    qd = dev(q)
+    _, idx, _ = fa.allocate_scan_topk(planes, lo, step, var, store, qd, group, B, k)
+    kd, k64 = _bf16_rows(keys)
+    vd, v64 = _bf16_rows(vals)
+    out = host(fa.sparse_attention(kd, vd, store, qd, idx, group))
+    idx = host(idx)
+    rng = np.random.default_rng(0)
+    for i in range(H * group):
+        dense = O.attention(k64[0], v64[0], q[i], 128 ** -0.5)
+        ref = O.sparse_attention(k64[0], v64[0], q[i], idx[i], 128 ** -0.5)
+        assert np.abs(out[i] - ref).max() <= 1e-4 * np.abs(v64[0][idx[i]]).max()
+        err = O.attention_error(out[i], dense)
+        err_rand = O.attention_error(O.sparse_attention(k64[0], v64[0], q[i], rng.choice(n, k, replace=False),
+                                                        128 ** -0.5), dense)
+        print(f"query {i}: attention error top-{k} {err:.4f}, random {err_rand:.4f}")
+        assert err < err_rand
+
+
 def test_host_resident_store_matches_device():
     """The store read zero-copy from pinned host memory gives the same
     result as the HBM-resident store."""
