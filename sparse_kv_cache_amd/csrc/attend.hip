@@ -10,7 +10,8 @@
 //
 // Split form: the k selected rows of a query are cut into chunks of
 // kAttChunk; one workgroup per (chunk, query) gathers its K and V rows once
-// (K for the scores, V staged in LDS for the weighted sum) and writes the
+// (K for the scores, V staged in LDS for the weighted sum), 16 lanes per row
+// so that each load instruction reads whole 128-byte lines, and writes the
 // chunk's partial (max m_s, sum l_s, o_s); a second kernel combines the
 // chunks of each query: M = max_s m_s, o = sum_s e^(m_s - M) o_s /
 // sum_s e^(m_s - M) l_s.  All arithmetic is fp32.
@@ -22,13 +23,24 @@
 namespace fathom {
 namespace {
 
-constexpr int kAttThreads = 256;                   // two threads per selected row
-constexpr int kAttChunk = kAttThreads / 2;         // selected rows per workgroup
+constexpr int kAttThreads = 256;
 constexpr int kAttWaves = kAttThreads / 64;
-constexpr int kHalf = kD / 2;                      // channels per thread in the score
+constexpr int kAttChunk = 128;                     // selected rows per workgroup
+constexpr int kRowLanes = 16;                      // lanes per row: 16 bytes (8 channels) each
+constexpr int kRowsPerPass = 64 / kRowLanes;       // rows a wavefront loads per instruction
+constexpr int kPasses = kAttChunk / (kAttWaves * kRowsPerPass);
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Sum over the 16 lanes of a DPP row, returned to all of them.
+__device__ __forceinline__ float row_sum16(float v) {
+  v += __uint_as_float(dpp_u32<kDppXor1>(0u, __float_as_uint(v)));
+  v += __uint_as_float(dpp_u32<kDppXor2>(0u, __float_as_uint(v)));
+  v += __uint_as_float(dpp_u32<kDppRowHalfMirror>(0u, __float_as_uint(v)));
+  v += __uint_as_float(dpp_u32<kDppRowMirror>(0u, __float_as_uint(v)));
+  return v;
+}
 
 struct AttendArgs {
   const uint16_t* krows;   // bf16 rows: head h, key i at krows[h * stride_head + i * stride_token]
@@ -43,9 +55,12 @@ struct AttendArgs {
   float* out;              // [Q][kD]
 };
 
+// Workgroup = (chunk of kAttChunk selected rows, query).  Wavefront w loads
+// rows w * kRowsPerPass * kPasses + ...: per instruction, 4 rows of 16 lanes
+// each, a lane taking 16 bytes (8 channels) of a row, so every instruction
+// covers whole 128-byte lines.
 __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(AttendArgs a) {
-  __shared__ float qs[kD];
-  __shared__ uint32_t vs[kAttChunk][kHalf + 1];    // bf16 pairs; +1 word against bank conflicts
+  __shared__ uint4 vs[kAttChunk][kRowLanes + 1];   // staged V rows; +16 bytes against bank conflicts
   __shared__ float ps[kAttChunk];
   __shared__ float wred[kAttWaves][2];
   __shared__ float opart[kAttWaves][kD];
@@ -54,55 +69,64 @@ __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(AttendArgs 
   const int h = qi / a.group;
   const int i0 = split * kAttChunk;
   const int cnt = min(kAttChunk, a.topk - i0);
-  const int j = t >> 1, half = t & 1;              // row slot and channel half of this thread
-  // the selected row: index load, then both row loads in one round trip
-  const bool valid = j < cnt;
-  int64_t key = valid ? a.idx[int64_t(qi) * a.topk + i0 + j] : 0;
-  const bool in_range = valid && key >= 0 && key < a.n;
-  if (!in_range) key = 0;                          // (row 0 is read and ignored)
-  const int64_t row = int64_t(h) * a.stride_head + key * a.stride_token + half * kHalf;
-  const uint4* kr = reinterpret_cast<const uint4*>(a.krows + row);
-  const uint4* vr = reinterpret_cast<const uint4*>(a.vrows + row);
-  uint4 kw[8], vw[8];
+  const int piece = lane & (kRowLanes - 1), sub = lane / kRowLanes;
+  // this lane's 8 query channels, scaled
+  float qv[8];
+  {
+    const float4* qp = reinterpret_cast<const float4*>(a.q + int64_t(qi) * kD + 8 * piece);
+    const float4 q0 = qp[0], q1 = qp[1];
+    qv[0] = q0.x * a.scale; qv[1] = q0.y * a.scale; qv[2] = q0.z * a.scale; qv[3] = q0.w * a.scale;
+    qv[4] = q1.x * a.scale; qv[5] = q1.y * a.scale; qv[6] = q1.z * a.scale; qv[7] = q1.w * a.scale;
+  }
+  // the rows of this lane in each pass: indexes first, then all row loads
+  int slot[kPasses];
+  bool ok[kPasses];
+  uint4 kw[kPasses], vw[kPasses];
 #pragma unroll
-  for (int r = 0; r < 8; ++r) kw[r] = kr[r];
+  for (int p = 0; p < kPasses; ++p) {
+    slot[p] = (wave * kPasses + p) * kRowsPerPass + sub;
+    const int jj = min(slot[p], cnt - 1);
+    const int64_t key = a.idx[int64_t(qi) * a.topk + i0 + jj];
+    ok[p] = slot[p] < cnt && key >= 0 && key < a.n;
+    const int64_t row = int64_t(h) * a.stride_head + (ok[p] ? key : 0) * a.stride_token + 8 * piece;
+    kw[p] = *reinterpret_cast<const uint4*>(a.krows + row);
+    vw[p] = *reinterpret_cast<const uint4*>(a.vrows + row);
+  }
+  float sv[kPasses];
+  float m = -INFINITY;
 #pragma unroll
-  for (int r = 0; r < 8; ++r) vw[r] = vr[r];
-  if (t < kD) qs[t] = a.q[int64_t(qi) * kD + t] * a.scale;
-  __syncthreads();
-  float dot = 0.0f;
-#pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    const float* qp = &qs[half * kHalf + 8 * r];
-    const uint32_t w[4] = {kw[r].x, kw[r].y, kw[r].z, kw[r].w};
+  for (int p = 0; p < kPasses; ++p) {
+    const uint32_t w[4] = {kw[p].x, kw[p].y, kw[p].z, kw[p].w};
+    float dot = 0.0f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      dot = fmaf(bf16_lo(w[e]), qp[2 * e], dot);
-      dot = fmaf(bf16_hi(w[e]), qp[2 * e + 1], dot);
+      dot = fmaf(bf16_lo(w[e]), qv[2 * e], dot);
+      dot = fmaf(bf16_hi(w[e]), qv[2 * e + 1], dot);
     }
-    uint32_t* vd = &vs[j][half * (kHalf / 2) + 4 * r];
-    vd[0] = vw[r].x;
-    vd[1] = vw[r].y;
-    vd[2] = vw[r].z;
-    vd[3] = vw[r].w;
+    dot = row_sum16(dot);
+    sv[p] = ok[p] ? dot : -INFINITY;
+    m = fmaxf(m, sv[p]);
+    vs[slot[p]][piece] = vw[p];
   }
-  dot += __uint_as_float(dpp_u32<kDppXor1>(0u, __float_as_uint(dot)));   // the other half's channels
-  const float s = in_range ? dot : -INFINITY;
   // chunk maximum and the weights
-  float m = s;
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  for (int off = 16; off < 64; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
   if (lane == 0) wred[wave][0] = m;
   __syncthreads();
   m = wred[0][0];
 #pragma unroll
   for (int w = 1; w < kAttWaves; ++w) m = fmaxf(m, wred[w][0]);
-  // (a chunk always holds a valid row unless every index is out of range)
-  const float p = (in_range && half == 0) ? expf(s - m) : 0.0f;
-  if (half == 0) ps[j] = p;
-  float l = p;
+  float l = 0.0f;
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) l += __shfl_xor(l, off, 64);
+  for (int p = 0; p < kPasses; ++p) {
+    const float pr = ok[p] ? expf(sv[p] - m) : 0.0f;
+    if (piece == 0) {
+      ps[slot[p]] = pr;
+      l += pr;
+    }
+  }
+#pragma unroll
+  for (int off = 16; off < 64; off <<= 1) l += __shfl_xor(l, off, 64);
   if (lane == 0) wred[wave][1] = l;
   __syncthreads();
   // weighted sum of the staged V rows: wavefront w takes rows w, w + 4, ...;
@@ -110,7 +134,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(AttendArgs 
   float o0 = 0.0f, o1 = 0.0f;
   for (int r = wave; r < cnt; r += kAttWaves) {
     const float pr = ps[r];
-    const uint32_t vv = vs[r][lane];
+    const uint32_t vv = reinterpret_cast<const uint32_t*>(&vs[r][0])[lane];
     o0 = fmaf(pr, bf16_lo(vv), o0);
     o1 = fmaf(pr, bf16_hi(vv), o1);
   }
