@@ -124,6 +124,45 @@ def pack_planes(codes: np.ndarray, ldw: int) -> np.ndarray:
     return out
 
 
+def append_codes(keys_new: np.ndarray, lo: np.ndarray, step: np.ndarray) -> np.ndarray:
+    """Codes of keys appended to a packed head at decode time.
+
+    READING(Z18): a growing cache [Abs s1; Art para 1] keeps the quantizer
+    fixed at packing: r = fl32(16 step) (exact, step being r / 16),
+    inv = fl32(16 / r) (0 for r = 0), and the packer's code rule clamped to
+    [0, 15], since a new key may fall outside the packed range:
+        code = min(15, max(0, floor(fl32(fl32(K - lo) * inv)))).
+    keys_new float32 [m, d] -> codes uint8 [m, d].
+    """
+    keys_new = np.asarray(keys_new, dtype=np.float32)
+    assert keys_new.ndim == 2 and np.all(np.isfinite(keys_new)), "keys must be finite [m, d]"
+    lo = np.asarray(lo, dtype=np.float32)
+    r = (np.asarray(step, dtype=np.float32) * np.float32(LEVELS)).astype(np.float32)
+    inv = np.zeros_like(r)
+    pos = r > 0
+    inv[pos] = np.float32(LEVELS) / r[pos]
+    t = (keys_new - lo[None, :]).astype(np.float32)
+    u = (t * inv[None, :]).astype(np.float32)
+    code = np.clip(np.floor(u), 0.0, np.float32(LEVELS - 1))
+    return code.astype(np.uint8)
+
+
+def append_planes(planes: np.ndarray, n: int, codes_new: np.ndarray) -> np.ndarray:
+    """The head's planes with the codes of keys n .. n + m - 1 written in
+    (bits already there are replaced).  planes uint32 [d, 4, ldw]."""
+    planes = np.array(planes, dtype=np.uint32, copy=True)
+    codes_new = np.asarray(codes_new, dtype=np.uint8)
+    m, d = codes_new.shape
+    assert n + m <= planes.shape[2] * 32
+    for t in range(m):
+        w, b = divmod(n + t, 32)
+        for c in range(d):
+            for j in range(PLANES):
+                bit = (int(codes_new[t, c]) >> (PLANES - 1 - j)) & 1
+                planes[c, j, w] = (planes[c, j, w] & ~np.uint32(1 << b)) | np.uint32(bit << b)
+    return planes
+
+
 def unpack_plane_bits(planes: np.ndarray, n: int) -> np.ndarray:
     """Inverse view of ``pack_planes``: bits uint8 [d, 4, n]."""
     planes = np.ascontiguousarray(planes, dtype="<u4")
