@@ -100,6 +100,21 @@ int fathom_pack_planes(const float* keys, int64_t stride_head, int64_t stride_to
                        const fathom_store_desc* store, uint32_t* planes, float* lo, float* step,
                        float* var, void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/* Decode-time append ([Abs] s1; [Art] para 1: the cache grows by a token per
+ * step): keys n .. n + m - 1 of every head, with n = store->n the head's
+ * current length, are written into the planes of a store packed by
+ * fathom_pack_planes, under the head's packed quantizer: r = fl32(16 step),
+ * inv = fl32(16 / r) (0 if r = 0), code = min(15, max(0, floor(fl32(fl32(K -
+ * lo) * inv)))) -- the packer's rule, clamped since a new key may fall outside
+ * the packed range.  The bits of those keys are replaced; no other bit, and
+ * neither lo, step nor var, changes.  keys: float32, key n + t of head h at
+ * keys[h*stride_head + t*stride_token + c] (channel stride 1); 1 <= m and
+ * n + m <= 32 * store->ldw (the rows' capacity).  Afterwards the store holds
+ * n + m keys: pass n + m to the scan.  One kernel launch on hip_stream. */
+int fathom_append_keys(const float* keys, int64_t stride_head, int64_t stride_token, int32_t m,
+                       const fathom_store_desc* store, uint32_t* planes, const float* lo, const float* step,
+                       void* hip_stream);
+
 /* Per-query bit allocation by reverse water-filling ([Art] para 3; [Abs] s2,
  * s3).  q: float32 [num_q][d]; var: float32 [H][d] (any calibrated channel
  * variance, e.g. the packer's); budget_bits B in [0, 4d].

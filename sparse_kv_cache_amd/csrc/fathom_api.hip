@@ -215,6 +215,30 @@ int fathom_pack_planes(const float* keys, int64_t stride_head, int64_t stride_to
   return ok();
 }
 
+int fathom_append_keys(const float* keys, int64_t stride_head, int64_t stride_token, int32_t m,
+                       const fathom_store_desc* store, uint32_t* planes, const float* lo, const float* step,
+                       void* hip_stream) {
+  int st = check_store(store);
+  if (st != FATHOM_OK) return st;
+  if (!keys || !planes || !lo || !step) return fail(FATHOM_ERR_INVALID_ARG, "keys, planes, lo and step must be non-NULL");
+  if (m < 1) return fail(FATHOM_ERR_INVALID_ARG, "m must be >= 1");
+  if (store->n + m > store->ldw * 32)
+    return fail(FATHOM_ERR_INVALID_ARG, "n + m = %lld exceeds the rows' capacity %lld",
+                static_cast<long long>(store->n + m), static_cast<long long>(store->ldw * 32));
+  if (store->n + m > kMaxKeys)
+    return fail(FATHOM_ERR_UNSUPPORTED, "n + m = %lld above %lld", static_cast<long long>(store->n + m),
+                static_cast<long long>(kMaxKeys));
+  if (stride_token < kD) return fail(FATHOM_ERR_INVALID_ARG, "stride_token must be >= d");
+  if (store->num_kv_heads > 1 && stride_head < int64_t(m) * stride_token)
+    return fail(FATHOM_ERR_INVALID_ARG, "stride_head must be >= m * stride_token");
+  if (!aligned(keys, 4) || !aligned(planes, 16) || !aligned(lo, 4) || !aligned(step, 4))
+    return fail(FATHOM_ERR_INVALID_ARG, "keys, lo and step must be 4-byte aligned, planes 16-byte aligned");
+  hipError_t e = launch_append(keys, stride_head, stride_token, m, store->num_kv_heads, store->n, store->ldw,
+                               planes, lo, step, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return hip_fail(e, "fathom_append_keys launch");
+  return ok();
+}
+
 int fathom_allocate(const float* q, int32_t num_q, int32_t group, const float* var,
                     const fathom_store_desc* store, int32_t budget_bits, uint8_t* alloc,
                     void* hip_stream) {

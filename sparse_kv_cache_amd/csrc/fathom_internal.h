@@ -41,6 +41,9 @@ hipError_t launch_pack(const float* keys, int64_t stride_head, int64_t stride_to
                        int64_t ldw, uint32_t* planes, float* lo, float* step, float* var,
                        const PackWorkspace& ws, hipStream_t stream);
 
+hipError_t launch_append(const float* keys, int64_t stride_head, int64_t stride_token, int m, int H, int64_t n,
+                         int64_t ldw, uint32_t* planes, const float* lo, const float* step, hipStream_t stream);
+
 hipError_t launch_allocate(const float* q, int num_q, int group, const float* var, int budget,
                            uint8_t* alloc, hipStream_t stream);
 

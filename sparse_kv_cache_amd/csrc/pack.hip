@@ -227,7 +227,53 @@ __global__ void pack_final_kernel(int count, int64_t n, PackWorkspace ws, float*
   }
 }
 
+// Decode-time append: keys n .. n + m - 1 of every head are quantized with
+// the head's packed quantizer (lo, step fixed; inv = fl32(16 / fl32(16
+// step)), the packer's own inverse) and their codes, clamped to [0, 15],
+// written into the planes.  One thread per (head, channel, touched word)
+// builds the word's new bits for all four planes and replaces them
+// (read-modify-write; no other thread touches that word).
+__global__ __launch_bounds__(256) void append_kernel(const float* __restrict__ keys, int64_t stride_head,
+                                                     int64_t stride_token, int m, int64_t n, int64_t ldw,
+                                                     int64_t w0, int nw, int H, uint32_t* __restrict__ planes,
+                                                     const float* __restrict__ lo, const float* __restrict__ step) {
+  const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (gid >= int64_t(H) * kD * nw) return;
+  const int wi = static_cast<int>(gid % nw);
+  const int c = static_cast<int>((gid / nw) % kD);
+  const int h = static_cast<int>(gid / (int64_t(nw) * kD));
+  const int64_t w = w0 + wi;
+  const float l = lo[h * kD + c];
+  const float r = __fmul_rn(step[h * kD + c], 16.0f);   // exact power-of-two scaling
+  const float inv = r > 0.0f ? __fdiv_rn(16.0f, r) : 0.0f;
+  uint32_t mask = 0u, bits[kPlanes] = {0u, 0u, 0u, 0u};
+  const int64_t first = max(n, w * 32), last = min(n + m, w * 32 + 32);
+  for (int64_t i = first; i < last; ++i) {
+    const float x = keys[int64_t(h) * stride_head + (i - n) * stride_token + c];
+    const float u = __fmul_rn(__fsub_rn(x, l), inv);
+    const int code = static_cast<int>(fminf(fmaxf(floorf(u), 0.0f), 15.0f));
+    const uint32_t b = 1u << static_cast<int>(i & 31);
+    mask |= b;
+#pragma unroll
+    for (int j = 0; j < kPlanes; ++j) bits[j] |= ((code >> (kPlanes - 1 - j)) & 1) ? b : 0u;
+  }
+  uint32_t* row = planes + (int64_t(h) * kD + c) * kPlanes * ldw + w;
+#pragma unroll
+  for (int j = 0; j < kPlanes; ++j) row[j * ldw] = (row[j * ldw] & ~mask) | bits[j];
+}
+
 }  // namespace
+
+hipError_t launch_append(const float* keys, int64_t stride_head, int64_t stride_token, int m, int H, int64_t n,
+                         int64_t ldw, uint32_t* planes, const float* lo, const float* step, hipStream_t stream) {
+  const int64_t w0 = n / 32, w1 = (n + m - 1) / 32;
+  const int nw = static_cast<int>(w1 - w0 + 1);
+  const int64_t threads = int64_t(H) * kD * nw;
+  const int blocks = static_cast<int>((threads + 255) / 256);
+  hipLaunchKernelGGL(append_kernel, dim3(blocks), dim3(256), 0, stream, keys, stride_head, stride_token, m, n,
+                     ldw, w0, nw, H, planes, lo, step);
+  return hipGetLastError();
+}
 
 hipError_t launch_pack(const float* keys, int64_t stride_head, int64_t stride_token, int H, int64_t n,
                        int64_t ldw, uint32_t* planes, float* lo, float* step, float* var,

@@ -32,6 +32,7 @@ EXPORTS = (
     "fathom_plane_ldw",
     "fathom_workspace_bytes",
     "fathom_pack_planes",
+    "fathom_append_keys",
     "fathom_allocate",
     "fathom_control_allocate",
     "fathom_scan_topk",
@@ -74,6 +75,7 @@ def _load():
         "fathom_plane_ldw": (i64, [i64]),
         "fathom_workspace_bytes": (sz, [i32, SD, i32, i32]),
         "fathom_pack_planes": (ctypes.c_int, [P, i64, i64, SD, P, P, P, P, P, sz, P]),
+        "fathom_append_keys": (ctypes.c_int, [P, i64, i64, i32, SD, P, P, P, P]),
         "fathom_allocate": (ctypes.c_int, [P, i32, i32, P, SD, i32, P, P]),
         "fathom_control_allocate": (ctypes.c_int, [P, i32, i32, i32, P, P]),
         "fathom_scan_topk": (ctypes.c_int, [P, P, P, SD, P, P, i32, i32, i32, P, P, P, P, sz, P]),
@@ -151,6 +153,18 @@ def pack_planes(keys: torch.Tensor, store: Optional[StoreDesc] = None, *, with_v
                                 workspace.numel(), _stream(stream))
     _check(st, "fathom_pack_planes")
     return planes, lo, step, var
+
+
+def append_keys(keys: torch.Tensor, store: StoreDesc, planes: torch.Tensor, lo: torch.Tensor,
+                step: torch.Tensor, stream=None) -> StoreDesc:
+    """Write keys float32 [H, m, d] (token stride may exceed d) as keys
+    store.n .. store.n + m - 1 of every head; returns the store grown by m."""
+    assert keys.dtype == torch.float32 and keys.dim() == 3 and keys.stride(2) == 1
+    H, m, d = keys.shape
+    st = lib.fathom_append_keys(_ptr(keys), keys.stride(0), keys.stride(1), m, ctypes.byref(store), _ptr(planes),
+                                _ptr(lo), _ptr(step), _stream(stream))
+    _check(st, "fathom_append_keys")
+    return StoreDesc(store.num_kv_heads, store.d, store.n + m, store.ldw)
 
 
 def allocate(q: torch.Tensor, var: torch.Tensor, group: int, budget: int,

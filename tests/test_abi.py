@@ -155,6 +155,22 @@ def test_attention_validation():
     assert fa.workspace_bytes(fa.FATHOM_OP_ATTEND, SD(8, 128, 1 << 20, 32768), 32, 2048) == 32 * 16 * 130 * 4
 
 
+def _append(store=None, m=1, stride_token=128, keys=FAKE, planes=FAKE):
+    store = store or SD(2, 128, 1000, 32)
+    return lib.fathom_append_keys(keys, m * stride_token, stride_token, m, ctypes.byref(store), planes, FAKE, FAKE,
+                                  None)
+
+
+def test_append_validation():
+    assert _append(m=0) == fa.FATHOM_ERR_INVALID_ARG
+    assert _append(m=25) == fa.FATHOM_ERR_INVALID_ARG          # 1000 + 25 > 32 * 32 words
+    assert _append(stride_token=64) == fa.FATHOM_ERR_INVALID_ARG
+    assert _append(keys=None) == fa.FATHOM_ERR_INVALID_ARG
+    assert _append(planes=ctypes.c_void_p(0x1004)) == fa.FATHOM_ERR_INVALID_ARG
+    assert _append(store=SD(2, 256, 1000, 32)) == fa.FATHOM_ERR_UNSUPPORTED
+    assert "capacity" in (_append(m=25) and lib.fathom_last_error().decode())
+
+
 def test_misc_validation():
     assert lib.fathom_host_device_pointer(None, None) == fa.FATHOM_ERR_INVALID_ARG
     assert lib.fathom_timing_read(None, None) == fa.FATHOM_ERR_INVALID_ARG

@@ -327,6 +327,52 @@ def test_control_reads_through_the_scan(mode, budget):
         check_topk(idx[i], val[i], s_ref, k, n)
 
 
+def test_append_keys_then_scan():
+    """Decode-time appends (one token, then chunks crossing plane words) give
+    the oracle's planes bit for bit, and the scan over the grown store
+    matches the oracle's scores and top-k."""
+    say("append")
+    n0, H, group, B, k = 9000, 2, 4, 92, 200
+    chunks = [1, 7, 33, 100, 1]
+    total = n0 + sum(chunks)
+    keys, q = synth.make_inputs(77, H, total, H * group)
+    store = fa.store_desc(H, n0, 128, ldw=fa.plane_ldw(total))
+    planes = torch.zeros((H, 128, 4, store.ldw), dtype=torch.int32, device=DEV)
+    kd = dev(keys)
+    _, lo, step, var = fa.pack_planes(kd[:, :n0], store, planes=planes)
+    ref_planes, ref_codes = [], []
+    for h in range(H):
+        p_ref, lo_ref, st_ref, _, codes = O.pack_head(keys[h, :n0])
+        grown = np.zeros((128, 4, store.ldw), np.uint32)
+        grown[:, :, :p_ref.shape[2]] = p_ref
+        ref_planes.append((grown, lo_ref, st_ref))
+        ref_codes.append([codes])
+    n = n0
+    for m in chunks:
+        store = fa.append_keys(kd[:, n:n + m], store, planes, lo, step)
+        for h in range(H):
+            grown, lo_ref, st_ref = ref_planes[h]
+            new = O.append_codes(keys[h, n:n + m], lo_ref, st_ref)
+            ref_planes[h] = (O.append_planes(grown, n, new), lo_ref, st_ref)
+            ref_codes[h].append(new)
+        n += m
+        got = host(planes).view(np.uint32)
+        for h in range(H):
+            assert np.array_equal(got[h], ref_planes[h][0]), (m, h)
+    assert store.n == total
+    qd = dev(q)
+    alloc = fa.allocate(qd, var, group, B, store)
+    sc = torch.empty((H * group, total), dtype=torch.float32, device=DEV)
+    idx, val = fa.scan_topk(planes, lo, step, store, qd, alloc, group, k, all_scores=sc)
+    idx, val, sc, alloc = host(idx), host(val), host(sc), host(alloc)
+    for i in range(H * group):
+        _, lo_ref, st_ref = ref_planes[i // group]
+        codes = np.concatenate(ref_codes[i // group])
+        s_ref = oracle_scores(codes, lo_ref, st_ref, q[i], alloc[i])
+        check_scores(sc[i], s_ref)
+        check_topk(idx[i], val[i], s_ref, k, total)
+
+
 def _bf16_rows(x_np):
     """float32 [H, n, d] -> (bfloat16 device tensor, the same values as float64)."""
     t = torch.from_numpy(np.ascontiguousarray(x_np)).to(DEV).to(torch.bfloat16)
