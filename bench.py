@@ -102,6 +102,8 @@ def main():
                     help="leave the main-kernel timing events off (for traces of the bare step)")
     ap.add_argument("--control-steps", type=int, default=50,
                     help="steps per fixed-width control read (0: skip the controls)")
+    ap.add_argument("--host-steps", type=int, default=10,
+                    help="steps with the plane store in pinned host memory, read over PCIe (0: skip)")
     ap.add_argument("--attention-steps", type=int, default=50,
                     help="steps of attention over the selected rows (0: skip)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -236,6 +238,33 @@ def main():
             }
             log(f"control {name}: {c_ms * 1e3:.1f} us/step")
 
+    # the same step with the plane store in pinned host memory, read zero-copy
+    # over PCIe (after the timed region; never the headline value)
+    host_resident = None
+    if args.host_steps > 0:
+        pinned = torch.empty(planes0.shape, dtype=planes0.dtype, pin_memory=True)
+        pinned.copy_(planes0)
+        torch.cuda.synchronize()
+        hptr = fa.host_device_pointer(pinned)
+
+        def host_step():
+            fa.allocate_scan_topk(planes0, lo, step, var, store, qd, G, budget, k, workspace=scan_ws, alloc=alloc,
+                                  out_idx=out_idx, out_score=out_score, planes_ptr=hptr)
+        host_step()
+        torch.cuda.synchronize()
+        h0 = time.perf_counter()
+        for _ in range(args.host_steps):
+            host_step()
+        torch.cuda.synchronize()
+        h_ms = (time.perf_counter() - h0) * 1e3 / args.host_steps
+        host_resident = {
+            "ms_per_step": round(h_ms, 4),
+            "gkeys_per_s": round(H * n / (h_ms * 1e-3) / 1e9, 3),
+            "pcie_gbs": round(alg_plane_bytes / (h_ms * 1e-3) / 1e9, 1),
+        }
+        log(f"host-resident store: {h_ms * 1e3:.1f} us/step")
+        del pinned
+
     # attention over the rows the last step selected (after the timed region)
     attention = None
     if args.attention_steps > 0:
@@ -310,6 +339,7 @@ def main():
         "pack_ms": round(pack_ms, 3),
         "controls": controls,
         "attention": attention,
+        "host_resident": host_resident,
         "kernel_source": source_digest(),
     }
     print(json.dumps(rec), flush=True)
