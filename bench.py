@@ -111,7 +111,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported "
               "(the plane store shards by KV head or session with no exchange; see the design notes)",
               file=sys.stderr)
         return 2

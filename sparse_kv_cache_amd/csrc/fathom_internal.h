@@ -6,7 +6,7 @@
 
 namespace fathom {
 
-constexpr int kD = 128;            // channels supported by this build
+constexpr int kD = 128;            // channels per key (the only d supported)
 constexpr int kPlanes = 4;         // 4-bit K cache -> 4 bit planes
 constexpr int kMaxK = 4096;        // largest top-k
 constexpr size_t kChunkTableBytes = 12288;   // one (KV head, query chunk) scan table
