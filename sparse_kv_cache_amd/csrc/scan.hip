@@ -1278,6 +1278,10 @@ __global__ __launch_bounds__(kMainThreads) void scan_sample_kernel(ScanArgs a) {
 // The fast merge path keeps at most k - 1 + kBucketMax keys at the front of
 // the sort buffer; its digit tables live behind them.
 constexpr int kFastKept = 8192;
+// Workgroups per query in the merge: each repeats the load, histogram and
+// scan, then places only the output ranks [w k / kMergeSplit, (w + 1) k /
+// kMergeSplit); the general and fallback paths run in workgroup 0 alone.
+constexpr int kMergeSplit = 4;
 static_assert(kMaxK - 1 + kBucketMax <= kFastKept, "kept keys stay in front of the digit tables");
 static_assert(kFastKept * 8 + sizeof(DigitLds) <= kCandCap * 8, "digit tables fit in the sort buffer");
 
@@ -1399,7 +1403,11 @@ __global__ __launch_bounds__(kSelectThreads) void scan_merge_kernel(ScanArgs a, 
   __shared__ QueryLds qs;
   __shared__ uint32_t s_count[2];
   __shared__ uint32_t s_wave[kSelectWaves];
+  __shared__ uint32_t s_span[2];   // positions filled by this workgroup's scatter
   const int q = blockIdx.x;
+  const int part = blockIdx.y;
+  const uint32_t p_lo = static_cast<uint32_t>(int64_t(k) * part / kMergeSplit);
+  const uint32_t p_hi = static_cast<uint32_t>(int64_t(k) * (part + 1) / kMergeSplit);
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   static_assert(PT * kSelectThreads == kCandCap, "one register per candidate slot");
@@ -1472,16 +1480,35 @@ __global__ __launch_bounds__(kSelectThreads) void scan_merge_kernel(ScanArgs a, 
         __syncthreads();
         digit_scan(D, static_cast<uint32_t>(k) - 1u);
         if (D.big == 0u) {
+          // this workgroup scatters the buckets that overlap its output
+          // ranks [p_lo, p_hi); they fill positions [s_span[0], s_span[1])
           const uint32_t bstar = D.bstar;
-          const uint32_t nkeep = D.bstart + D.bcount;   // <= k - 1 + kBucketMax
+          if (tid == 0) {
+            s_span[0] = 0xffffffffu;
+            s_span[1] = 0u;
+          }
+          __syncthreads();
+          uint32_t lo_w = 0xffffffffu, hi_w = 0u;
 #pragma unroll
           for (int j = 0; j < PT; ++j) {
             const uint32_t d = (v[j] >> shift) & dmask;
-            if (j < nj && ((pm >> j) & 1u) && d >= bstar)
-              keys[D.start[d] + atomicAdd(&D.cursor[d], 1u)] = sort_key(v[j], id[j]);
+            if (j < nj && ((pm >> j) & 1u) && d >= bstar) {
+              const uint32_t b0 = D.start[d], b1 = b0 + D.hist[d];
+              if (b0 < p_hi && b1 > p_lo) {
+                keys[b0 + atomicAdd(&D.cursor[d], 1u)] = sort_key(v[j], id[j]);
+                lo_w = min(lo_w, b0);
+                hi_w = max(hi_w, b1);
+              }
+            }
+          }
+          const uint2 span = wave_max_min(hi_w, lo_w);
+          if (lane == 0 && span.x != 0u) {
+            atomicMin(&s_span[0], span.y);
+            atomicMax(&s_span[1], span.x);
           }
           __syncthreads();
-          for (uint32_t p = tid; p < nkeep; p += kSelectThreads) {
+          const uint32_t sp0 = s_span[0], sp1 = s_span[1];
+          for (uint32_t p = sp0 + tid; p < sp1; p += kSelectThreads) {
             const unsigned long long key = keys[p];
             const uint32_t d = (static_cast<uint32_t>(key >> 32) >> shift) & dmask;
             const uint32_t b0 = D.start[d], c = D.hist[d];
@@ -1494,7 +1521,7 @@ __global__ __launch_bounds__(kSelectThreads) void scan_merge_kernel(ScanArgs a, 
             }
             for (; i < c; ++i) rank += keys[b0 + i] > key ? 1u : 0u;
             const uint32_t pos = b0 + rank;
-            if (pos < static_cast<uint32_t>(k)) {
+            if (pos >= p_lo && pos < p_hi) {
               out_idx[int64_t(q) * k + pos] = static_cast<int32_t>(~static_cast<uint32_t>(key));
               out_score[int64_t(q) * k + pos] = ordered_to_float(static_cast<uint32_t>(key >> 32));
             }
@@ -1502,7 +1529,7 @@ __global__ __launch_bounds__(kSelectThreads) void scan_merge_kernel(ScanArgs a, 
           placed = true;
         }
       }
-      if (placed) return;
+      if (placed || part != 0) return;   // uniform
       // General path (all scores equal, or a bucket too large to order by
       // counting): the k-th best candidate score by radix select; every
       // candidate at or above it is kept and sorted.
@@ -1525,6 +1552,7 @@ __global__ __launch_bounds__(kSelectThreads) void scan_merge_kernel(ScanArgs a, 
     }
   }
   if (!fast) {
+    if (part != 0) return;   // uniform
     // (the early loads are consumed on this path too, so the compiler keeps
     // them ahead of the count test instead of sinking them into the fast path)
 #pragma unroll
@@ -1707,7 +1735,7 @@ hipError_t launch_scan_topk(const uint32_t* planes, const float* lo, const float
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(scan_merge_kernel, dim3(num_q), dim3(kSelectThreads), 0, stream, a, k, out_idx,
+  hipLaunchKernelGGL(scan_merge_kernel, dim3(num_q, kMergeSplit), dim3(kSelectThreads), 0, stream, a, k, out_idx,
                      out_score);
   return hipGetLastError();
 }
