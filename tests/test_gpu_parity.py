@@ -542,3 +542,40 @@ def test_qwen3_8b_1m_full_size():
         l, s, _, codes = heads[i // G]
         s_ref = oracle_scores(codes, l, s, q[i], alloc_ref[i])
         check_topk(idx[i], val[i], s_ref, w.k, n)
+
+
+def test_multi_session_full_size():
+    """The many-session shape at full size (128 KV heads = 16 sessions x 8
+    heads, 131,072 keys each, 512 query heads, k = 1024), through the fused
+    call; three heads are checked against the oracle end to end."""
+    w = synth.WORKLOADS["multi_session"]
+    H, n, G, Q = w.num_kv_heads, w.n, w.group, w.num_q
+    say("multi_session", H, n, Q, w.k)
+    check = (0, 77, 127)
+    keys_d = torch.empty((H, n, 128), dtype=torch.float32, device=DEV)
+    kept, q = {}, None
+    for kind, *rest in synth.stream_inputs(w.seed, H, n, Q):
+        if kind == "head":
+            h, kh = rest
+            keys_d[h].copy_(torch.from_numpy(kh))
+            if h in check:
+                kept[h] = kh
+        else:
+            q = rest[0]
+    store = fa.store_desc(H, n, 128)
+    planes, lo, step, var = fa.pack_planes(keys_d, store)
+    del keys_d
+    torch.cuda.empty_cache()
+    alloc, idx, val = fa.allocate_scan_topk(planes, lo, step, var, store, dev(q), G, 92, w.k)
+    alloc, idx, val = host(alloc), host(idx), host(val)
+    planes_h = host(planes).view(np.uint32)
+    for h in check:
+        p_ref, lo_ref, st_ref, var_ref, codes = O.pack_head(kept[h])
+        assert np.array_equal(planes_h[h], p_ref), h
+        assert np.array_equal(host(var[h]), var_ref), h
+        for g in range(G):
+            i = h * G + g
+            assert np.array_equal(alloc[i], O.allocate(q[i], var_ref, 92)), i
+            s_ref = oracle_scores(codes, lo_ref, st_ref, q[i], alloc[i])
+            check_topk(idx[i], val[i], s_ref, w.k, n)
+
