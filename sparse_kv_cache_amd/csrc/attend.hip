@@ -157,17 +157,30 @@ __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(AttendArgs 
   }
 }
 
+// (every partial of the query loads at once: the loop over chunks is
+// unrolled to its bound, kMaxK / kAttChunk)
+constexpr int kMaxSplits = kMaxK / kAttChunk;
+
 __global__ __launch_bounds__(kD) void attend_combine_kernel(AttendArgs a) {
   const int qi = blockIdx.x, c = threadIdx.x;
   const float* src = a.part + int64_t(qi) * a.nsplit * (kD + 2);
+  float ov[kMaxSplits], mv[kMaxSplits], lv[kMaxSplits];
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s) {
+    const int ss = min(s, a.nsplit - 1);   // (re-reads the last chunk; weighted 0 below)
+    ov[s] = src[ss * (kD + 2) + c];
+    mv[s] = src[ss * (kD + 2) + kD];
+    lv[s] = src[ss * (kD + 2) + kD + 1];
+  }
   float M = -INFINITY;
-  for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, src[s * (kD + 2) + kD]);
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s) M = s < a.nsplit ? fmaxf(M, mv[s]) : M;
   float o = 0.0f, L = 0.0f;
-  for (int s = 0; s < a.nsplit; ++s) {
-    const float ms = src[s * (kD + 2) + kD];
-    const float w = ms == -INFINITY ? 0.0f : expf(ms - M);
-    o = fmaf(w, src[s * (kD + 2) + c], o);
-    L = fmaf(w, src[s * (kD + 2) + kD + 1], L);
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s) {
+    const float w = (s < a.nsplit && mv[s] != -INFINITY) ? expf(mv[s] - M) : 0.0f;
+    o = fmaf(w, ov[s], o);
+    L = fmaf(w, lv[s], L);
   }
   a.out[int64_t(qi) * kD + c] = L > 0.0f ? o / L : 0.0f;
 }

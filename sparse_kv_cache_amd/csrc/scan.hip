@@ -43,6 +43,7 @@
 
 #include <hip/hip_ext.h>
 
+#include <algorithm>
 #include <climits>
 #include <type_traits>
 
@@ -94,7 +95,11 @@ constexpr int kStageDwords = 8 * kDmaDwords;
 #define WAVE_CAND 32
 #endif
 constexpr int kWaveCand = WAVE_CAND;           // candidates per (wave, query) buffered in LDS
-constexpr int kTopR = 64;                      // largest sample rank served by per-block lane maxima
+// Largest sample rank served by per-block group maxima: up to half the
+// lanes, so that the rank-th largest lane maximum usually leaves at most 64
+// candidates for the sort (nearer 64 the selection falls back to a search).
+constexpr int kTopR = 32;
+constexpr int kListEntries = 512;              // group maxima kept per query (all sampled blocks)
 constexpr int kSelectThreads = 1024;
 constexpr int kSelectWaves = kSelectThreads / 64;
 
@@ -122,7 +127,7 @@ struct ScanArgs {
   float* all_scores;
   int sample_stride;  // distance between sampled blocks, in 1024-key blocks
   int rsel;           // sample rank of the threshold
-  int top_lists;      // rsel <= kTopR: sampled blocks store their lane maxima only,
+  int top_lists;      // rsel <= kTopR: sampled blocks store their group maxima only,
                       //   and the main kernel selects theta from them
   int nsb;            // sampled blocks per head
   int chunks_per_head;
@@ -629,15 +634,18 @@ __global__ __launch_bounds__(kSelectThreads) void scan_threshold_kernel(
   }
 }
 
-// ------------------------------------------------ per-block lane maxima
+// ------------------------------------------------ per-block group maxima
 // For rsel <= kTopR the sample kernel stores, per sampled block and query,
-// only the maxima of the 64 groups of 16 keys that one lane scores (as
-// ordered keys, in the block's slot of kTopR words at the front of the
-// query's sample row).  The rsel-th largest of these maxima never exceeds
-// the rsel-th largest sampled score and, while the best rsel scores fall in
-// distinct groups, equals it; the threshold then selects from at most
-// kSampleMaxBlocks * 64 values instead of the whole sample.
-static_assert(kTopR * 16 == kTileWords * 32, "a block's list holds one maximum per 16 keys");
+// only the maxima of groups of gs keys scored by one lane (gs = 16 with 5 to
+// 8 sampled blocks, 8 with 3 or 4, 4 with 2, 2 with 1, so that the blocks
+// together keep at most kListEntries maxima), as ordered keys at the front
+// of the query's sample row, block b at b * (1024 / gs).  The rsel-th
+// largest of these maxima never exceeds the rsel-th largest sampled score
+// and, while the best rsel scores fall in distinct groups, equals it; the
+// threshold then selects from at most kListEntries values instead of the
+// whole sample.
+__host__ __device__ inline int group_keys(int nsb) { return nsb > 4 ? 16 : nsb > 2 ? 8 : nsb > 1 ? 4 : 2; }
+static_assert(kSampleMaxBlocks * (kSampleBlockKeys / 16) <= kListEntries, "the group maxima fit the list");
 
 
 // r-th largest (1 <= r <= number of values) of the ordered keys v[m] of the
@@ -1008,11 +1016,13 @@ __global__ __launch_bounds__(kMainThreads, kMainWgPerCu * kMainWaves / 4) void s
   // With per-block lists, wavefront g selects theta of query q0 + g itself
   // (every workgroup of the chunk gets the same value): its lanes load entry
   // `lane` of each sampled block's list together with the table.
-  uint32_t lv[kSampleMaxBlocks];
+  constexpr int kLv = kListEntries / 64;
+  uint32_t lv[kLv];
   if (a.top_lists && wave < GQ) {   // uniform
     const uint32_t* row = reinterpret_cast<const uint32_t*>(a.sample) + int64_t(q0 + wave) * kSampleMaxKeys;
+    const int entries = a.nsb * (kSampleBlockKeys / group_keys(a.nsb));
 #pragma unroll
-    for (int m = 0; m < kSampleMaxBlocks; ++m) lv[m] = m < a.nsb ? row[m * kTopR + lane] : 0u;
+    for (int m = 0; m < kLv; ++m) lv[m] = m * 64 + lane < entries ? row[m * 64 + lane] : 0u;
   }
   {
     // (read unconditionally, with the table, and used only without lists)
@@ -1041,7 +1051,7 @@ __global__ __launch_bounds__(kMainThreads, kMainWgPerCu * kMainWaves / 4) void s
   if (a.top_lists) {   // uniform
     if (wave < GQ) {
       const float th = ordered_to_float(
-          wave_rth_largest<kSampleMaxBlocks>(lv, static_cast<uint32_t>(a.rsel), reinterpret_cast<uint32_t*>(&cbuf[wave][0][0])));
+          wave_rth_largest<kLv>(lv, static_cast<uint32_t>(a.rsel), reinterpret_cast<uint32_t*>(&cbuf[wave][0][0])));
       if (lane == 0) theta_s[wave] = th;   // (workgroup 0 stores it at the end)
     }
     lds_barrier();
@@ -1242,7 +1252,7 @@ __global__ __launch_bounds__(kMainThreads) void scan_sample_kernel(ScanArgs a) {
     int tv[kWaveKeys];
     limb_sums(acc, tv);
     const float sigma = T.sigma[G], Cq = T.C[G];
-    uint32_t mx = 0u;
+    uint32_t ok[kWaveKeys];
 #pragma unroll
     for (int i = 0; i < kWaveKeys; ++i) {
       const int64_t key = column_key(tile_, wave, col, i >> 3) + (i & 7);
@@ -1250,18 +1260,38 @@ __global__ __launch_bounds__(kMainThreads) void scan_sample_kernel(ScanArgs a) {
       const float sc = fmaf(static_cast<float>(t), sigma, Cq);
       const int local = static_cast<int>(key - int64_t(tile_) * kTileWords * 32);
       const float score = key < a.n ? sc : -INFINITY;
-      mx = max(mx, float_to_ordered(score));
+      ok[i] = float_to_ordered(score);
       if (!a.top_lists) a.sample[int64_t(q0 + G) * kSampleMaxKeys + sbi * kSampleBlockKeys + local] = score;
     }
-    // one maximum per 16 keys: a lane's own, or (8 keys per lane) those of
-    // two neighbouring columns
     if (a.top_lists) {
-      uint32_t* list = reinterpret_cast<uint32_t*>(a.sample) + int64_t(q0 + G) * kSampleMaxKeys + sbi * kTopR;
-      if constexpr (kWaveKeys == 16) {
-        list[wave * 16 + col] = mx;
+      // maxima of the lane's keys in groups of 2, 4, 8 and 16 (the last
+      // across two lanes when a lane scores 8 keys); the group size is
+      // uniform
+      const int gs = group_keys(a.nsb);
+      uint32_t* list = reinterpret_cast<uint32_t*>(a.sample) + int64_t(q0 + G) * kSampleMaxKeys +
+                       sbi * (kSampleBlockKeys / gs);
+      uint32_t m2[kWaveKeys / 2], m4[kWaveKeys / 4], m8[kWaveKeys / 8];
+#pragma unroll
+      for (int g = 0; g < kWaveKeys / 2; ++g) m2[g] = max(ok[2 * g], ok[2 * g + 1]);
+#pragma unroll
+      for (int g = 0; g < kWaveKeys / 4; ++g) m4[g] = max(m2[2 * g], m2[2 * g + 1]);
+#pragma unroll
+      for (int g = 0; g < kWaveKeys / 8; ++g) m8[g] = max(m4[2 * g], m4[2 * g + 1]);
+      const int lane_slot = wave * 16 + col;   // the lane's place among the block's lanes
+      if (gs == 2) {
+#pragma unroll
+        for (int g = 0; g < kWaveKeys / 2; ++g) list[lane_slot * (kWaveKeys / 2) + g] = m2[g];
+      } else if (gs == 4) {
+#pragma unroll
+        for (int g = 0; g < kWaveKeys / 4; ++g) list[lane_slot * (kWaveKeys / 4) + g] = m4[g];
+      } else if (gs == 8) {
+#pragma unroll
+        for (int g = 0; g < kWaveKeys / 8; ++g) list[lane_slot * (kWaveKeys / 8) + g] = m8[g];
+      } else if constexpr (kWaveKeys == 16) {
+        list[lane_slot] = max(m8[0], m8[1]);
       } else {
-        mx = max(mx, dpp_u32<kDppXor1>(mx, mx));
-        if ((col & 1) == 0) list[wave * 8 + (col >> 1)] = mx;
+        const uint32_t m16 = max(m8[0], dpp_u32<kDppXor1>(m8[0], m8[0]));
+        if ((col & 1) == 0) list[wave * 8 + (col >> 1)] = m16;
       }
     }
   });
@@ -1278,9 +1308,10 @@ __global__ __launch_bounds__(kMainThreads) void scan_sample_kernel(ScanArgs a) {
 // The fast merge path keeps at most k - 1 + kBucketMax keys at the front of
 // the sort buffer; its digit tables live behind them.
 constexpr int kFastKept = 8192;
-// Workgroups per query in the merge: each repeats the load, histogram and
-// scan, then places only the output ranks [w k / kMergeSplit, (w + 1) k /
-// kMergeSplit); the general and fallback paths run in workgroup 0 alone.
+// Workgroups per query in the merge (up to kMergeSplit, fewer with many
+// queries: each repeats the load, histogram and scan): workgroup w places
+// only the output ranks [w k / W, (w + 1) k / W); the general and fallback
+// paths run in workgroup 0 alone.
 constexpr int kMergeSplit = 4;
 static_assert(kMaxK - 1 + kBucketMax <= kFastKept, "kept keys stay in front of the digit tables");
 static_assert(kFastKept * 8 + sizeof(DigitLds) <= kCandCap * 8, "digit tables fit in the sort buffer");
@@ -1406,8 +1437,9 @@ __global__ __launch_bounds__(kSelectThreads) void scan_merge_kernel(ScanArgs a, 
   __shared__ uint32_t s_span[2];   // positions filled by this workgroup's scatter
   const int q = blockIdx.x;
   const int part = blockIdx.y;
-  const uint32_t p_lo = static_cast<uint32_t>(int64_t(k) * part / kMergeSplit);
-  const uint32_t p_hi = static_cast<uint32_t>(int64_t(k) * (part + 1) / kMergeSplit);
+  const int parts = static_cast<int>(gridDim.y);
+  const uint32_t p_lo = static_cast<uint32_t>(int64_t(k) * part / parts);
+  const uint32_t p_hi = static_cast<uint32_t>(int64_t(k) * (part + 1) / parts);
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   static_assert(PT * kSelectThreads == kCandCap, "one register per candidate slot");
@@ -1679,9 +1711,17 @@ hipError_t launch_scan_topk(const uint32_t* planes, const float* lo, const float
   a.tables = ws.tables;
   a.all_scores = all_scores;
 
-  // sampled blocks: up to 8 blocks of 1024 keys spread evenly over the head
+  const int full = group / kQueryChunk;
+  const int rest = group % kQueryChunk;
+  a.chunks_per_head = full + (rest > 0 ? 1 : 0);
+  const int64_t chunk_count = int64_t(H) * a.chunks_per_head;
+
+  // sampled blocks: up to 8 blocks of 1024 keys spread evenly over the head;
+  // with many (head, chunk) pairs fewer, so that the sample kernel stays
+  // near 512 workgroups (one pass over the GPU) -- at least 2
   const int64_t nblocks = (n + kSampleBlockKeys - 1) / kSampleBlockKeys;
-  const int nsb = static_cast<int>(nblocks < kSampleMaxBlocks ? nblocks : kSampleMaxBlocks);
+  const int64_t blocks_cap = std::max<int64_t>(2, std::min<int64_t>(kSampleMaxBlocks, 512 / chunk_count));
+  const int nsb = static_cast<int>(std::min(nblocks, blocks_cap));
   const int64_t stride = nblocks / nsb;
   a.sample_stride = static_cast<int>(stride);
   int64_t svalid = 0;
@@ -1702,10 +1742,6 @@ hipError_t launch_scan_topk(const uint32_t* planes, const float* lo, const float
 
   // main-kernel work split: kMainWgPerCu resident workgroups per CU, each
   // taking a contiguous run of tiles of one (head, query chunk)
-  const int full = group / kQueryChunk;
-  const int rest = group % kQueryChunk;
-  a.chunks_per_head = full + (rest > 0 ? 1 : 0);
-  const int64_t chunk_count = int64_t(H) * a.chunks_per_head;
   const int64_t total_tiles = chunk_count * a.tiles;
   const int64_t target_wgs = 256 * kMainWgPerCu;
   a.tiles_per_wg = static_cast<int>((total_tiles + target_wgs - 1) / target_wgs);
@@ -1735,7 +1771,8 @@ hipError_t launch_scan_topk(const uint32_t* planes, const float* lo, const float
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(scan_merge_kernel, dim3(num_q, kMergeSplit), dim3(kSelectThreads), 0, stream, a, k, out_idx,
+  const int merge_parts = std::max(1, std::min(kMergeSplit, 256 / std::max(1, num_q)));
+  hipLaunchKernelGGL(scan_merge_kernel, dim3(num_q, merge_parts), dim3(kSelectThreads), 0, stream, a, k, out_idx,
                      out_score);
   return hipGetLastError();
 }
