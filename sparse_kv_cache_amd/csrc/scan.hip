@@ -1118,16 +1118,19 @@ __global__ __launch_bounds__(kMainThreads, kMainWgPerCu * kMainWaves / 4) void s
     const uint32_t cap = static_cast<uint32_t>(kWaveCand);
     const uint32_t spill = slot0 + mine > cap ? slot0 + mine - max(slot0, cap) : 0u;
     uint32_t gpos = 0;
-    if (__ballot(spill != 0) != 0) {   // uniform; rare
+    if (__ballot(spill != 0) != 0) {   // uniform
+      // the last lane of each query's row reserves the row's spilled slots:
+      // one atomic per query, all in flight together
       const uint32_t sincl = row_incl_sum(spill);
+      uint32_t gb = 0;
+      if (col == 15 && qvalid && sincl != 0) gb = atomicAdd(&a.count[q0 + G], sincl);
+      uint32_t rb = 0;
 #pragma unroll
       for (int g = 0; g < GQ; ++g) {
-        const uint32_t total = read_lane(sincl, 16 * g + 15);
-        uint32_t gb = 0;
-        if (lane == 0 && total != 0) gb = atomicAdd(&a.count[q0 + g], total);
-        gb = read_lane(gb, 0);
-        gpos = G == g ? gb + sincl - spill : gpos;
+        const uint32_t b = read_lane(gb, 16 * g + 15);
+        rb = G == g ? b : rb;
       }
+      gpos = rb + sincl - spill;
     }
     if (bits != 0) {
       // Lanes pass few keys: walk the set bits only.  The key's t is picked
