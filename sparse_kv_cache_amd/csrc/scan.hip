@@ -930,6 +930,23 @@ struct TileScanner {
   __device__ void run(Epi&& epi) {
     int step_i = 0, slot = 0;
     for (int ti = 0, tile = first_tile; ti < ntiles; ++ti, tile += tile_stride) {
+      // Issue priority falls in four steps over the run.  The workgroups
+      // sharing a CU start together; with equal priority the oldest wins
+      // arbitration and the youngest ends up scanning alone at the end, at
+      // a fraction of the CU's throughput.  Falling priority lets the ones
+      // behind catch up, so they finish close together.
+      {
+        const int level = (4 * ti) / ntiles;   // uniform
+        if (level == 0) {
+          __builtin_amdgcn_s_setprio(3);
+        } else if (level == 1) {
+          __builtin_amdgcn_s_setprio(2);
+        } else if (level == 2) {
+          __builtin_amdgcn_s_setprio(1);
+        } else {
+          __builtin_amdgcn_s_setprio(0);
+        }
+      }
       v4i acc[kWaveKeys];
       auto step = [&](auto first, int b) {
         // the last steps have fewer loads behind them: wait for all
