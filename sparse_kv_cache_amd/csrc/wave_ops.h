@@ -8,8 +8,9 @@
 
 namespace fathom {
 
-// Cross-lane steps use DPP (operand routing inside the VALU instruction)
-// rather than ds_bpermute, whose LDS round trip is ~100 cycles per step.
+// Cross-lane steps use DPP (operand routing inside the VALU instruction) and
+// lane swaps rather than ds_bpermute, whose LDS round trip is ~100 cycles per
+// step and queues behind the scan's LDS traffic.
 // GFX9 DPP controls: quad_perm, row_shr:n, row_mirror, row_half_mirror,
 // row_bcast:15 / row_bcast:31 (rows are 16 lanes).
 constexpr int kDppXor1 = 0xB1;          // quad_perm [1,0,3,2]
@@ -28,7 +29,10 @@ __device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t v) {
                                                            RowMask, 0xf, false));
 }
 
-// v of lane (lane ^ J): DPP for J < 16, lane shuffle otherwise.
+// v of lane (lane ^ J): DPP for J < 16; for 16 and 32 the gfx950 lane swaps
+// (v_permlane16_swap / v_permlane32_swap: with v in both operands, the first
+// result holds each pair's lower half of v in both halves of the pair, the
+// second its upper half), which stay in the VALU.
 template <int J>
 __device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
   if constexpr (J == 1) {
@@ -41,8 +45,13 @@ __device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
     return (threadIdx.x & 4) ? dn : up;
   } else if constexpr (J == 8) {
     return dpp_u32<kDppRowRor + 8>(v, v);               // rotation by half a row
+  } else if constexpr (J == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (threadIdx.x & 16) ? r[0] : r[1];
   } else {
-    return static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), J, 64));
+    static_assert(J == 32, "xor distances 1 .. 32");
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (threadIdx.x & 32) ? r[0] : r[1];
   }
 }
 
