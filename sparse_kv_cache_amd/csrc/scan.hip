@@ -1760,10 +1760,14 @@ hipError_t launch_scan_topk(const uint32_t* planes, const float* lo, const float
   a.top_lists = rsel <= kTopR ? 1 : 0;
   a.nsb = nsb;
 
-  // main-kernel work split: kMainWgPerCu resident workgroups per CU, each
-  // taking a contiguous run of tiles of one (head, query chunk)
+  // main-kernel work split: each workgroup takes a contiguous run of tiles
+  // of one (head, query chunk).  With per-block lists every workgroup first
+  // selects theta itself, so the tiles go to one generation of resident
+  // workgroups (kMainWgPerCu per CU); with theta from the threshold kernel
+  // the start is cheap and four generations of shorter runs balance better
+  // (workgroups that finish early are replaced by new ones).
   const int64_t total_tiles = chunk_count * a.tiles;
-  const int64_t target_wgs = 256 * kMainWgPerCu;
+  const int64_t target_wgs = int64_t(a.top_lists ? 1 : 4) * 256 * kMainWgPerCu;
   a.tiles_per_wg = static_cast<int>((total_tiles + target_wgs - 1) / target_wgs);
   if (a.tiles_per_wg < 1) a.tiles_per_wg = 1;
 
