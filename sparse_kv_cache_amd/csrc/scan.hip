@@ -930,13 +930,14 @@ struct TileScanner {
   __device__ void run(Epi&& epi) {
     int step_i = 0, slot = 0;
     for (int ti = 0, tile = first_tile; ti < ntiles; ++ti, tile += tile_stride) {
-      // Issue priority falls in four steps over the run.  The workgroups
-      // sharing a CU start together; with equal priority the oldest wins
-      // arbitration and the youngest ends up scanning alone at the end, at
-      // a fraction of the CU's throughput.  Falling priority lets the ones
-      // behind catch up, so they finish close together.
+      // Issue priority falls over the last tiles of the run (3 until four
+      // remain, then one step per tile).  The workgroups sharing a CU start
+      // together; with equal priority the oldest wins arbitration and the
+      // youngest ends up scanning alone at the end, at a fraction of the
+      // CU's throughput.  Falling priority lets the ones behind catch up, so
+      // they finish close together.
       {
-        const int level = (4 * ti) / ntiles;   // uniform
+        const int level = min(3, max(0, ti - (ntiles - 4)));   // uniform
         if (level == 0) {
           __builtin_amdgcn_s_setprio(3);
         } else if (level == 1) {
