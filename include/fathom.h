@@ -169,9 +169,6 @@ int fathom_allocate_scan_topk(const uint32_t* planes, const float* lo, const flo
                               int32_t budget_bits, int32_t k, uint8_t* alloc, int32_t* out_idx,
                               float* out_score, void* workspace, size_t workspace_bytes, void* hip_stream);
 
-/* Device-visible address of pinned host memory (allocated with hipHostMalloc
- * or torch pin_memory), for a plane store kept in host RAM ([Art] para 1;
- * [Abs] s1: the index lives in host memory).  Not for registered memory. */
 /* Attention over the selected keys: the decode step after the top-k scan
  * ([Abs] title and s1; [Art] findings bullet 2 for its error measure).  For
  * query q (KV head h = q / group) and its k selected rows i = idx[q][0..k):
@@ -191,6 +188,9 @@ int fathom_sparse_attention(const uint16_t* k_rows, const uint16_t* v_rows, int6
                             const int32_t* idx, int32_t num_q, int32_t group, int32_t k, float scale,
                             float* out, void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/* Device-visible address of pinned host memory (allocated with hipHostMalloc
+ * or torch pin_memory), for a plane store kept in host RAM ([Art] para 1;
+ * [Abs] s1: the index lives in host memory).  Not for registered memory. */
 int fathom_host_device_pointer(void* pinned_host, void** device_ptr);
 
 /* Static text for a status code. */
