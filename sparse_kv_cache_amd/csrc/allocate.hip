@@ -11,11 +11,12 @@ constexpr int kWavesPerBlock = 4;
 __global__ __launch_bounds__(kWavesPerBlock * 64) void allocate_kernel(
     const float* __restrict__ q, int num_q, int group, const float* __restrict__ var, int budget,
     uint8_t* __restrict__ alloc) {
+  __shared__ uint32_t scratch[kWavesPerBlock][64];   // per wavefront, for the rank selection
   const int lane = threadIdx.x & 63;
   const int qi = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
   if (qi >= num_q) return;                 // uniform per wavefront
   const int h = qi / group;
-  const uint2 b = allocate_query_wave(q + int64_t(qi) * kD, var + int64_t(h) * kD, budget);
+  const uint2 b = allocate_query_wave(q + int64_t(qi) * kD, var + int64_t(h) * kD, budget, &scratch[threadIdx.x >> 6][0]);
   const uint16_t pair = static_cast<uint16_t>(b.x | (b.y << 8));
   *reinterpret_cast<uint16_t*>(alloc + int64_t(qi) * kD + 2 * lane) = pair;
 }

@@ -13,7 +13,9 @@
 // the B-th largest ordering key bits(w_c) - j 2^24, channel c takes every
 // plane whose key exceeds theta, and the candidates equal to theta (at most
 // one per channel) are filled in ascending channel order until sum b_c = B.
-// theta is found by a search on the int32 key with wavefront counts.
+// theta is found in two stages: a search on the key's top byte with
+// wavefront counts, then a rank selection on the low 24 bits of the channels
+// whose count still changes inside that byte.
 #ifndef FATHOM_ALLOCATE_WAVE_H
 #define FATHOM_ALLOCATE_WAVE_H
 
@@ -45,13 +47,57 @@ __device__ inline int lanes_below(uint64_t mask) {
   return __popcll(mask & below);
 }
 
+// r-th largest (1 <= r <= 64, r <= number of present values) of the
+// wavefront's values v0, v1 (0 marks an absent value): the r-th largest lane
+// maximum L has at least r values at or above it; when at most 64 do, they
+// are compacted one per lane through scratch (64 words of LDS private to the
+// wavefront) and sorted; otherwise a bisection with three probes per round
+// finds the rank.
+__device__ inline uint32_t rth_largest2(uint32_t v0, uint32_t v1, uint32_t r, uint32_t* scratch) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t L = static_cast<uint32_t>(
+      __builtin_amdgcn_readlane(static_cast<int>(wave_sort_desc(max(v0, v1))), static_cast<int>(r) - 1));
+  const uint64_t b0 = __ballot(v0 >= L), b1 = __ballot(v1 >= L);
+  const uint32_t c = static_cast<uint32_t>(__popcll(b0) + __popcll(b1));
+  if (L != 0u && c <= 64u) {   // uniform
+    if (v0 >= L) scratch[lanes_below(b0)] = v0;
+    if (v1 >= L) scratch[__popcll(b0) + lanes_below(b1)] = v1;
+    __builtin_amdgcn_wave_barrier();
+    const uint32_t x = static_cast<uint32_t>(lane) < c ? scratch[lane] : 0u;
+    return static_cast<uint32_t>(
+        __builtin_amdgcn_readlane(static_cast<int>(wave_sort_desc(x)), static_cast<int>(r) - 1));
+  }
+  // invariant: count(>= lo) >= r > count(>= hi); counts <= 128 fit 10 bits
+  uint32_t lo = 0u, hi = 0xffffffffu;
+  while (hi - lo > 1u) {
+    const uint32_t step = max(1u, (hi - lo) / 4u);
+    const uint32_t t1 = min(lo + step, hi - 1u);
+    const uint32_t t2 = min(t1 + step, hi - 1u);
+    const uint32_t t3 = min(t2 + step, hi - 1u);
+    auto cnt = [&](uint32_t t) { return (v0 >= t ? 1u : 0u) + (v1 >= t ? 1u : 0u); };
+    const uint32_t packed = wave_sum_u32(cnt(t1) | (cnt(t2) << 10) | (cnt(t3) << 20));
+    if ((packed >> 20) >= r) {
+      lo = t3;
+    } else if (((packed >> 10) & 1023u) >= r) {
+      lo = t2;
+      hi = t3;
+    } else if ((packed & 1023u) >= r) {
+      lo = t1;
+      hi = t2;
+    } else {
+      hi = t1;
+    }
+  }
+  return lo;
+}
+
 }  // namespace alloc_detail
 
 // Allocation of one query: q_row and var_row are its d = 128 query values and
 // its KV head's channel variances.  Returns (b_{2l}, b_{2l+1}) for lane l.
 // Every lane of the wavefront must call it (ballots).
 __device__ inline uint2 allocate_query_wave(const float* __restrict__ q_row, const float* __restrict__ var_row,
-                                            int budget) {
+                                            int budget, uint32_t* scratch) {
   using namespace alloc_detail;
   const int lane = threadIdx.x & 63;
   const int c0 = 2 * lane;
@@ -61,54 +107,67 @@ __device__ inline uint2 allocate_query_wave(const float* __restrict__ q_row, con
   const float w1 = __fmul_rn(__fmul_rn(qv.y, qv.y), vv.y);
   const int k0 = __float_as_int(w0);       // w >= 0, so the bit pattern orders like the value
   const int k1 = __float_as_int(w1);
-  // The search runs on u = key - kKeyLo, which is >= 0 for every candidate
-  // key and below 2^32, so all of it is 32-bit unsigned arithmetic.
-  // Candidates of channel c with u >= t: the keys k_c - j 2^24 (j = 0..3)
-  // are evenly spaced, so that is min(4, (u_c - t) / 2^24 + 1) when u_c >= t.
+  // The search runs on u = key - kKeyLo, which is >= 3 2^24 for every
+  // channel's top key (and >= 0 for every candidate) and below 2^32, so all
+  // of it is 32-bit unsigned arithmetic.
   constexpr uint32_t kKeyLo = static_cast<uint32_t>(-3 * kKeyStep);   // -3 2^24 as a bit pattern
   const uint32_t u0 = static_cast<uint32_t>(k0) - kKeyLo, u1 = static_cast<uint32_t>(k1) - kKeyLo;
-  auto cnt1 = [](uint32_t u, uint32_t t) -> uint32_t { return u >= t ? min(4u, ((u - t) >> 24) + 1u) : 0u; };
   int b0 = 0, b1 = 0;
   if (budget >= kPlanes * kD) {
     b0 = b1 = kPlanes;
   } else if (budget > 0) {
-    // Search for the budget-th largest key with three probes per round:
-    // their counts (each <= 4d = 512 < 2^10) are packed into one word, so one
-    // wavefront sum serves all three.  Invariant: count(lo) >= budget >
-    // count(hi).  The start bracket comes from the lanes' larger keys in
-    // descending order, M_1 >= M_2 >= ...: with r = ceil(budget / 4), the r
-    // lanes whose larger key is >= M_r each have a channel with all four
-    // candidates >= M_r - 3 2^24, so that key counts >= 4r >= budget; and
-    // fewer than r' = ceil(r / 2) lanes hold a key above M_r', at most two
-    // channels each, so M_r' + 1 counts <= 8 (r' - 1) < budget.
+    // The budget-th largest candidate key, in two stages on u = U 2^24 + f
+    // (U the top byte, f the low 24 bits).  Channel c's candidates are
+    // u_c - j 2^24 (j = 0..3), so at t = T 2^24 it counts
+    // clamp(U_c - T + 1, 0, 4).  Stage 1 finds the largest T whose count is
+    // >= budget (three probes per round share one packed wavefront sum;
+    // count(0) = 4d since every U_c >= 3, count(256) = 0).  Inside
+    // [T 2^24, (T + 1) 2^24) only channels with a_c = U_c - T + 1 in 1..4
+    // change count, each by one once t passes T 2^24 + f_c.  With
+    // m = count(T 2^24) - budget, the key is therefore T 2^24 plus the
+    // (m + 1)-th smallest f_c over those s channels (m < s, else the count
+    // at (T + 1) 2^24 would still reach the budget).  Stage 2 takes that
+    // rank from whichever end of the s values it is nearer, so it is <= 64.
     const uint32_t B = static_cast<uint32_t>(budget);
-    const int r = (budget + 3) / 4, r2 = (r + 1) / 2;   // r in 1..128, r2 in 1..64
-    const uint32_t msort = wave_sort_desc(static_cast<uint32_t>(max(k0, k1)));   // keys are >= 0
-    const uint32_t m_r = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(msort), min(r, 64) - 1));
-    const uint32_t m_r2 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(msort), r2 - 1));
-    uint32_t lo = r <= 64 ? m_r : 0u;                      // key M_r - 3 2^24 (else -3 2^24: count 4d)
-    uint32_t hi = m_r2 + 1u - kKeyLo;                      // key M_r' + 1
-    while (hi - lo > 1u) {
-      const uint32_t step = max(1u, (hi - lo) / 4u);
-      const uint32_t t1 = min(lo + step, hi - 1u);
-      const uint32_t t2 = min(t1 + step, hi - 1u);
-      const uint32_t t3 = min(t2 + step, hi - 1u);
-      uint32_t packed = (cnt1(u0, t1) + cnt1(u1, t1)) | ((cnt1(u0, t2) + cnt1(u1, t2)) << 10) |
-                        ((cnt1(u0, t3) + cnt1(u1, t3)) << 20);
+    const int U0 = static_cast<int>(u0 >> 24), U1 = static_cast<int>(u1 >> 24);
+    auto chi = [](int U, int T) -> uint32_t { return static_cast<uint32_t>(min(4, max(0, U - T + 1))); };
+    int tlo = 0, thi = 256;
+    uint32_t clo = 4u * kD;   // count(tlo 2^24)
+    while (thi - tlo > 1) {
+      const int step = max(1, (thi - tlo) / 4);
+      const int t1 = min(tlo + step, thi - 1);
+      const int t2 = min(t1 + step, thi - 1);
+      const int t3 = min(t2 + step, thi - 1);
+      uint32_t packed = (chi(U0, t1) + chi(U1, t1)) | ((chi(U0, t2) + chi(U1, t2)) << 10) |
+                        ((chi(U0, t3) + chi(U1, t3)) << 20);
       packed = wave_sum_u32(packed);
-      const uint32_t c1 = packed & 1023u, c2 = (packed >> 10) & 1023u, c3 = packed >> 20;
-      if (c3 >= B) {
-        lo = t3;
-      } else if (c2 >= B) {
-        lo = t2;
-        hi = t3;
-      } else if (c1 >= B) {
-        lo = t1;
-        hi = t2;
+      const uint32_t n1 = packed & 1023u, n2 = (packed >> 10) & 1023u, n3 = packed >> 20;
+      if (n3 >= B) {
+        tlo = t3;
+        clo = n3;
+      } else if (n2 >= B) {
+        tlo = t2;
+        clo = n2;
+        thi = t3;
+      } else if (n1 >= B) {
+        tlo = t1;
+        clo = n1;
+        thi = t2;
       } else {
-        hi = t1;
+        thi = t1;
       }
     }
+    const bool s0 = U0 - tlo + 1 >= 1 && U0 - tlo + 1 <= 4, s1 = U1 - tlo + 1 >= 1 && U1 - tlo + 1 <= 4;
+    const uint32_t f0 = u0 & (kKeyStep - 1u), f1 = u1 & (kKeyStep - 1u);
+    const uint32_t m = clo - B;
+    const uint32_t sc = static_cast<uint32_t>(wave_count(s0) + wave_count(s1));
+    uint32_t fsel;
+    if (m + 1u <= sc - m) {   // uniform: (m + 1)-th smallest = (m + 1)-th largest of 2^24 - f
+      fsel = kKeyStep - rth_largest2(s0 ? kKeyStep - f0 : 0u, s1 ? kKeyStep - f1 : 0u, m + 1u, scratch);
+    } else {                  // (s - m)-th largest of f + 1
+      fsel = rth_largest2(s0 ? f0 + 1u : 0u, s1 ? f1 + 1u : 0u, sc - m, scratch) - 1u;
+    }
+    const uint32_t lo = static_cast<uint32_t>(tlo) * kKeyStep + fsel;   // the budget-th largest u
     const long long theta = static_cast<long long>(static_cast<int>(lo + kKeyLo));   // the budget-th largest key
     int gt0 = 0, gt1 = 0;
     bool tie0 = false, tie1 = false;

@@ -1256,7 +1256,9 @@ __global__ __launch_bounds__(kMainThreads) void scan_sample_kernel(ScanArgs a) {
   if (a.top_lists && blockIdx.x == 0 && static_cast<int>(threadIdx.x) < GQ) a.count[q0 + threadIdx.x] = 0u;
   if (a.var) {   // uniform
     if (wave < GQ) {
-      const uint2 b = allocate_query_wave(a.q + int64_t(q0 + wave) * kD, a.var + int64_t(h) * kD, a.budget);
+      // (the ring is free until the plane loads start: 64 words per wavefront)
+      const uint2 b = allocate_query_wave(a.q + int64_t(q0 + wave) * kD, a.var + int64_t(h) * kD, a.budget,
+                                          &ring[0][64 * wave]);
       const uint16_t pair = static_cast<uint16_t>(b.x | (b.y << 8));
       s_alloc[wave][lane] = pair;
     }
