@@ -33,8 +33,10 @@
  *     run planes[h][c][0..t-1][*].
  *   - Query head q reads KV head q / group; num_q must equal H * group
  *     (grouped-query attention; sessions are flattened into H).
- *   - Supported: d = 128 channels, 1 <= n <= 2^26 keys per head.  Keys and
- *     queries must be finite.
+ *   - Supported: d = 128 channels, 1 <= n <= 2^26 keys per head, and one
+ *     head's plane block (d * 4 * ldw words) below 4 GiB, i.e. ldw <= 2^21 - 4
+ *     (the scan addresses a head with 32-bit byte offsets); larger stores are
+ *     rejected with FATHOM_ERR_UNSUPPORTED.  Keys and queries must be finite.
  */
 #ifndef FATHOM_H
 #define FATHOM_H
@@ -121,6 +123,9 @@ int fathom_append_keys(const float* keys, int64_t stride_head, int64_t stride_to
  * w_c = fl32(fl32(q_c^2) var_c); candidate (c, j) has the int32 ordering key
  * bits(w_c) - j*2^24 (the order of w_c 4^-j); the B best candidates by
  * (key desc, c asc, j asc) are taken and alloc[q][c] = number taken from c.
+ * var holds variances, so >= 0: a weight w_c that is not a positive number
+ * (from a negative, -0 or NaN var_c) is read as +0: the channel has no
+ * importance.  The same rule holds in fathom_allocate_scan_topk.
  * Output alloc: uint8 [num_q][d], every row sums to B, entries in 0..4. */
 int fathom_allocate(const float* q, int32_t num_q, int32_t group, const float* var,
                     const fathom_store_desc* store, int32_t budget_bits, uint8_t* alloc,
@@ -151,7 +156,17 @@ int fathom_control_allocate(const float* q, int32_t num_q, int32_t mode, int32_t
  * index asc): out_idx int32 [num_q][k], out_score float32 [num_q][k].
  * all_scores: NULL, or float32 [num_q][n] receiving every score (a debug and
  * parity aid; costs n*4 bytes of writes per query).
- * alloc values above 4 are read as 4.  Scores are accumulated in fp32.
+ * alloc values above 4 are read as 4.
+ * Score arithmetic (fixed point, on the int8 matrix cores): per query, let U
+ * be the union of its group's plane prefixes and S = sum over its planes in U
+ * of |W| with W = q_c step_c 2^(3-j) (0 where the query skips the plane).
+ * Each weight is rounded to the integer V = round(W 2^30 / S); the sum
+ * t = sum V bit over the key's planes is exact in int32 (int8 digits of V,
+ * int32 matrix-core accumulation, exact recombination), and the returned
+ * score is fl32(fl32(t) * fl32(S 2^-30) + C_q) with C_q summed in float64
+ * and rounded once.  Its distance from the exact real score is at most
+ * (|U| / 2) 2^-30 S (weight rounding, |U| <= 512) plus the two fp32
+ * roundings.  The top-k is exact over these scores.
  * workspace: >= fathom_workspace_bytes(FATHOM_OP_SCAN, store, num_q, k). */
 int fathom_scan_topk(const uint32_t* planes, const float* lo, const float* step,
                      const fathom_store_desc* store, const float* q, const uint8_t* alloc,
@@ -207,6 +222,16 @@ const char* fathom_last_error(void);
  * the last read, and clears the record.  At most 4096 launches are kept. */
 int fathom_timing_enable(int32_t enable);
 int fathom_timing_read(double* total_ms, int32_t* launches);
+
+/* Measurement aid (not a step of the method): the HBM read ceiling that the
+ * scan's roofline fraction is set against.  Reads `bytes` (a positive
+ * multiple of 16) at src (a 16-byte aligned device pointer) once, in 16-byte
+ * non-temporal loads spread over the whole GPU, and folds them into values
+ * that are written to sink (uint32 [fathom_stream_read_sink_words()], device)
+ * only in the improbable case that one equals a fixed constant.  One kernel
+ * launch on hip_stream; time it with events on that stream. */
+int fathom_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* hip_stream);
+int32_t fathom_stream_read_sink_words(void);
 
 #ifdef __cplusplus
 }

@@ -211,10 +211,15 @@ def importance(q: np.ndarray, var: np.ndarray) -> np.ndarray:
     """w_c = fl32(fl32(q_c * q_c) * var_c), the variance-weighted importance.
 
     READING(Z6): the weight is q^2 sigma^2 on a 4^-j distortion ladder.
+    var holds variances: finite and >= 0 (asserted).  A variance of -0 is the
+    value 0, and so is the weight it gives: the result is normalised to +0 so
+    that its bit pattern orders like its value (READING(Z19)).
     """
     q = np.asarray(q, dtype=np.float32)
     var = np.asarray(var, dtype=np.float32)
-    return ((q * q).astype(np.float32) * var).astype(np.float32)
+    assert np.all(np.isfinite(var)) and np.all(var >= 0), "var must hold finite variances >= 0"
+    w = ((q * q).astype(np.float32) * var).astype(np.float32)
+    return (w + np.float32(0.0)).astype(np.float32)
 
 
 def ordering_keys(w: np.ndarray) -> np.ndarray:

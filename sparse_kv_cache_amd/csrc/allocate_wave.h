@@ -103,9 +103,14 @@ __device__ inline uint2 allocate_query_wave(const float* __restrict__ q_row, con
   const int c0 = 2 * lane;
   const float2 qv = *reinterpret_cast<const float2*>(q_row + c0);
   const float2 vv = *reinterpret_cast<const float2*>(var_row + c0);
-  const float w0 = __fmul_rn(__fmul_rn(qv.x, qv.x), vv.x);
-  const float w1 = __fmul_rn(__fmul_rn(qv.y, qv.y), vv.y);
-  const int k0 = __float_as_int(w0);       // w >= 0, so the bit pattern orders like the value
+  // A variance is >= 0.  A weight that is not a positive number (a negative,
+  // -0 or NaN var_c) is read as +0, so every weight is +0, positive or +inf
+  // and its bit pattern orders like its value.
+  float w0 = __fmul_rn(__fmul_rn(qv.x, qv.x), vv.x);
+  float w1 = __fmul_rn(__fmul_rn(qv.y, qv.y), vv.y);
+  w0 = w0 > 0.0f ? w0 : 0.0f;
+  w1 = w1 > 0.0f ? w1 : 0.0f;
+  const int k0 = __float_as_int(w0);
   const int k1 = __float_as_int(w1);
   // The search runs on u = key - kKeyLo, which is >= 3 2^24 for every
   // channel's top key (and >= 0 for every candidate) and below 2^32, so all

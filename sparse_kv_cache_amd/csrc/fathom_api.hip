@@ -53,8 +53,18 @@ int check_store(const fathom_store_desc* s) {
   if (s->ldw < words || s->ldw % 4 != 0)
     return fail(FATHOM_ERR_INVALID_ARG, "ldw = %lld must be >= ceil(n/32) = %lld and a multiple of 4",
                 static_cast<long long>(s->ldw), static_cast<long long>(words));
-  if (static_cast<int64_t>(s->num_kv_heads) * kD * kPlanes * s->ldw > (int64_t(1) << 40))
-    return fail(FATHOM_ERR_UNSUPPORTED, "plane store larger than 4 TiB");
+  // The scan addresses a head's plane block with 32-bit byte offsets (row
+  // offsets and the buffer resource's record count), so one head's block
+  // must stay below 4 GiB.
+  const int64_t head_bytes = int64_t(kD) * kPlanes * s->ldw * 4;
+  if (head_bytes > kMaxHeadBytes)
+    return fail(FATHOM_ERR_UNSUPPORTED, "one head's plane block is %lld bytes, above the %lld addressable (ldw = %lld)",
+                static_cast<long long>(head_bytes), static_cast<long long>(kMaxHeadBytes),
+                static_cast<long long>(s->ldw));
+  if (static_cast<int64_t>(s->num_kv_heads) * head_bytes > kMaxStoreBytes)
+    return fail(FATHOM_ERR_UNSUPPORTED, "plane store of %lld bytes is above the supported %lld bytes",
+                static_cast<long long>(static_cast<int64_t>(s->num_kv_heads) * head_bytes),
+                static_cast<long long>(kMaxStoreBytes));
   return FATHOM_OK;
 }
 
@@ -322,6 +332,17 @@ int fathom_sparse_attention(const uint16_t* k_rows, const uint16_t* v_rows, int6
   if (e != hipSuccess) return hip_fail(e, "fathom_sparse_attention launch");
   return ok();
 }
+
+int fathom_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* hip_stream) {
+  if (!src || !sink) return fail(FATHOM_ERR_INVALID_ARG, "src and sink must be non-NULL");
+  if (bytes < 16 || bytes % 16 != 0) return fail(FATHOM_ERR_INVALID_ARG, "bytes must be a positive multiple of 16");
+  if (!aligned(src, 16) || !aligned(sink, 4)) return fail(FATHOM_ERR_INVALID_ARG, "src must be 16-byte aligned");
+  hipError_t e = launch_stream_read(src, bytes, sink, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return hip_fail(e, "fathom_stream_read launch");
+  return ok();
+}
+
+int32_t fathom_stream_read_sink_words(void) { return stream_read_blocks(); }
 
 int fathom_host_device_pointer(void* pinned_host, void** device_ptr) {
   if (!pinned_host || !device_ptr) return fail(FATHOM_ERR_INVALID_ARG, "pointers must be non-NULL");

@@ -16,6 +16,11 @@ constexpr int kSampleMaxBlocks = 8;     // sampled blocks per KV head
 constexpr int kSampleMaxKeys = kSampleBlockKeys * kSampleMaxBlocks;
 constexpr int kQueryChunk = 4;     // query heads scored together per workgroup
 constexpr int64_t kMaxKeys = int64_t(1) << 26;
+// One head's plane block (d * 4 rows of ldw words) is addressed with 32-bit
+// byte offsets; the largest block is therefore 2^32 - 1 bytes (ldw <=
+// 2^21 - 4, i.e. at most 67,108,736 keys per head).
+constexpr int64_t kMaxHeadBytes = (int64_t(1) << 32) - 1;
+constexpr int64_t kMaxStoreBytes = int64_t(1) << 42;   // 4 TiB of planes per call
 
 // Monotone map float -> uint32 (larger float <-> larger integer).
 __host__ __device__ inline uint32_t float_to_ordered(float f) {
@@ -56,6 +61,11 @@ int attend_splits(int k);
 hipError_t launch_attend(const uint16_t* k_rows, const uint16_t* v_rows, int64_t stride_head,
                          int64_t stride_token, int64_t n, const float* q, const int32_t* idx, int num_q,
                          int group, int k, float scale, float* part, float* out, hipStream_t stream);
+
+// Measurement aid: a streaming read of `bytes` (a multiple of 16) from src;
+// sink holds stream_read_blocks() words (written only on an improbable value).
+int stream_read_blocks();
+hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream);
 
 struct ScanWorkspace {
   float* theta;      // [Q] candidate threshold per query

@@ -12,18 +12,28 @@
 //   C_q    = sum_c q_c (lo_c + step_c 2^(3-b_qc))      (bin-centre offsets).
 //
 // Launch sequence per call (all on the caller's stream):
-//   1. scan_sample_kernel    builds each chunk's table and scores up to 8
-//                            sampled 1024-key blocks per KV head, the way
-//                            the main kernel does;
-//   2. scan_threshold_kernel per query, a radix select on the sample picks a
-//                            score theta expected to leave ~2k keys above it;
-//   3. scan_main_kernel      every key of every head, see below; keys scoring
-//                            >= theta go to a per-query candidate list;
-//   4. scan_merge_kernel     per query, radix-selects the k-th candidate, sorts
-//                            the survivors and writes the top-k.  If the list
-//                            holds fewer than k keys or overflowed, the
-//                            workgroup recomputes the query's scores and
-//                            selects the exact top-k (ties by index).
+//   1. scan_sample_kernel    one workgroup per (sampled 1024-key block, KV
+//                            head, query chunk).  With the fused allocation
+//                            its wavefront g first allocates query g's bits
+//                            (allocate_wave.h).  It builds the chunk's union
+//                            and scan table (workgroup 0 stores the table),
+//                            then scores its block the way the main kernel
+//                            does.  When the sample rank of the threshold is
+//                            <= 32 it keeps only per-group maxima of the
+//                            block's scores, otherwise every sampled score;
+//   2. scan_threshold_kernel only when that rank is > 32: per query, a digit
+//                            select over the sampled scores gives theta;
+//   3. scan_main_kernel      every key of every head, see below.  With the
+//                            group maxima, each workgroup selects theta
+//                            itself from them while its first plane loads
+//                            are in flight.  Keys whose score can reach
+//                            theta go to a per-query candidate list;
+//   4. scan_merge_kernel     per query, one digit pass orders the candidates
+//                            into buckets and places the k best by counting.
+//                            If the list holds fewer than k keys scoring >=
+//                            theta, or overflowed, workgroup 0 recomputes the
+//                            query's scores and selects the exact top-k
+//                            (ties by index).
 //
 // Main kernel.  A workgroup owns one KV head and a chunk of <= 4 of its GQA
 // query heads, and reads, once, the union U of the chunk's plane prefixes
@@ -33,13 +43,16 @@
 //   A (16 x 64): each query's weights of the block in fixed point,
 //       V = round(W 2^30 / sum|W|), split into four balanced base-256 int8
 //       digits ("limbs"); row 4g+l holds limb l of query g;
-//   B (64 x 16): bit[p][key] as int8 0 or -1, built from the 32-bit plane
-//       words with byte permutes (no transpose: a column is a 2-key pair);
-// so one MFMA gives all 4 queries' 4 limb sums of 16 keys over 64 planes, and
-// the int32 sums recombine into sum_p V bit in fp32 (two roundings).  The weights'
-// tables (limbs, scale, offset C_q) are built once per chunk by the sample
-// kernel.  Keys whose score can reach theta are kept in an LDS buffer per
-// query and flushed to the global candidate list at the end.
+//   B (64 x 16): the bits.  The plane words of a block stream into LDS by DMA;
+//       the LDS transpose read (ds_read_b64_tr_b8) gives each lane, per byte,
+//       one plane of eight consecutive keys, and one AND per dword with
+//       0x01010101 << e keeps key e's bit of every plane, as bit * 2^e;
+// so one MFMA gives all 4 queries' 4 limb sums of 16 keys over 64 planes; the
+// epilogue unscales the limbs by shifts and recombines them into the exact
+// integer t = sum_p V bit, and the score is fma(float(t), sum|W| 2^-30, C_q).
+// The tables (limbs, scale, offset C_q, union rows) are built once per chunk
+// by the sample kernel.  Keys whose t can reach theta are kept in LDS lists
+// per (wavefront, query) and flushed to the global candidate list at the end.
 
 #include <hip/hip_ext.h>
 

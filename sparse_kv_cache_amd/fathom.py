@@ -43,6 +43,8 @@ EXPORTS = (
     "fathom_last_error",
     "fathom_timing_enable",
     "fathom_timing_read",
+    "fathom_stream_read",
+    "fathom_stream_read_sink_words",
 )
 
 
@@ -87,6 +89,8 @@ def _load():
         "fathom_last_error": (ctypes.c_char_p, []),
         "fathom_timing_enable": (ctypes.c_int, [i32]),
         "fathom_timing_read": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32)]),
+        "fathom_stream_read": (ctypes.c_int, [P, i64, P, P]),
+        "fathom_stream_read_sink_words": (i32, []),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -286,3 +290,13 @@ def timing_read():
     cnt = ctypes.c_int32()
     _check(lib.fathom_timing_read(ctypes.byref(ms), ctypes.byref(cnt)), "fathom_timing_read")
     return ms.value, cnt.value
+
+
+def stream_read(src: torch.Tensor, sink: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Streaming read of the whole of src (a measurement aid: the HBM read
+    ceiling).  Returns the sink buffer."""
+    nbytes = src.numel() * src.element_size()
+    if sink is None:
+        sink = torch.zeros(int(lib.fathom_stream_read_sink_words()), dtype=torch.int32, device=src.device)
+    _check(lib.fathom_stream_read(_ptr(src), nbytes, _ptr(sink), _stream(stream)), "fathom_stream_read")
+    return sink

@@ -174,3 +174,27 @@ def test_append_validation():
 def test_misc_validation():
     assert lib.fathom_host_device_pointer(None, None) == fa.FATHOM_ERR_INVALID_ARG
     assert lib.fathom_timing_read(None, None) == fa.FATHOM_ERR_INVALID_ARG
+
+
+def test_per_head_block_limit():
+    """The scan addresses one head's plane block with 32-bit byte offsets: a
+    block of 2^32 bytes or more is rejected on the host (a larger legal ldw
+    would otherwise wrap row offsets onto low rows)."""
+    top = (1 << 21) - 4                       # largest ldw whose block is < 4 GiB
+    ok = SD(1, 128, top * 32, top)
+    assert fa.workspace_bytes(fa.FATHOM_OP_PACK, ok) > 0
+    for n, ldw in (((1 << 26), 1 << 21), (1000, 1 << 21), (1000, 1 << 22)):
+        s = SD(1, 128, n, ldw)
+        assert fa.workspace_bytes(fa.FATHOM_OP_PACK, s) == 0
+        assert _pack(s) == fa.FATHOM_ERR_UNSUPPORTED
+        assert "addressable" in lib.fathom_last_error().decode()
+        assert _scan(s, num_q=4, k=16) == fa.FATHOM_ERR_UNSUPPORTED
+    # the whole store: 1025 heads of just under 4 GiB exceed 4 TiB
+    assert _pack(SD(1025, 128, top * 32, top)) == fa.FATHOM_ERR_UNSUPPORTED
+
+
+def test_stream_read_validation():
+    assert lib.fathom_stream_read_sink_words() > 0
+    assert lib.fathom_stream_read(None, 1 << 20, FAKE, None) == fa.FATHOM_ERR_INVALID_ARG
+    assert lib.fathom_stream_read(FAKE, 1000, FAKE, None) == fa.FATHOM_ERR_INVALID_ARG
+    assert lib.fathom_stream_read(ctypes.c_void_p(0x1008), 1 << 20, FAKE, None) == fa.FATHOM_ERR_INVALID_ARG

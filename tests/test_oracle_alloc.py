@@ -126,3 +126,26 @@ def test_continuous_water_level_bracket():
         theta = min(taken_vals)
         bstar = np.clip(np.log(w / theta) / np.log(4.0), 0, 4)
         assert np.all(np.abs(b - bstar) <= 1 + 1e-9)
+
+
+def test_signed_zero_variance_is_zero():
+    """-0 and +0 are the same variance: the allocation cannot depend on the
+    sign of a zero (a bit-pattern ordering without the +0 normalisation would
+    rank -0 channels below every other candidate)."""
+    rng = np.random.default_rng(12)
+    q = rng.standard_normal(128).astype(np.float32)
+    var = rng.lognormal(0, 1, 128).astype(np.float32)
+    var[::5] = 0.0
+    neg = var.copy()
+    neg[::10] = -0.0            # half of the zero channels carry the sign
+    assert np.signbit(neg[0]) and not np.signbit(neg[5])
+    for B in (0, 1, 100, 300, 400, 450, 511, 512):
+        assert np.array_equal(O.allocate(q, neg, B), O.allocate(q, var, B)), B
+
+
+@pytest.mark.parametrize("bad", [-1.0, np.nan, np.inf])
+def test_variance_must_be_finite_and_non_negative(bad):
+    var = np.ones(128, np.float32)
+    var[7] = bad
+    with pytest.raises(AssertionError):
+        O.allocate(np.ones(128, np.float32), var, 92)
