@@ -15,6 +15,13 @@
 
 using namespace fathom;
 
+// Scratch memory of fathom_allocate_scan_topk_noalloc: a static device array
+// that each GPU the library runs on holds until the process ends.  Host code
+// never uses the array's name as an address (on the host it names a stand-in,
+// not device memory): its device address is taken once per device with
+// hipGetSymbolAddress and kept per device.
+static __device__ __align__(256) unsigned char scratch[FATHOM_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 thread_local char g_last_error[512] = "";
@@ -99,6 +106,10 @@ ScanLayout scan_layout(int num_q) {
   L.total = off;
   return L;
 }
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};   // device address of `scratch` per device
 
 // kernel timing record
 std::mutex g_timing_mu;
@@ -298,6 +309,41 @@ int fathom_allocate_scan_topk(const uint32_t* planes, const float* lo, const flo
   if (!var) return fail(FATHOM_ERR_INVALID_ARG, "var must be non-NULL");
   return scan_impl("fathom_allocate_scan_topk launch", planes, lo, step, store, q, nullptr, num_q, group, k,
                    out_idx, out_score, nullptr, workspace, workspace_bytes, hip_stream, var, budget_bits, alloc);
+}
+
+int fathom_allocate_scan_topk_noalloc(const uint32_t* planes, const float* lo, const float* step, const float* var,
+                                      const fathom_store_desc* store, const float* q, int32_t num_q, int32_t group,
+                                      int32_t budget_bits, int32_t k, uint8_t* alloc, int32_t* out_idx,
+                                      float* out_score, void* hip_stream) {
+  if (!var) return fail(FATHOM_ERR_INVALID_ARG, "var must be non-NULL");
+  if (num_q < 1 || num_q > FATHOM_NOALLOC_MAX_Q)
+    return fail(FATHOM_ERR_UNSUPPORTED, "num_q = %d outside [1, %d] for the allocation-free call", num_q,
+                FATHOM_NOALLOC_MAX_Q);
+  const size_t need = scan_layout(num_q).total;
+  if (need > FATHOM_NOALLOC_SCRATCH_BYTES)
+    return fail(FATHOM_ERR_UNSUPPORTED, "the call needs %zu scratch bytes, above the static %d", need,
+                FATHOM_NOALLOC_SCRATCH_BYTES);
+  int device = -1;
+  hipError_t e = hipGetDevice(&device);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (device < 0 || device >= kMaxDevices) return fail(FATHOM_ERR_UNSUPPORTED, "device %d above %d", device, kMaxDevices);
+  void* ptr = nullptr;
+  {
+    // set-up, once per device with that device current: the array's device
+    // address (each GPU holds its own copy at its own address)
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[device]) {
+      void* p = nullptr;
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+      if (!p || !aligned(p, 256)) return fail(FATHOM_ERR_HIP, "static scratch has no 256-byte aligned address");
+      g_scratch_ptr[device] = p;
+    }
+    ptr = g_scratch_ptr[device];
+  }
+  return scan_impl("fathom_allocate_scan_topk_noalloc launch", planes, lo, step, store, q, nullptr, num_q, group,
+                   k, out_idx, out_score, nullptr, ptr, FATHOM_NOALLOC_SCRATCH_BYTES, hip_stream, var, budget_bits,
+                   alloc);
 }
 
 int fathom_sparse_attention(const uint16_t* k_rows, const uint16_t* v_rows, int64_t stride_head,

@@ -27,6 +27,8 @@ FATHOM_OP_ATTEND = 2
 FATHOM_CONTROL_UNIFORM = 0
 FATHOM_CONTROL_TOP_CHANNELS = 1
 MAX_K = 4096
+NOALLOC_MAX_Q = 64
+NOALLOC_SCRATCH_BYTES = 12 << 20
 
 EXPORTS = (
     "fathom_plane_ldw",
@@ -37,6 +39,7 @@ EXPORTS = (
     "fathom_control_allocate",
     "fathom_scan_topk",
     "fathom_allocate_scan_topk",
+    "fathom_allocate_scan_topk_noalloc",
     "fathom_sparse_attention",
     "fathom_host_device_pointer",
     "fathom_status_string",
@@ -82,6 +85,7 @@ def _load():
         "fathom_control_allocate": (ctypes.c_int, [P, i32, i32, i32, P, P]),
         "fathom_scan_topk": (ctypes.c_int, [P, P, P, SD, P, P, i32, i32, i32, P, P, P, P, sz, P]),
         "fathom_allocate_scan_topk": (ctypes.c_int, [P, P, P, P, SD, P, i32, i32, i32, i32, P, P, P, P, sz, P]),
+        "fathom_allocate_scan_topk_noalloc": (ctypes.c_int, [P, P, P, P, SD, P, i32, i32, i32, i32, P, P, P, P]),
         "fathom_sparse_attention": (ctypes.c_int, [P, P, i64, i64, SD, P, P, i32, i32, i32, ctypes.c_float, P, P,
                                                    sz, P]),
         "fathom_host_device_pointer": (ctypes.c_int, [P, ctypes.POINTER(P)]),
@@ -241,6 +245,21 @@ def allocate_scan_topk(planes: torch.Tensor, lo: torch.Tensor, step: torch.Tenso
                                        Q, group, budget, k, _ptr(alloc), _ptr(out_idx), _ptr(out_score),
                                        _ptr(workspace), workspace.numel(), _stream(stream))
     _check(st, "fathom_allocate_scan_topk")
+    return alloc, out_idx, out_score
+
+
+def allocate_scan_topk_noalloc(planes: torch.Tensor, lo: torch.Tensor, step: torch.Tensor, var: torch.Tensor,
+                               store: StoreDesc, q: torch.Tensor, group: int, budget: int, k: int, *,
+                               alloc: torch.Tensor, out_idx: torch.Tensor, out_score: torch.Tensor,
+                               planes_ptr: Optional[int] = None, stream=None):
+    """allocate_scan_topk() with the library's static scratch memory: no
+    workspace, and nothing allocated here either (every output is passed in)."""
+    Q = q.shape[0]
+    pp = ctypes.c_void_p(planes_ptr) if planes_ptr is not None else _ptr(planes)
+    st = lib.fathom_allocate_scan_topk_noalloc(pp, _ptr(lo), _ptr(step), _ptr(var), ctypes.byref(store), _ptr(q),
+                                               Q, group, budget, k, _ptr(alloc), _ptr(out_idx), _ptr(out_score),
+                                               _stream(stream))
+    _check(st, "fathom_allocate_scan_topk_noalloc")
     return alloc, out_idx, out_score
 
 

@@ -198,3 +198,13 @@ def test_stream_read_validation():
     assert lib.fathom_stream_read(None, 1 << 20, FAKE, None) == fa.FATHOM_ERR_INVALID_ARG
     assert lib.fathom_stream_read(FAKE, 1000, FAKE, None) == fa.FATHOM_ERR_INVALID_ARG
     assert lib.fathom_stream_read(ctypes.c_void_p(0x1008), 1 << 20, FAKE, None) == fa.FATHOM_ERR_INVALID_ARG
+
+
+def test_noalloc_rejects_on_host():
+    s = SD(65, 128, 1000, 32)
+    st = lib.fathom_allocate_scan_topk_noalloc(FAKE, FAKE, FAKE, FAKE, ctypes.byref(s), FAKE, 65, 1, 92, 10, FAKE,
+                                               FAKE, FAKE, None)
+    assert st == fa.FATHOM_ERR_UNSUPPORTED and "allocation-free" in lib.fathom_last_error().decode()
+    s = SD(2, 128, 1000, 32)
+    assert lib.fathom_allocate_scan_topk_noalloc(FAKE, FAKE, FAKE, None, ctypes.byref(s), FAKE, 8, 4, 92, 10, FAKE,
+                                                 FAKE, FAKE, None) == fa.FATHOM_ERR_INVALID_ARG
