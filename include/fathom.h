@@ -67,12 +67,30 @@ enum { FATHOM_CONTROL_UNIFORM = 0, FATHOM_CONTROL_TOP_CHANNELS = 1 };
 #define FATHOM_MAX_K 4096
 
 /* Shape of a plane store: H KV heads, d channels, n keys per head, ldw words
- * per plane row.  Passed by pointer; the library does not keep it. */
+ * per plane row.  Passed by pointer; the library does not keep it.
+ *
+ * lengths (ragged sessions: [Art] para 1, many sessions of different lengths
+ * decode at once): NULL, or a device array int32 [H] holding the number of
+ * keys of each head.  Head h then holds n_h = min(max(lengths[h], 0), n)
+ * keys, n being the bound no head exceeds (ldw >= ceil(n / 32) as always).
+ * With lengths:
+ *   - fathom_pack_planes quantizes each head over its own n_h keys (a head
+ *     with n_h = 0 gets lo = step = var = 0 and all-zero planes);
+ *   - fathom_append_keys writes head h's new keys at position n_h and adds m
+ *     to lengths[h];
+ *   - the scans rank head h's n_h keys only: no index >= n_h is returned, and
+ *     a query whose head holds fewer than k keys gets its n_h keys followed
+ *     by index -1 with score -inf;
+ *   - fathom_sparse_attention skips indexes >= n_h.
+ * Bits of keys >= n_h are zero after packing (appends keep them so).  The
+ * array is read on the device when the work runs, so it is not validated on
+ * the host; out-of-range values are clamped as above. */
 typedef struct fathom_store_desc {
   int32_t num_kv_heads;
   int32_t d;
   int64_t n;
   int64_t ldw;
+  int32_t* lengths;
 } fathom_store_desc;
 
 /* Words per plane row for n keys: ceil(n / 32) rounded up to a multiple of 4
@@ -112,7 +130,10 @@ int fathom_pack_planes(const float* keys, int64_t stride_head, int64_t stride_to
  * neither lo, step nor var, changes.  keys: float32, key n + t of head h at
  * keys[h*stride_head + t*stride_token + c] (channel stride 1); 1 <= m and
  * n + m <= 32 * store->ldw (the rows' capacity).  Afterwards the store holds
- * n + m keys: pass n + m to the scan.  One kernel launch on hip_stream. */
+ * n + m keys: pass n + m to the scan.  One kernel launch on hip_stream.
+ * With store->lengths, head h's keys go to positions n_h .. n_h + m - 1
+ * (n_h as clamped there) and lengths[h] becomes n_h + m, in a second launch;
+ * n + m <= 32 * ldw still bounds every head, and n + m is the new bound. */
 int fathom_append_keys(const float* keys, int64_t stride_head, int64_t stride_token, int32_t m,
                        const fathom_store_desc* store, uint32_t* planes, const float* lo, const float* step,
                        void* hip_stream);

@@ -193,12 +193,25 @@ def channel_variance(codes: np.ndarray, step: np.ndarray) -> np.ndarray:
     return var.astype(np.float32)
 
 
-def pack_head(keys: np.ndarray):
-    """All per-head store products: (planes, lo, step, var, codes)."""
+def pack_head(keys: np.ndarray, ldw: int | None = None):
+    """All per-head store products: (planes, lo, step, var, codes).
+
+    ldw: row length in words (default plane_ldw(n)); a longer row, as when
+    heads of different lengths share one store, holds zero padding bits.
+    READING(Z20): a head holding no key has no range: lo = step = var = 0 and
+    all-zero planes.
+    """
+    keys = np.asarray(keys, dtype=np.float32)
+    n, d = keys.shape
+    if ldw is None:
+        ldw = plane_ldw(n)
+    if n == 0:
+        z = np.zeros(d, np.float32)
+        return np.zeros((d, PLANES, ldw), np.uint32), z, z.copy(), z.copy(), np.zeros((0, d), np.uint8)
     lo, hi = key_range(keys)
     step, inv = quant_scale(lo, hi)
     codes = quantize(keys, lo, inv)
-    planes = pack_planes(codes, plane_ldw(keys.shape[0]))
+    planes = pack_planes(codes, ldw)
     var = channel_variance(codes, step)
     return planes, lo, step, var, codes
 
@@ -375,6 +388,22 @@ def topk(scores: np.ndarray, k: int):
     idx = np.arange(s.shape[0])
     order = np.lexsort((idx, -s))[:k]
     return order.astype(np.int32), s[order].astype(np.float32)
+
+
+def topk_padded(scores: np.ndarray, k: int):
+    """``topk`` over a head that may hold fewer than k keys (ragged sessions).
+
+    READING(Z20): the first min(k, n) ranks are the top-k of the n scores
+    (score desc, index asc); ranks n .. k - 1 hold index -1 and score -inf.
+    scores float [n], n >= 0 -> (idx int32 [k], score float32 [k]).
+    """
+    s = np.asarray(scores, dtype=np.float64)
+    m = min(k, s.shape[0])
+    idx = np.full(k, -1, np.int32)
+    val = np.full(k, -np.inf, np.float32)
+    if m > 0:
+        idx[:m], val[:m] = topk(s, m)
+    return idx, val
 
 
 # --------------------------------------------------------------------------

@@ -47,6 +47,7 @@ struct AttendArgs {
   const uint16_t* vrows;
   int64_t stride_head, stride_token;
   int64_t n;
+  const int32_t* lengths;  // null, or keys per head
   const float* q;          // [Q][kD]
   const int32_t* idx;      // [Q][k]
   int group, topk, nsplit;
@@ -67,6 +68,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(AttendArgs 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int qi = blockIdx.y, split = blockIdx.x;
   const int h = qi / a.group;
+  const int64_t nh = head_length(a.lengths, h, a.n);
   const int i0 = split * kAttChunk;
   const int cnt = min(kAttChunk, a.topk - i0);
   const int piece = lane & (kRowLanes - 1), sub = lane / kRowLanes;
@@ -87,7 +89,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(AttendArgs 
     slot[p] = (wave * kPasses + p) * kRowsPerPass + sub;
     const int jj = min(slot[p], cnt - 1);
     const int64_t key = a.idx[int64_t(qi) * a.topk + i0 + jj];
-    ok[p] = slot[p] < cnt && key >= 0 && key < a.n;
+    ok[p] = slot[p] < cnt && key >= 0 && key < nh;
     const int64_t row = int64_t(h) * a.stride_head + (ok[p] ? key : 0) * a.stride_token + 8 * piece;
     kw[p] = *reinterpret_cast<const uint4*>(a.krows + row);
     vw[p] = *reinterpret_cast<const uint4*>(a.vrows + row);
@@ -190,7 +192,7 @@ __global__ __launch_bounds__(kD) void attend_combine_kernel(AttendArgs a) {
 int attend_splits(int k) { return (k + kAttChunk - 1) / kAttChunk; }
 
 hipError_t launch_attend(const uint16_t* k_rows, const uint16_t* v_rows, int64_t stride_head,
-                         int64_t stride_token, int64_t n, const float* q, const int32_t* idx, int num_q,
+                         int64_t stride_token, int64_t n, const int32_t* lengths, const float* q, const int32_t* idx, int num_q,
                          int group, int k, float scale, float* part, float* out, hipStream_t stream) {
   AttendArgs a{};
   a.krows = k_rows;
@@ -198,6 +200,7 @@ hipError_t launch_attend(const uint16_t* k_rows, const uint16_t* v_rows, int64_t
   a.stride_head = stride_head;
   a.stride_token = stride_token;
   a.n = n;
+  a.lengths = lengths;
   a.q = q;
   a.idx = idx;
   a.group = group;

@@ -68,6 +68,7 @@ int check_store(const fathom_store_desc* s) {
     return fail(FATHOM_ERR_UNSUPPORTED, "one head's plane block is %lld bytes, above the %lld addressable (ldw = %lld)",
                 static_cast<long long>(head_bytes), static_cast<long long>(kMaxHeadBytes),
                 static_cast<long long>(s->ldw));
+  if (s->lengths && !aligned(s->lengths, 4)) return fail(FATHOM_ERR_INVALID_ARG, "lengths must be 4-byte aligned");
   if (static_cast<int64_t>(s->num_kv_heads) * head_bytes > kMaxStoreBytes)
     return fail(FATHOM_ERR_UNSUPPORTED, "plane store of %lld bytes is above the supported %lld bytes",
                 static_cast<long long>(static_cast<int64_t>(s->num_kv_heads) * head_bytes),
@@ -170,7 +171,8 @@ int scan_impl(const char* where, const uint32_t* planes, const float* lo, const 
       timed = true;
     }
   }
-  hipError_t e = launch_scan_topk(planes, lo, step, store->num_kv_heads, store->n, store->ldw, q, alloc,
+  hipError_t e = launch_scan_topk(planes, lo, step, store->num_kv_heads, store->n, store->lengths, store->ldw, q,
+                                  alloc,
                                   num_q, group, k, out_idx, out_score, all_scores, ws,
                                   timed ? &timing : nullptr, static_cast<hipStream_t>(hip_stream), var,
                                   budget_bits, alloc_out);
@@ -230,7 +232,7 @@ int fathom_pack_planes(const float* keys, int64_t stride_head, int64_t stride_to
                    reinterpret_cast<unsigned long long*>(w + L.s1),
                    reinterpret_cast<unsigned long long*>(w + L.s2)};
   hipError_t e = launch_pack(keys, store->num_kv_heads > 1 ? stride_head : 0, stride_token,
-                             store->num_kv_heads, store->n, store->ldw, planes, lo, step, var, ws,
+                             store->num_kv_heads, store->n, store->lengths, store->ldw, planes, lo, step, var, ws,
                              static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return hip_fail(e, "fathom_pack_planes launch");
   return ok();
@@ -254,8 +256,8 @@ int fathom_append_keys(const float* keys, int64_t stride_head, int64_t stride_to
     return fail(FATHOM_ERR_INVALID_ARG, "stride_head must be >= m * stride_token");
   if (!aligned(keys, 4) || !aligned(planes, 16) || !aligned(lo, 4) || !aligned(step, 4))
     return fail(FATHOM_ERR_INVALID_ARG, "keys, lo and step must be 4-byte aligned, planes 16-byte aligned");
-  hipError_t e = launch_append(keys, stride_head, stride_token, m, store->num_kv_heads, store->n, store->ldw,
-                               planes, lo, step, static_cast<hipStream_t>(hip_stream));
+  hipError_t e = launch_append(keys, stride_head, stride_token, m, store->num_kv_heads, store->n, store->lengths,
+                               store->ldw, planes, lo, step, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return hip_fail(e, "fathom_append_keys launch");
   return ok();
 }
@@ -373,7 +375,8 @@ int fathom_sparse_attention(const uint16_t* k_rows, const uint16_t* v_rows, int6
   if (!workspace || !aligned(workspace, 256) || workspace_bytes < need)
     return fail(FATHOM_ERR_WORKSPACE, "attention needs a 256-byte aligned workspace of %zu bytes (got %zu)", need,
                 workspace_bytes);
-  hipError_t e = launch_attend(k_rows, v_rows, stride_head, stride_token, store->n, q, idx, num_q, group, k, scale,
+  hipError_t e = launch_attend(k_rows, v_rows, stride_head, stride_token, store->n, store->lengths, q, idx, num_q,
+                               group, k, scale,
                                static_cast<float*>(workspace), out, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return hip_fail(e, "fathom_sparse_attention launch");
   return ok();

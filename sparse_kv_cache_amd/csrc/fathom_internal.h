@@ -32,6 +32,14 @@ __host__ __device__ inline float ordered_to_float(uint32_t o) {
   return __builtin_bit_cast(float, u);
 }
 
+// Keys held by head h: n, or with a per-head length array (ragged
+// sessions) lengths[h] clamped to [0, n].
+__device__ inline int64_t head_length(const int32_t* lengths, int h, int64_t n) {
+  if (!lengths) return n;
+  const int64_t v = lengths[h];
+  return v < 0 ? 0 : (v > n ? n : v);
+}
+
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the first HIP error met while enqueuing.
 
@@ -43,11 +51,12 @@ struct PackWorkspace {
 };
 
 hipError_t launch_pack(const float* keys, int64_t stride_head, int64_t stride_token, int H, int64_t n,
-                       int64_t ldw, uint32_t* planes, float* lo, float* step, float* var,
+                       const int32_t* lengths, int64_t ldw, uint32_t* planes, float* lo, float* step, float* var,
                        const PackWorkspace& ws, hipStream_t stream);
 
 hipError_t launch_append(const float* keys, int64_t stride_head, int64_t stride_token, int m, int H, int64_t n,
-                         int64_t ldw, uint32_t* planes, const float* lo, const float* step, hipStream_t stream);
+                         int32_t* lengths, int64_t ldw, uint32_t* planes, const float* lo, const float* step,
+                         hipStream_t stream);
 
 hipError_t launch_allocate(const float* q, int num_q, int group, const float* var, int budget,
                            uint8_t* alloc, hipStream_t stream);
@@ -59,7 +68,7 @@ hipError_t launch_control_allocate(const float* q, int num_q, int mode, int budg
 // (partials into part [num_q][attend_splits(k)][kD + 2], then the combine).
 int attend_splits(int k);
 hipError_t launch_attend(const uint16_t* k_rows, const uint16_t* v_rows, int64_t stride_head,
-                         int64_t stride_token, int64_t n, const float* q, const int32_t* idx, int num_q,
+                         int64_t stride_token, int64_t n, const int32_t* lengths, const float* q, const int32_t* idx, int num_q,
                          int group, int k, float scale, float* part, float* out, hipStream_t stream);
 
 // Measurement aid: a streaming read of `bytes` (a multiple of 16) from src;
@@ -81,7 +90,8 @@ struct ScanTiming {
 };
 
 hipError_t launch_scan_topk(const uint32_t* planes, const float* lo, const float* step, int H,
-                            int64_t n, int64_t ldw, const float* q, const uint8_t* alloc, int num_q,
+                            int64_t n, const int32_t* lengths, int64_t ldw, const float* q, const uint8_t* alloc,
+                            int num_q,
                             int group, int k, int32_t* out_idx, float* out_score,
                             float* all_scores, const ScanWorkspace& ws, const ScanTiming* timing,
                             hipStream_t stream, const float* var = nullptr, int budget = 0,

@@ -36,12 +36,13 @@ __global__ void pack_init_kernel(PackWorkspace ws, int count) {
 // with ordered-integer atomics (exact, order independent).
 __global__ __launch_bounds__(kRangeThreads) void pack_range_kernel(
     const float* __restrict__ keys, int64_t stride_head, int64_t stride_token, int64_t n,
-    PackWorkspace ws) {
+    const int32_t* __restrict__ lengths, PackWorkspace ws) {
   const int h = blockIdx.y;
   const int cg = threadIdx.x & 31;          // channels 4cg .. 4cg+3
   const int r0 = threadIdx.x >> 5;          // 0..7
+  const int64_t nh = head_length(lengths, h, n);
   const int64_t row_begin = int64_t(blockIdx.x) * kRangeRows;
-  const int64_t row_end = row_begin + kRangeRows < n ? row_begin + kRangeRows : n;
+  const int64_t row_end = row_begin + kRangeRows < nh ? row_begin + kRangeRows : nh;
   const float* base = keys + int64_t(h) * stride_head + 4 * cg;
 
   float mn[4], mx[4];
@@ -109,8 +110,11 @@ __device__ __forceinline__ void transpose32x16(uint32_t (&x)[32], uint32_t (&y)[
 
 __global__ __launch_bounds__(kQuantThreads) void pack_quant_kernel(
     const float* __restrict__ keys, int64_t stride_head, int64_t stride_token, int64_t n,
-    int64_t ldw, int num_tiles, int tiles_per_wg, uint32_t* __restrict__ planes, PackWorkspace ws) {
+    const int32_t* __restrict__ lengths, int64_t ldw, int num_tiles, int tiles_per_wg,
+    uint32_t* __restrict__ planes, PackWorkspace ws) {
   const int h = blockIdx.y;
+  const int64_t nh = head_length(lengths, h, n);
+  const int64_t last_key = nh > 0 ? nh - 1 : 0;   // (key 0 exists: n >= 1)
   const int tid = threadIdx.x;
   const int cg = tid & 31;          // channels 4cg .. 4cg+3
   const int hw = tid >> 5;          // word slot 0..7
@@ -140,15 +144,16 @@ __global__ __launch_bounds__(kQuantThreads) void pack_quant_kernel(
 #pragma unroll
       for (int half = 0; half < 32; half += kKeyBatch) {
         float4 v[kKeyBatch];
-        // unconditional loads: keys past n read key n-1 and are masked below
+        // unconditional loads: keys past the head's length read its last
+        // key and are masked below
 #pragma unroll
         for (int b = 0; b < kKeyBatch; ++b) {
-          const int64_t i = min<int64_t>(key0 + half + b, n - 1);
+          const int64_t i = min<int64_t>(key0 + half + b, last_key);
           v[b] = *reinterpret_cast<const float4*>(head_keys + i * stride_token);
         }
 #pragma unroll
         for (int b = 0; b < kKeyBatch; ++b) {
-          const bool valid = key0 + half + b < n;
+          const bool valid = key0 + half + b < nh;
           const float kv[4] = {v[b].x, v[b].y, v[b].z, v[b].w};
           uint32_t packed = 0u;
 #pragma unroll
@@ -206,10 +211,17 @@ __global__ __launch_bounds__(kQuantThreads) void pack_quant_kernel(
   }
 }
 
-__global__ void pack_final_kernel(int count, int64_t n, PackWorkspace ws, float* __restrict__ lo,
-                                  float* __restrict__ step, float* __restrict__ var) {
+__global__ void pack_final_kernel(int count, int64_t n_bound, const int32_t* __restrict__ lengths, PackWorkspace ws,
+                                  float* __restrict__ lo, float* __restrict__ step, float* __restrict__ var) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= count) return;
+  const int64_t n = head_length(lengths, i / kD, n_bound);
+  if (n == 0) {   // an empty head: no range, zero step and variance
+    lo[i] = 0.0f;
+    step[i] = 0.0f;
+    if (var) var[i] = 0.0f;
+    return;
+  }
   const float l = ordered_to_float(ws.kmin[i]);
   const float hi = ordered_to_float(ws.kmax[i]);
   const float r = __fsub_rn(hi, l);
@@ -227,29 +239,34 @@ __global__ void pack_final_kernel(int count, int64_t n, PackWorkspace ws, float*
   }
 }
 
-// Decode-time append: keys n .. n + m - 1 of every head are quantized with
-// the head's packed quantizer (lo, step fixed; inv = fl32(16 / fl32(16
-// step)), the packer's own inverse) and their codes, clamped to [0, 15],
-// written into the planes.  One thread per (head, channel, touched word)
-// builds the word's new bits for all four planes and replaces them
-// (read-modify-write; no other thread touches that word).
+// Decode-time append: keys n_h .. n_h + m - 1 of every head h (n_h = n, or
+// the head's own length) are quantized with the head's packed quantizer (lo,
+// step fixed; inv = fl32(16 / fl32(16 step)), the packer's own inverse) and
+// their codes, clamped to [0, 15], written into the planes.  One thread per
+// (head, channel, word slot) builds a touched word's new bits for all four
+// planes and replaces them (read-modify-write; no other thread touches that
+// word).  Slot wi is word n_h / 32 + wi; slots past the last touched word
+// return at once.
 __global__ __launch_bounds__(256) void append_kernel(const float* __restrict__ keys, int64_t stride_head,
-                                                     int64_t stride_token, int m, int64_t n, int64_t ldw,
-                                                     int64_t w0, int nw, int H, uint32_t* __restrict__ planes,
+                                                     int64_t stride_token, int m, int64_t n,
+                                                     const int32_t* __restrict__ lengths, int64_t ldw, int nw,
+                                                     int H, uint32_t* __restrict__ planes,
                                                      const float* __restrict__ lo, const float* __restrict__ step) {
   const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (gid >= int64_t(H) * kD * nw) return;
   const int wi = static_cast<int>(gid % nw);
   const int c = static_cast<int>((gid / nw) % kD);
   const int h = static_cast<int>(gid / (int64_t(nw) * kD));
-  const int64_t w = w0 + wi;
+  const int64_t nh = head_length(lengths, h, n);
+  const int64_t w = nh / 32 + wi;
+  if (w * 32 >= nh + m) return;            // (nh + m <= n + m <= 32 ldw, so w < ldw below)
   const float l = lo[h * kD + c];
   const float r = __fmul_rn(step[h * kD + c], 16.0f);   // exact power-of-two scaling
   const float inv = r > 0.0f ? __fdiv_rn(16.0f, r) : 0.0f;
   uint32_t mask = 0u, bits[kPlanes] = {0u, 0u, 0u, 0u};
-  const int64_t first = max(n, w * 32), last = min(n + m, w * 32 + 32);
+  const int64_t first = max(nh, w * 32), last = min(nh + m, w * 32 + 32);
   for (int64_t i = first; i < last; ++i) {
-    const float x = keys[int64_t(h) * stride_head + (i - n) * stride_token + c];
+    const float x = keys[int64_t(h) * stride_head + (i - nh) * stride_token + c];
     const float u = __fmul_rn(__fsub_rn(x, l), inv);
     const int code = static_cast<int>(fminf(fmaxf(floorf(u), 0.0f), 15.0f));
     const uint32_t b = 1u << static_cast<int>(i & 31);
@@ -262,27 +279,38 @@ __global__ __launch_bounds__(256) void append_kernel(const float* __restrict__ k
   for (int j = 0; j < kPlanes; ++j) row[j * ldw] = (row[j * ldw] & ~mask) | bits[j];
 }
 
+// After an append with per-head lengths: lengths[h] = n_h + m (a launch of
+// its own, so that every thread of the append has read the old length).
+__global__ void append_lengths_kernel(int32_t* __restrict__ lengths, int64_t n, int m, int H) {
+  const int h = blockIdx.x * blockDim.x + threadIdx.x;
+  if (h < H) lengths[h] = static_cast<int32_t>(head_length(lengths, h, n) + m);
+}
+
 }  // namespace
 
 hipError_t launch_append(const float* keys, int64_t stride_head, int64_t stride_token, int m, int H, int64_t n,
-                         int64_t ldw, uint32_t* planes, const float* lo, const float* step, hipStream_t stream) {
-  const int64_t w0 = n / 32, w1 = (n + m - 1) / 32;
-  const int nw = static_cast<int>(w1 - w0 + 1);
+                         int32_t* lengths, int64_t ldw, uint32_t* planes, const float* lo, const float* step,
+                         hipStream_t stream) {
+  // word slots per (head, channel): exactly the touched words for one
+  // start n, enough for any start with per-head lengths
+  const int nw = lengths ? (m + 31) / 32 + 1 : static_cast<int>((n + m - 1) / 32 - n / 32 + 1);
   const int64_t threads = int64_t(H) * kD * nw;
   const int blocks = static_cast<int>((threads + 255) / 256);
   hipLaunchKernelGGL(append_kernel, dim3(blocks), dim3(256), 0, stream, keys, stride_head, stride_token, m, n,
-                     ldw, w0, nw, H, planes, lo, step);
+                     lengths, ldw, nw, H, planes, lo, step);
+  if (lengths)
+    hipLaunchKernelGGL(append_lengths_kernel, dim3((H + 255) / 256), dim3(256), 0, stream, lengths, n, m, H);
   return hipGetLastError();
 }
 
 hipError_t launch_pack(const float* keys, int64_t stride_head, int64_t stride_token, int H, int64_t n,
-                       int64_t ldw, uint32_t* planes, float* lo, float* step, float* var,
+                       const int32_t* lengths, int64_t ldw, uint32_t* planes, float* lo, float* step, float* var,
                        const PackWorkspace& ws, hipStream_t stream) {
   const int count = H * kD;
   hipLaunchKernelGGL(pack_init_kernel, dim3((count + 255) / 256), dim3(256), 0, stream, ws, count);
   const int range_blocks = static_cast<int>((n + kRangeRows - 1) / kRangeRows);
   hipLaunchKernelGGL(pack_range_kernel, dim3(range_blocks, H), dim3(kRangeThreads), 0, stream, keys,
-                     stride_head, stride_token, n, ws);
+                     stride_head, stride_token, n, lengths, ws);
   // tiles cover every word of the padded rows, so padding words are written
   // as zero; about 1024 workgroups in total, whatever H
   const int num_tiles = static_cast<int>((ldw + kQuantWords - 1) / kQuantWords);
@@ -290,8 +318,8 @@ hipError_t launch_pack(const float* keys, int64_t stride_head, int64_t stride_to
   const int tiles_per_wg = static_cast<int>(std::max<int64_t>(1, (num_tiles + want - 1) / want));
   const int quant_blocks = (num_tiles + tiles_per_wg - 1) / tiles_per_wg;
   hipLaunchKernelGGL(pack_quant_kernel, dim3(quant_blocks, H), dim3(kQuantThreads), 0, stream, keys,
-                     stride_head, stride_token, n, ldw, num_tiles, tiles_per_wg, planes, ws);
-  hipLaunchKernelGGL(pack_final_kernel, dim3((count + 255) / 256), dim3(256), 0, stream, count, n, ws,
+                     stride_head, stride_token, n, lengths, ldw, num_tiles, tiles_per_wg, planes, ws);
+  hipLaunchKernelGGL(pack_final_kernel, dim3((count + 255) / 256), dim3(256), 0, stream, count, n, lengths, ws,
                      lo, step, var);
   return hipGetLastError();
 }

@@ -126,6 +126,7 @@ struct ScanArgs {
   int budget;           //   (budget bits) and writes them to alloc_out, which alloc then names
   uint8_t* alloc_out;
   int64_t n;
+  const int32_t* lengths;   // null, or keys per head (head_length clamps them to [0, n])
   int64_t ldw;
   int nwords;         // ceil(n / 32)
   int group;          // query heads per KV head
@@ -145,7 +146,24 @@ struct ScanArgs {
   int nsb;            // sampled blocks per head
   int chunks_per_head;
   void* tables;       // [H * chunks_per_head] ChunkTable, written by the sample kernel
+  int k;              // top-k
 };
+
+// Sampled blocks of a head of nh keys when every head has its own length:
+// nsb blocks, block i at 1024-key block i * stride (stride from the head's
+// own length, so the sample spreads over it).  Returns the stride; svalid
+// gets the number of sampled keys below nh.
+__device__ inline int ragged_sample(int64_t nh, int nsb, int& svalid) {
+  const int64_t nbl = (nh + kSampleBlockKeys - 1) / kSampleBlockKeys;
+  const int64_t stride = max<int64_t>(1, nbl / nsb);
+  int64_t sv = 0;
+  for (int i = 0; i < nsb; ++i) {
+    const int64_t left = nh - int64_t(i) * stride * kSampleBlockKeys;
+    sv += left <= 0 ? 0 : (left < kSampleBlockKeys ? left : kSampleBlockKeys);
+  }
+  svalid = static_cast<int>(sv);
+  return static_cast<int>(stride);
+}
 
 template <int GQ>
 struct UnionLds {
@@ -597,13 +615,28 @@ __device__ uint2 block_select_fn(int64_t count, uint32_t r, SelectLds& L, Get ge
 // least rsel sampled keys score >= theta.
 __global__ __launch_bounds__(kSelectThreads) void scan_threshold_kernel(
     const float* __restrict__ sample, int stot, uint32_t rsel, float* __restrict__ theta,
-    uint32_t* __restrict__ count) {
+    uint32_t* __restrict__ count, const int32_t* __restrict__ lengths, int64_t n, int k, int group, int nsb) {
   __shared__ SelectLds L;
   __shared__ DigitLds D;
   constexpr int PT = kSampleMaxKeys / kSelectThreads;
   static_assert(PT * kSelectThreads == kSampleMaxKeys, "one register per sample slot");
   const int q = blockIdx.x;
   const int tid = threadIdx.x;
+  if (lengths) {   // uniform: the rank from the query's own head length
+    const int64_t nh = head_length(lengths, q / group, n);
+    int svalid = 0;
+    ragged_sample(nh, nsb, svalid);
+    if (svalid == 0) {   // an empty head: no key passes
+      if (tid == 0) {
+        theta[q] = INFINITY;
+        count[q] = 0u;
+      }
+      return;
+    }
+    int64_t r = (2 * int64_t(k) * svalid + nh - 1) / nh;
+    r = max<int64_t>(r, min(svalid, 16));
+    rsel = static_cast<uint32_t>(min<int64_t>(r, svalid));
+  }
   uint32_t v[PT];
   // unconditional loads (the sample rows are allocated in full); slots past
   // the sample are masked afterwards
@@ -1080,8 +1113,10 @@ __global__ __launch_bounds__(kMainThreads, kMainWgPerCu * kMainWaves / 4) void s
     theta_s[threadIdx.x & 3] = (a.top_lists || static_cast<int>(threadIdx.x & 3) >= GQ) ? 0.0f : theta_in;
   }
   __syncthreads();
+  const int64_t nh = head_length(a.lengths, h, a.n);
+  const int head_tiles = static_cast<int>(((nh + 31) / 32 + kTileWords - 1) / kTileWords);
   const int tile_begin = blockIdx.x * a.tiles_per_wg;
-  const int tile_end = min(a.tiles, tile_begin + a.tiles_per_wg);
+  const int tile_end = min(min(a.tiles, head_tiles), tile_begin + a.tiles_per_wg);
   TileScanner scanner(a, T, ring, h, tile_begin, 1, tile_end - tile_begin);
   scanner.prologue();   // the first plane loads are in flight during the selection
   if (a.top_lists) {   // uniform
@@ -1120,8 +1155,8 @@ __global__ __launch_bounds__(kMainThreads, kMainWgPerCu * kMainWaves / 4) void s
     const int64_t key0 = column_key(tile, wave, col, 0);
     const int64_t key1 = kWaveX == 2 ? column_key(tile, wave, col, 1) : key0;
     auto key_of = [&](int i) { return (i < 8 ? key0 : key1) + (i & 7); };
-    const int nv0 = qvalid ? static_cast<int>(max<int64_t>(0, min<int64_t>(8, a.n - key0))) : 0;
-    const int nv1 = (kWaveX == 2 && qvalid) ? static_cast<int>(max<int64_t>(0, min<int64_t>(8, a.n - key1))) : 0;
+    const int nv0 = qvalid ? static_cast<int>(max<int64_t>(0, min<int64_t>(8, nh - key0))) : 0;
+    const int nv1 = (kWaveX == 2 && qvalid) ? static_cast<int>(max<int64_t>(0, min<int64_t>(8, nh - key1))) : 0;
     int tv[kWaveKeys];
     limb_sums(acc, tv);
     auto t_of = [&](int i) { return (i & 7) == 7 ? -tv[i] : tv[i]; };
@@ -1284,7 +1319,13 @@ __global__ __launch_bounds__(kMainThreads) void scan_sample_kernel(ScanArgs a) {
   const int col = lane & 15;
   const int G = lane >> 4;
   const int sbi = blockIdx.x;
-  const int tile = sbi * a.sample_stride;   // a sampled block is one tile
+  const int64_t nh = head_length(a.lengths, h, a.n);
+  int stride = a.sample_stride;
+  if (a.lengths) {   // uniform
+    int svalid_unused = 0;
+    stride = ragged_sample(nh, a.nsb, svalid_unused);
+  }
+  const int tile = sbi * stride;   // a sampled block is one tile
   TileScanner sc(a, T, ring, h, tile, 0, 1);
   sc.prologue();   // the block's plane words load while the limbs are built
   table_limbs<GQ>(s, T, wsum);
@@ -1300,7 +1341,7 @@ __global__ __launch_bounds__(kMainThreads) void scan_sample_kernel(ScanArgs a) {
       const int t = (i & 7) == 7 ? -tv[i] : tv[i];
       const float sc = fmaf(static_cast<float>(t), sigma, Cq);
       const int local = static_cast<int>(key - int64_t(tile_) * kTileWords * 32);
-      const float score = key < a.n ? sc : -INFINITY;
+      const float score = key < nh ? sc : -INFINITY;
       ok[i] = float_to_ordered(score);
       if (!a.top_lists) a.sample[int64_t(q0 + G) * kSampleMaxKeys + sbi * kSampleBlockKeys + local] = score;
     }
@@ -1423,7 +1464,9 @@ __device__ void sort_regs_desc(unsigned long long (&x)[E], unsigned long long* b
   }
 }
 
-// Sorts the first `kept` keys of buf (descending) and writes the first k.
+// Sorts the first `kept` keys of buf (descending) and writes the first k;
+// ranks at or past `kept` (a head holding fewer than k keys) get index -1
+// and score -inf.  Needs kSelectThreads * E >= max(kept, k).
 template <int E>
 __device__ void sort_and_write(unsigned long long* buf, unsigned kept, int k, int q,
                                int32_t* __restrict__ out_idx, float* __restrict__ out_score) {
@@ -1437,8 +1480,9 @@ __device__ void sort_and_write(unsigned long long* buf, unsigned kept, int k, in
   for (int e = 0; e < E; ++e) {
     const unsigned i = t * E + e;
     if (i < static_cast<unsigned>(k)) {
-      out_idx[int64_t(q) * k + i] = static_cast<int32_t>(~static_cast<uint32_t>(x[e]));
-      out_score[int64_t(q) * k + i] = ordered_to_float(static_cast<uint32_t>(x[e] >> 32));
+      const bool real = i < kept;
+      out_idx[int64_t(q) * k + i] = real ? static_cast<int32_t>(~static_cast<uint32_t>(x[e])) : -1;
+      out_score[int64_t(q) * k + i] = real ? ordered_to_float(static_cast<uint32_t>(x[e] >> 32)) : -INFINITY;
     }
   }
 }
@@ -1630,8 +1674,11 @@ __global__ __launch_bounds__(kSelectThreads) void scan_merge_kernel(ScanArgs a, 
     // them ahead of the count test instead of sinking them into the fast path)
 #pragma unroll
     for (int j = 0; j < kSpecSlots; ++j) asm volatile("" : : "v"(v[j]), "v"(id[j]));
-    // exact fallback: radix select over recomputed scores
+    // exact fallback: radix select over recomputed scores, of the head's nh
+    // keys; a head holding fewer than k keys returns all of them
     const int h = q / a.group;
+    const int64_t nh = head_length(a.lengths, h, a.n);
+    const int keff = static_cast<int>(min<int64_t>(k, nh));
     const uint32_t* head_planes = a.planes + int64_t(h) * kD * kPlanes * a.ldw;
     if (tid < kD) {
       const float lo = a.lo[h * kD + tid], st = a.step[h * kD + tid];
@@ -1646,18 +1693,18 @@ __global__ __launch_bounds__(kSelectThreads) void scan_merge_kernel(ScanArgs a, 
     __syncthreads();
     if (tid == 0) qs.C = static_cast<float>(qs.cpart[0] + qs.cpart[1]);
     __syncthreads();
-    const uint2 sel = block_select_fn(a.n, static_cast<uint32_t>(k), L, [&](int64_t i) {
+    const uint2 sel = keff > 0 ? block_select_fn(nh, static_cast<uint32_t>(keff), L, [&](int64_t i) {
       return float_to_ordered(query_score(head_planes, a.ldw, qs, i));
-    });
-    const uint32_t kth = sel.x;                                   // ordered score of the k-th key
+    }) : make_uint2(0xffffffffu, 0u);   // (uniform; nothing to select)
+    const uint32_t kth = sel.x;                                   // ordered score of the keff-th key
     const uint32_t need_eq = sel.y;                               // ties at kth to take
-    const uint32_t n_gt = static_cast<uint32_t>(k) - need_eq;     // keys strictly above it
+    const uint32_t n_gt = static_cast<uint32_t>(keff) - need_eq;  // keys strictly above it
     if (tid == 0) s_count[0] = 0;
     __syncthreads();
     uint32_t eq_taken = 0;
-    for (int64_t base = 0; base < a.n; base += blockDim.x) {
+    for (int64_t base = 0; base < (keff > 0 ? nh : 0); base += blockDim.x) {
       const int64_t i = base + tid;
-      const bool valid = i < a.n;
+      const bool valid = i < nh;
       const uint32_t v = valid ? float_to_ordered(query_score(head_planes, a.ldw, qs, i)) : 0u;
       const bool gt = valid && v > kth;
       const bool eq = valid && v == kth;
@@ -1682,16 +1729,18 @@ __global__ __launch_bounds__(kSelectThreads) void scan_merge_kernel(ScanArgs a, 
       __syncthreads();
     }
     __syncthreads();
-    kept = static_cast<unsigned>(k);
+    kept = static_cast<unsigned>(keff);
   }
-  // kept >= k keys in keys[0, kept): sort them and write the first k
-  if (kept <= kSelectThreads) {
+  // keys[0, kept) hold the kept keys (kept >= k unless the head holds fewer
+  // than k): sort them and write the first k
+  const unsigned span = max(kept, static_cast<unsigned>(k));
+  if (span <= kSelectThreads) {
     sort_and_write<1>(keys, kept, k, q, out_idx, out_score);
-  } else if (kept <= 2 * kSelectThreads) {
+  } else if (span <= 2 * kSelectThreads) {
     sort_and_write<2>(keys, kept, k, q, out_idx, out_score);
-  } else if (kept <= 4 * kSelectThreads) {
+  } else if (span <= 4 * kSelectThreads) {
     sort_and_write<4>(keys, kept, k, q, out_idx, out_score);
-  } else if (kept <= 8 * kSelectThreads) {
+  } else if (span <= 8 * kSelectThreads) {
     sort_and_write<8>(keys, kept, k, q, out_idx, out_score);
   } else {
     sort_and_write<16>(keys, kept, k, q, out_idx, out_score);
@@ -1725,11 +1774,13 @@ void launch_class(int gq, const ScanArgs& a, int H, int nsb, bool sample_phase, 
 }  // namespace
 
 hipError_t launch_scan_topk(const uint32_t* planes, const float* lo, const float* step, int H,
-                            int64_t n, int64_t ldw, const float* q, const uint8_t* alloc, int num_q,
-                            int group, int k, int32_t* out_idx, float* out_score,
+                            int64_t n, const int32_t* lengths, int64_t ldw, const float* q, const uint8_t* alloc,
+                            int num_q, int group, int k, int32_t* out_idx, float* out_score,
                             float* all_scores, const ScanWorkspace& ws, const ScanTiming* timing,
                             hipStream_t stream, const float* var, int budget, uint8_t* alloc_out) {
   ScanArgs a{};
+  a.lengths = lengths;
+  a.k = k;
   a.planes = planes;
   a.lo = lo;
   a.step = step;
@@ -1778,7 +1829,9 @@ hipError_t launch_scan_topk(const uint32_t* planes, const float* lo, const float
   if (rsel < rmin) rsel = rmin;
   if (rsel > svalid) rsel = svalid;
   a.rsel = static_cast<int>(rsel);
-  a.top_lists = rsel <= kTopR ? 1 : 0;
+  // With per-head lengths the rank differs per head: the threshold kernel
+  // takes each query's rank from its head's length.
+  a.top_lists = (rsel <= kTopR && !lengths) ? 1 : 0;
   a.nsb = nsb;
 
   // main-kernel work split: each workgroup takes a contiguous run of tiles
@@ -1811,7 +1864,8 @@ hipError_t launch_scan_topk(const uint32_t* planes, const float* lo, const float
     }
     if (sample_phase && !a.top_lists) {
       hipLaunchKernelGGL(scan_threshold_kernel, dim3(num_q), dim3(kSelectThreads), 0, stream, ws.sample,
-                         nsb * kSampleBlockKeys, static_cast<uint32_t>(rsel), ws.theta, ws.count);
+                         nsb * kSampleBlockKeys, static_cast<uint32_t>(rsel), ws.theta, ws.count, lengths, n, k,
+                         group, nsb);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

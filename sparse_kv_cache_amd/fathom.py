@@ -57,6 +57,7 @@ class StoreDesc(ctypes.Structure):
         ("d", ctypes.c_int32),
         ("n", ctypes.c_int64),
         ("ldw", ctypes.c_int64),
+        ("lengths", ctypes.c_void_p),
     ]
 
 
@@ -125,8 +126,14 @@ def plane_ldw(n: int) -> int:
     return int(lib.fathom_plane_ldw(n))
 
 
-def store_desc(num_kv_heads: int, n: int, d: int = 128, ldw: Optional[int] = None) -> StoreDesc:
-    return StoreDesc(num_kv_heads, d, n, plane_ldw(n) if ldw is None else ldw)
+def store_desc(num_kv_heads: int, n: int, d: int = 128, ldw: Optional[int] = None,
+               lengths: Optional[torch.Tensor] = None) -> StoreDesc:
+    """Store descriptor; ``lengths`` (int32 [H] on the GPU) gives each head its
+    own number of keys (at most n).  The caller keeps that tensor alive."""
+    if lengths is not None:
+        assert lengths.dtype == torch.int32 and lengths.numel() == num_kv_heads and lengths.is_contiguous()
+    return StoreDesc(num_kv_heads, d, n, plane_ldw(n) if ldw is None else ldw,
+                     None if lengths is None else lengths.data_ptr())
 
 
 def workspace_bytes(op: int, store: StoreDesc, num_q: int = 1, k: int = 1) -> int:
@@ -166,13 +173,14 @@ def pack_planes(keys: torch.Tensor, store: Optional[StoreDesc] = None, *, with_v
 def append_keys(keys: torch.Tensor, store: StoreDesc, planes: torch.Tensor, lo: torch.Tensor,
                 step: torch.Tensor, stream=None) -> StoreDesc:
     """Write keys float32 [H, m, d] (token stride may exceed d) as keys
-    store.n .. store.n + m - 1 of every head; returns the store grown by m."""
+    store.n .. store.n + m - 1 of every head (with per-head lengths: at each
+    head's own length, which grows by m); returns the store grown by m."""
     assert keys.dtype == torch.float32 and keys.dim() == 3 and keys.stride(2) == 1
     H, m, d = keys.shape
     st = lib.fathom_append_keys(_ptr(keys), keys.stride(0), keys.stride(1), m, ctypes.byref(store), _ptr(planes),
                                 _ptr(lo), _ptr(step), _stream(stream))
     _check(st, "fathom_append_keys")
-    return StoreDesc(store.num_kv_heads, store.d, store.n + m, store.ldw)
+    return StoreDesc(store.num_kv_heads, store.d, store.n + m, store.ldw, store.lengths)
 
 
 def allocate(q: torch.Tensor, var: torch.Tensor, group: int, budget: int,

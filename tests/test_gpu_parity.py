@@ -693,3 +693,109 @@ def test_multi_session_full_size(multi_store, budget):
             i = h * G + g
             s_ref = oracle_scores(codes, lo_ref, st_ref, M["q"][i], alloc[i])
             check_topk(idx[i], val[i], s_ref, w.k, n)
+
+
+# ------------------------------------------------- ragged per-head lengths
+
+def check_ragged_query(idx_i, val_i, s_ref, k, nh):
+    """The first min(k, nh) ranks against the oracle's top-k of the head's nh
+    keys; the rest must be (-1, -inf)."""
+    m = min(k, nh)
+    ref_idx, ref_val = O.topk_padded(s_ref, k)
+    assert np.all(idx_i[m:] == -1) and np.all(np.isneginf(val_i[m:]))
+    if m:
+        check_topk(idx_i[:m], val_i[:m], s_ref, m, nh)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("lengths,n,G,B,k", [
+    ([70000, 0, 300, 1, 4097, 33333, 65537, 69999], 70000, 4, 92, 400),
+    ([131072, 20011, 99999, 131071, 47000, 8193, 120000, 64000,
+      1000, 131072, 77777, 30000, 111111, 5000, 90001, 128000], 131072, 4, 68, 1024),
+])
+def test_ragged_lengths_pack_scan_append(lengths, n, G, B, k):
+    """A batch of heads with their own lengths (some not multiples of 32 or
+    1024, one empty, some shorter than k) in one store: per-head packing,
+    the fused and the two-call scans, appends at each head's own length and
+    the scan of the grown store, all against the oracle run head by head on
+    that head's keys only."""
+    H = len(lengths)
+    m_app = 37
+    say("ragged lengths", H, n, G, B, k)
+    keys, q = synth.make_inputs(900 + H, H, n, H * G)
+    new_keys, _ = synth.make_inputs(901 + H, H, m_app, 1)
+    ln = dev(np.array(lengths, np.int32))
+    store = fa.store_desc(H, n, 128, ldw=fa.plane_ldw(n + m_app), lengths=ln)
+    kd = dev(keys)
+    planes = torch.empty((H, 128, 4, store.ldw), dtype=torch.int32, device=DEV)
+    _, lo, step, var = fa.pack_planes(kd, store, planes=planes)
+    planes_h, lo_h, step_h, var_h = host(planes).view(np.uint32), host(lo), host(step), host(var)
+    check = range(H) if H <= 8 else (0, 1, 4, 5, 8, 13)
+    refs = {}
+    for h in range(H):
+        if h not in check:
+            continue
+        p_ref, lo_ref, st_ref, var_ref, codes = O.pack_head(keys[h, :lengths[h]], ldw=store.ldw)
+        assert np.array_equal(planes_h[h], p_ref), h
+        assert np.array_equal(lo_h[h], lo_ref) and np.array_equal(step_h[h], st_ref), h
+        assert np.array_equal(var_h[h], var_ref), h
+        refs[h] = (lo_ref, st_ref, codes)
+    qd = dev(q)
+    alloc, idx, val = fa.allocate_scan_topk(planes, lo, step, var, store, qd, G, B, k)
+    alloc, idx, val = host(alloc), host(idx), host(val)
+    assert np.array_equal(alloc, O.allocate_all(q, var_h, G, B))
+    sc = torch.full((H * G, n), np.nan, dtype=torch.float32, device=DEV)
+    idx2, val2 = fa.scan_topk(planes, lo, step, store, qd, dev(alloc), G, k, all_scores=sc)
+    assert np.array_equal(host(idx2), idx) and np.array_equal(host(val2), val)
+    sc = host(sc)
+    for h in refs:
+        lo_ref, st_ref, codes = refs[h]
+        for g in range(G):
+            i = h * G + g
+            s_ref = oracle_scores(codes, lo_ref, st_ref, q[i], alloc[i]) if lengths[h] else np.zeros(0)
+            check_ragged_query(idx[i], val[i], s_ref, k, lengths[h])
+            if lengths[h]:
+                check_scores(sc[i, :lengths[h]], s_ref)
+            assert np.all(np.isnan(sc[i, lengths[h]:])), "scores past the head's length are not written"
+    # appends at each head's own length
+    store2 = fa.append_keys(dev(new_keys), store, planes, lo, step)
+    assert np.array_equal(host(ln), np.array(lengths, np.int32) + m_app)
+    assert store2.n == n + m_app
+    planes_h = host(planes).view(np.uint32)
+    for h in refs:
+        lo_ref, st_ref, codes = refs[h]
+        p_ref = O.pack_head(keys[h, :lengths[h]], ldw=store.ldw)[0]
+        new_codes = O.append_codes(new_keys[h], lo_ref, st_ref)
+        assert np.array_equal(planes_h[h], O.append_planes(p_ref, lengths[h], new_codes)), h
+        refs[h] = (lo_ref, st_ref, np.concatenate([codes, new_codes]))
+    alloc, idx, val = fa.allocate_scan_topk(planes, lo, step, var, store2, qd, G, B, k)
+    alloc, idx, val = host(alloc), host(idx), host(val)
+    for h in refs:
+        lo_ref, st_ref, codes = refs[h]
+        for g in range(G):
+            i = h * G + g
+            s_ref = oracle_scores(codes, lo_ref, st_ref, q[i], alloc[i])
+            check_ragged_query(idx[i], val[i], s_ref, k, lengths[h] + m_app)
+
+
+def test_ragged_lengths_attention_skips_rows_past_length():
+    say("ragged attention")
+    lengths = [5000, 0, 17, 2500]
+    H, n, G, k = 4, 5000, 2, 64
+    keys, q = synth.make_inputs(71, H, n, H * G)
+    vals = np.stack([synth.head_values(71, h, n) for h in range(H)])
+    kd, k64 = _bf16_rows(keys)
+    vd, v64 = _bf16_rows(vals)
+    ln = dev(np.array(lengths, np.int32))
+    store = fa.store_desc(H, n, 128, lengths=ln)
+    rng = np.random.default_rng(8)
+    idx = rng.choice(n, (H * G, k)).astype(np.int32)
+    out = host(fa.sparse_attention(kd, vd, store, dev(q), dev(idx), G))
+    for i in range(H * G):
+        h = i // G
+        ok = idx[i][idx[i] < lengths[h]]
+        if ok.size == 0:
+            assert np.all(out[i] == 0)
+            continue
+        ref = O.sparse_attention(k64[h], v64[h], q[i], ok, 128 ** -0.5)
+        assert np.abs(out[i] - ref).max() <= 1e-4 * np.abs(v64[h][ok]).max()

@@ -136,3 +136,31 @@ def test_decode_step_gqa_mapping():
         s = O.scores_from_codes(res["codes"][h], res["lo"][h], res["step"][h], q[i], b)
         assert np.array_equal(res["scores"][i], s)
         assert res["alloc"][i].sum() == 40
+
+
+def test_topk_padded_short_and_empty_heads():
+    """Ranks past a short head's length are (-1, -inf); the rest is the plain
+    top-k (checked against a brute-force sorted())."""
+    rng = np.random.default_rng(3)
+    s = rng.integers(0, 5, 7).astype(np.float64)          # ties on purpose
+    idx, val = O.topk_padded(s, 10)
+    ref = sorted(range(7), key=lambda i: (-s[i], i))
+    assert idx[:7].tolist() == ref and np.all(idx[7:] == -1)
+    assert np.all(val[7:] == -np.inf) and np.array_equal(val[:7], s[ref].astype(np.float32))
+    idx, val = O.topk_padded(s, 4)
+    assert idx.tolist() == ref[:4]
+    idx, val = O.topk_padded(np.zeros(0), 3)
+    assert idx.tolist() == [-1, -1, -1] and np.all(np.isneginf(val))
+
+
+def test_pack_head_empty_and_padded_rows():
+    """An empty head packs to zeros; a longer row only adds zero words to the
+    planes of the default row length."""
+    p, lo, st, var, codes = O.pack_head(np.zeros((0, 8), np.float32), ldw=12)
+    assert p.shape == (8, 4, 12) and not p.any() and not lo.any() and not st.any() and not var.any()
+    keys = np.random.default_rng(4).standard_normal((70, 8)).astype(np.float32)
+    a = O.pack_head(keys)
+    b = O.pack_head(keys, ldw=16)
+    assert np.array_equal(b[0][:, :, :a[0].shape[2]], a[0]) and not b[0][:, :, a[0].shape[2]:].any()
+    for x, y in zip(a[1:], b[1:]):
+        assert np.array_equal(x, y)
