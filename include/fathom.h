@@ -212,15 +212,17 @@ int fathom_allocate_scan_topk(const uint32_t* planes, const float* lo, const flo
  * GPU, held from the first such call on that GPU until the process ends)
  * instead of a caller workspace.  The call allocates nothing and takes no
  * workspace; the caller still passes every input and output.
- * Limits: num_q <= FATHOM_NOALLOC_MAX_Q (query heads per call), else
- * FATHOM_ERR_UNSUPPORTED and nothing is launched.  Runs on the current HIP
+ * Limits: num_q <= FATHOM_NOALLOC_MAX_Q (query heads per call) and
+ * fathom_workspace_bytes(FATHOM_OP_SCAN, store, num_q, k) <=
+ * FATHOM_NOALLOC_SCRATCH_BYTES (the 1M-key, 32-query, k = 2048 step needs
+ * about 8 MiB), else FATHOM_ERR_UNSUPPORTED and nothing is launched.  Runs on the current HIP
  * device; hip_stream must belong to it.  Every call on one GPU shares that
  * GPU's array (each call rewrites what it reads), so calls that overlap in
  * time on one GPU -- on two streams, or from two threads -- race and must be
  * serialized by the caller.  The first call on a device looks up the array's
  * address (hipGetSymbolAddress) and may fail with FATHOM_ERR_HIP. */
 #define FATHOM_NOALLOC_MAX_Q 64
-#define FATHOM_NOALLOC_SCRATCH_BYTES (12 << 20)
+#define FATHOM_NOALLOC_SCRATCH_BYTES (16 << 20)
 int fathom_allocate_scan_topk_noalloc(const uint32_t* planes, const float* lo, const float* step, const float* var,
                                       const fathom_store_desc* store, const float* q, int32_t num_q, int32_t group,
                                       int32_t budget_bits, int32_t k, uint8_t* alloc, int32_t* out_idx,

@@ -93,17 +93,24 @@ PackLayout pack_layout(int H) {
 }
 
 struct ScanLayout {
-  size_t theta, count, sample, cand, tables, total;
+  size_t theta, count, sample, cand, tables, rescue, rescue_cnt, rescue_hist, rescue_done, total;
+  int rescue_wgs;
 };
-ScanLayout scan_layout(int num_q) {
+ScanLayout scan_layout(int num_q, int64_t n, int k) {
   const size_t Q = static_cast<size_t>(num_q);
   ScanLayout L{};
+  L.rescue_wgs = rescue_wgs_for(n);
+  const size_t R = static_cast<size_t>(L.rescue_wgs);
   size_t off = 0;
   L.theta = off;  off = round_up(off + Q * 4, 256);
   L.count = off;  off = round_up(off + Q * 4, 256);
   L.sample = off; off = round_up(off + Q * kSampleMaxKeys * 4, 256);
   L.cand = off;   off = round_up(off + Q * kCandCap * 8, 256);
   L.tables = off; off = round_up(off + Q * kChunkTableBytes, 256);
+  L.rescue = off; off = round_up(off + size_t(kRescueSlots) * R * size_t(k) * 8, 256);
+  L.rescue_cnt = off;  off = round_up(off + size_t(kRescueSlots) * R * 8, 256);
+  L.rescue_hist = off; off = round_up(off + size_t(kRescueSlots) * kRescueHistBins * 4, 256);
+  L.rescue_done = off; off = round_up(off + size_t(kRescueSlots) * 4, 256);
   L.total = off;
   return L;
 }
@@ -151,14 +158,17 @@ int scan_impl(const char* where, const uint32_t* planes, const float* lo, const 
   if (!aligned(lo, 4) || !aligned(step, 4) || !aligned(q, 4) || !aligned(out_idx, 4) ||
       !aligned(out_score, 4) || (all_scores && !aligned(all_scores, 4)))
     return fail(FATHOM_ERR_INVALID_ARG, "float and int32 arrays must be 4-byte aligned");
-  const ScanLayout L = scan_layout(num_q);
+  const ScanLayout L = scan_layout(num_q, store->n, k);
   if (!workspace || !aligned(workspace, 256) || workspace_bytes < L.total)
     return fail(FATHOM_ERR_WORKSPACE, "scan needs a 256-byte aligned workspace of %zu bytes (got %zu)",
                 L.total, workspace_bytes);
   char* w = static_cast<char*>(workspace);
   ScanWorkspace ws{reinterpret_cast<float*>(w + L.theta), reinterpret_cast<uint32_t*>(w + L.count),
                    reinterpret_cast<float*>(w + L.sample), reinterpret_cast<uint2*>(w + L.cand),
-                   static_cast<void*>(w + L.tables)};
+                   static_cast<void*>(w + L.tables), reinterpret_cast<uint2*>(w + L.rescue),
+                   reinterpret_cast<uint2*>(w + L.rescue_cnt), reinterpret_cast<uint32_t*>(w + L.rescue_hist),
+                   reinterpret_cast<uint32_t*>(w + L.rescue_done),
+                   L.rescue_wgs};
 
   ScanTiming timing;
   bool timed = false;
@@ -199,8 +209,8 @@ size_t fathom_workspace_bytes(int32_t op, const fathom_store_desc* store, int32_
   if (check_store(store) != FATHOM_OK) return 0;
   if (op == FATHOM_OP_PACK) return pack_layout(store->num_kv_heads).total;
   if (op == FATHOM_OP_SCAN) {
-    if (num_q < 1 || k < 1) return 0;
-    return scan_layout(num_q).total;
+    if (num_q < 1 || k < 1 || k > kMaxK) return 0;
+    return scan_layout(num_q, store->n, k).total;
   }
   if (op == FATHOM_OP_ATTEND) {
     if (num_q < 1 || k < 1 || k > kMaxK) return 0;
@@ -321,7 +331,8 @@ int fathom_allocate_scan_topk_noalloc(const uint32_t* planes, const float* lo, c
   if (num_q < 1 || num_q > FATHOM_NOALLOC_MAX_Q)
     return fail(FATHOM_ERR_UNSUPPORTED, "num_q = %d outside [1, %d] for the allocation-free call", num_q,
                 FATHOM_NOALLOC_MAX_Q);
-  const size_t need = scan_layout(num_q).total;
+  if (!store || k < 1 || k > kMaxK) return fail(FATHOM_ERR_INVALID_ARG, "store must be non-NULL and 1 <= k <= %d", kMaxK);
+  const size_t need = scan_layout(num_q, store->n, k).total;
   if (need > FATHOM_NOALLOC_SCRATCH_BYTES)
     return fail(FATHOM_ERR_UNSUPPORTED, "the call needs %zu scratch bytes, above the static %d", need,
                 FATHOM_NOALLOC_SCRATCH_BYTES);

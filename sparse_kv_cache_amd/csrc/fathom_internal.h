@@ -15,6 +15,14 @@ constexpr int kSampleBlockKeys = 1024;  // keys per sampled block (32 plane word
 constexpr int kSampleMaxBlocks = 8;     // sampled blocks per KV head
 constexpr int kSampleMaxKeys = kSampleBlockKeys * kSampleMaxBlocks;
 constexpr int kQueryChunk = 4;     // query heads scored together per workgroup
+// Rescue of queries whose candidate list missed (too short or overflowed):
+// up to kRescueSlots such queries per call are rescored by workgroups of the
+// merge launch, each taking a slice of at most kRescueSlice keys of the head
+// (at most kRescueMaxWgs slices, so heads up to 4M keys).
+constexpr int kRescueSlots = 2;
+constexpr int kRescueSlice = 16384;
+constexpr int kRescueMaxWgs = 256;
+constexpr int kRescueHistBins = 2048;
 constexpr int64_t kMaxKeys = int64_t(1) << 26;
 // One head's plane block (d * 4 rows of ldw words) is addressed with 32-bit
 // byte offsets; the largest block is therefore 2^32 - 1 bytes (ldw <=
@@ -82,7 +90,19 @@ struct ScanWorkspace {
   float* sample;     // [Q][kSampleMaxKeys] scores of the sampled keys
   uint2* cand;       // [Q][kCandCap] (score bits, key index)
   void* tables;      // [Q][kChunkTableBytes] per (KV head, query chunk) scan tables (at most Q chunks)
+  uint2* rescue;     // [kRescueSlots][rescue_wgs][k] per-slice top-k lists (ordered score, index)
+  uint2* rescue_cnt;       // [kRescueSlots][rescue_wgs] entries in each list, and its lowest (ordered) score
+  uint32_t* rescue_hist;   // [kRescueSlots][kRescueHistBins] digits of all list entries
+  uint32_t* rescue_done;   // [kRescueSlots] slices finished
+  int rescue_wgs;          // slices (workgroups) per rescued query; 0: no rescue
 };
+
+// Rescue slices for heads of up to n keys (0 when a slice would exceed
+// kRescueSlice keys).
+inline int rescue_wgs_for(int64_t n) {
+  const int64_t r = (n + kRescueSlice - 1) / kRescueSlice;
+  return r <= kRescueMaxWgs ? static_cast<int>(r < 1 ? 1 : r) : 0;
+}
 
 struct ScanTiming {
   hipEvent_t start = nullptr;

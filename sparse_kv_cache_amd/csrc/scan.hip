@@ -147,6 +147,12 @@ struct ScanArgs {
   int chunks_per_head;
   void* tables;       // [H * chunks_per_head] ChunkTable, written by the sample kernel
   int k;              // top-k
+  int num_q;          // query heads of the call
+  uint2* rescue;      // rescue lists, counts, histograms and finished-slice counters (see the merge)
+  uint2* rescue_cnt;
+  uint32_t* rescue_hist;
+  uint32_t* rescue_done;
+  int rescue_wgs;
 };
 
 // Sampled blocks of a head of nh keys when every head has its own length:
@@ -533,6 +539,7 @@ __device__ uint2 block_select_regs(const uint32_t (&v)[PT], uint32_t pm, uint32_
 
 constexpr int kDigitBits = 11;
 constexpr int kBins = 1 << kDigitBits;
+static_assert(kBins == kRescueHistBins, "the rescue histograms use the digit's bins");
 constexpr int kBucketMax = 64;          // largest bucket the merge orders by counting
 static_assert(kBins == 2 * kSelectThreads, "the scan gives each thread two bins");
 
@@ -1078,6 +1085,7 @@ __global__ __launch_bounds__(kMainThreads, kMainWgPerCu * kMainWaves / 4) void s
   __shared__ uint32_t wkept[kMainWaves][4];
   __shared__ uint32_t wbase_s[kMainWaves][4];
   __shared__ float theta_s[4];
+  __shared__ uint32_t full_s[4];   // the query's global list has overflowed (seen by this workgroup)
   const int h = blockIdx.y / a.cph;
   const int q0 = h * a.group + a.qoff + (blockIdx.y % a.cph) * kQueryChunk;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
@@ -1111,6 +1119,7 @@ __global__ __launch_bounds__(kMainThreads, kMainWgPerCu * kMainWaves / 4) void s
     // (every thread stores, the same value per slot: a store under a branch
     // would pull the load into it)
     theta_s[threadIdx.x & 3] = (a.top_lists || static_cast<int>(threadIdx.x & 3) >= GQ) ? 0.0f : theta_in;
+    full_s[threadIdx.x & 3] = 0u;
   }
   __syncthreads();
   const int64_t nh = head_length(a.lengths, h, a.n);
@@ -1192,9 +1201,19 @@ __global__ __launch_bounds__(kMainThreads, kMainWgPerCu * kMainWaves / 4) void s
     if (__ballot(spill != 0) != 0) {   // uniform
       // the last lane of each query's row reserves the row's spilled slots:
       // one atomic per query, all in flight together
+      // Once a query's list has overflowed (count > kCandCap: the merge
+      // rescues it) further slots are useless: no more atomics on its count,
+      // and its candidates are not walked.
       const uint32_t sincl = row_incl_sum(spill);
       uint32_t gb = 0;
-      if (col == 15 && qvalid && sincl != 0) gb = atomicAdd(&a.count[q0 + G], sincl);
+      if (col == 15 && qvalid && sincl != 0) {
+        if (full_s[G]) {
+          gb = 0x40000000u;
+        } else {
+          gb = atomicAdd(&a.count[q0 + G], sincl);
+          if (gb + sincl > static_cast<uint32_t>(kCandCap)) full_s[G] = 1u;
+        }
+      }
       uint32_t rb = 0;
 #pragma unroll
       for (int g = 0; g < GQ; ++g) {
@@ -1203,7 +1222,7 @@ __global__ __launch_bounds__(kMainThreads, kMainWgPerCu * kMainWaves / 4) void s
       }
       gpos = rb + sincl - spill;
     }
-    if (bits != 0) {
+    if (bits != 0 && gpos < 0x40000000u) {
       // Lanes pass few keys: walk the set bits only.  The key's t is picked
       // from the registers by a select tree on the bits of its index (a
       // computed index into tv would move it to scratch).
@@ -1300,8 +1319,13 @@ __global__ __launch_bounds__(kMainThreads) void scan_sample_kernel(ScanArgs a) {
   const UnionInputs in = load_union_inputs<GQ>(a, h, q0);   // in flight during the allocation
   const uint8_t* ab = a.alloc + int64_t(q0) * kD;
   // the main kernel's candidate counts start at 0 (on the path without
-  // per-block lists the threshold kernel resets them)
+  // per-block lists the threshold kernel resets them), and so do the merge's
+  // rescue counters
   if (a.top_lists && blockIdx.x == 0 && static_cast<int>(threadIdx.x) < GQ) a.count[q0 + threadIdx.x] = 0u;
+  if (blockIdx.x == 0 && blockIdx.y == 0) {
+    if (static_cast<int>(threadIdx.x) < kRescueSlots) a.rescue_done[threadIdx.x] = 0u;
+    for (int i = threadIdx.x; i < kRescueSlots * kRescueHistBins; i += blockDim.x) a.rescue_hist[i] = 0u;
+  }
   if (a.var) {   // uniform
     if (wave < GQ) {
       // (the ring is free until the plane loads start: 64 words per wavefront)
@@ -1487,46 +1511,539 @@ __device__ void sort_and_write(unsigned long long* buf, unsigned kept, int k, in
   }
 }
 
-struct QueryLds {
-  float w[kD][kPlanes];
-  uint8_t b[kD];
-  double cpart[2];
-  float C;
+// What the merge needs to score keys of one query exactly as the main kernel
+// does: the query's nonzero fixed-point plane weights V (recombined from the
+// chunk table's int8 limbs), their rows, and the scale and offset.  The score
+// of key i is fmaf(float(t), sigma, C) with t = sum V bit_p(i), an exact
+// integer (wrapping int32 sums are exact because |t| < 2^31).
+struct QueryPlan {
+  uint32_t rowoff[kMaxUnion];   // byte offset of the plane row in the head
+  int32_t V[kMaxUnion];
+  uint32_t np;                  // planes with V != 0
+  uint32_t tneg, tpos;          // sums of the negative and of the positive V: t lies in [tneg, tpos]
+  float sigma, C;
 };
-
-// Score of key i for one query, plane by plane (fallback path).
-__device__ inline float query_score(const uint32_t* head_planes, int64_t ldw, const QueryLds& s,
-                                    int64_t i) {
-  const uint32_t* base = head_planes + (i >> 5);
-  const int bit = static_cast<int>(i & 31);
-  float acc = 0.0f;
-  for (int c = 0; c < kD; ++c) {
-    const int bc = s.b[c];
-    for (int j = 0; j < bc; ++j) {
-      const uint32_t x = base[int64_t(c * kPlanes + j) * ldw];
-      acc = fmaf(static_cast<float>((x >> bit) & 1u), s.w[c][j], acc);
-    }
-  }
-  return acc + s.C;
+// The plan sits at the end of the merge's sort buffer, behind the kept keys
+// and the digit tables.
+constexpr int kPlanSlots = static_cast<int>((sizeof(QueryPlan) + 7) / 8);
+static_assert(kFastKept + (sizeof(DigitLds) + 7) / 8 + kPlanSlots <= kCandCap, "the plan fits behind the digit tables");
+__device__ inline QueryPlan& plan_in(unsigned long long* keys) {
+  return *reinterpret_cast<QueryPlan*>(keys + kCandCap - kPlanSlots);
 }
 
-__global__ __launch_bounds__(kSelectThreads) void scan_merge_kernel(ScanArgs a, int k,
+// An 11-bit digit of the ordered scores of one query, placed below the bits
+// that every possible score shares (all scores lie between the scores of
+// t = tneg and t = tpos): digit(o) = (o >> shift) & mask, and bucket b holds
+// the scores from common | (b << shift) up.
+struct PlanDigit {
+  uint32_t shift, mask, common;
+};
+__device__ inline PlanDigit plan_digit(const QueryPlan& P) {
+  const uint32_t o_lo = float_to_ordered(fmaf(static_cast<float>(static_cast<int32_t>(P.tneg)), P.sigma, P.C));
+  const uint32_t o_hi = float_to_ordered(fmaf(static_cast<float>(static_cast<int32_t>(P.tpos)), P.sigma, P.C));
+  const uint32_t diff = o_lo ^ o_hi;
+  const int hi = diff ? 32 - __clz(diff) : 0;   // bits >= hi are common
+  const int width = min(kDigitBits, hi), shift = hi - width;
+  PlanDigit d;
+  d.shift = static_cast<uint32_t>(shift);
+  d.mask = (1u << width) - 1u;
+  d.common = hi >= 32 ? 0u : (o_lo & ~((1u << hi) - 1u));
+  return d;
+}
+
+// Whole workgroup (blockDim.x >= kMaxUnion); ends with a barrier.
+__device__ void load_plan(const ScanArgs& a, int q, QueryPlan& P) {
+  const int h = q / a.group, r = q % a.group, g = r % kQueryChunk;
+  const ChunkTable& T = *reinterpret_cast<const ChunkTable*>(
+      static_cast<const char*>(a.tables) + (size_t(h) * a.chunks_per_head + r / kQueryChunk) * kChunkTableBytes);
+  const int t = threadIdx.x;
+  if (t == 0) {
+    P.np = 0u;
+    P.tneg = 0u;
+    P.tpos = 0u;
+  }
+  __syncthreads();
+  const int U = T.U;
+  if (t < U) {
+    const int b = t / kBlockPlanes, G = (t % kBlockPlanes) / 16, byte = t % 16;
+    const int8_t* row = reinterpret_cast<const int8_t*>(&T.A[b][G][0]);
+    uint32_t v = 0;
+#pragma unroll
+    for (int l = 3; l >= 0; --l) v = (v << 8) + static_cast<uint32_t>(static_cast<int32_t>(row[(4 * g + l) * 16 + byte]));
+    if (v != 0u) {
+      const uint32_t slot = atomicAdd(&P.np, 1u);
+      P.rowoff[slot] = T.rowoff[t];
+      P.V[slot] = static_cast<int32_t>(v);
+      // (wrapping sums of one sign, exact: they stay below 2^31 in magnitude)
+      atomicAdd(static_cast<int32_t>(v) < 0 ? &P.tneg : &P.tpos, v);
+    }
+  }
+  if (t == 0) {
+    P.sigma = T.sigma[g];
+    P.C = T.C[g];
+  }
+  __syncthreads();
+}
+
+// Ordered score of key i of the head whose planes start at head_planes.
+__device__ inline uint32_t plan_score(const uint32_t* head_planes, const QueryPlan& P, int64_t i) {
+  const uint32_t* base = head_planes + (i >> 5);
+  const uint32_t sh = static_cast<uint32_t>(i & 31);
+  uint32_t t = 0;
+  const uint32_t np = P.np;
+#pragma unroll 8
+  for (uint32_t p = 0; p < np; ++p) {
+    const uint32_t w = base[P.rowoff[p] >> 2];
+    t += ((w >> sh) & 1u) ? static_cast<uint32_t>(P.V[p]) : 0u;
+  }
+  return float_to_ordered(fmaf(static_cast<float>(static_cast<int32_t>(t)), P.sigma, P.C));
+}
+
+// Ordered scores of keys i0 + j * kSelectThreads (j < PT, those below i_end;
+// slots past it get 0 and no load), all PT words of a plane loaded together.
+template <int PT>
+__device__ inline void plan_scores(const uint32_t* head_planes, const QueryPlan& P, int64_t i0, int64_t i_end,
+                                   uint32_t (&v)[PT]) {
+  static_assert(kSelectThreads % 32 == 0, "slots of a thread share the bit position");
+  const uint32_t sh = static_cast<uint32_t>(i0 & 31);
+  const int64_t last_word = (i_end - 1) >> 5;   // i_end > i0 >= 0 for any valid slot
+  uint32_t wo[PT], t[PT];
+#pragma unroll
+  for (int j = 0; j < PT; ++j) {
+    wo[j] = static_cast<uint32_t>(min<int64_t>((i0 + int64_t(j) * kSelectThreads) >> 5, max<int64_t>(last_word, 0)));
+    t[j] = 0u;
+  }
+  const uint32_t np = P.np;
+  for (uint32_t p = 0; p < np; ++p) {
+    const uint32_t* row = head_planes + (P.rowoff[p] >> 2);
+    const uint32_t V = static_cast<uint32_t>(P.V[p]);
+    uint32_t x[PT];
+#pragma unroll
+    for (int j = 0; j < PT; ++j) x[j] = row[wo[j]];
+#pragma unroll
+    for (int j = 0; j < PT; ++j) t[j] += ((x[j] >> sh) & 1u) ? V : 0u;
+  }
+#pragma unroll
+  for (int j = 0; j < PT; ++j)
+    v[j] = i0 + int64_t(j) * kSelectThreads < i_end
+               ? float_to_ordered(fmaf(static_cast<float>(static_cast<int32_t>(t[j])), P.sigma, P.C))
+               : 0u;
+}
+
+// Sum over the workgroup's kSelectThreads threads, returned to all.
+__device__ inline uint32_t block_sum(uint32_t v, uint32_t* s_wave) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  v = read_lane(wave_incl_sum(v), 63);
+  if (lane == 0) s_wave[wave] = v;
+  __syncthreads();
+  uint32_t tot = 0;
+  for (int wv = 0; wv < kSelectWaves; ++wv) tot += s_wave[wv];
+  __syncthreads();
+  return tot;
+}
+
+// Of `count` entries (ordered score, key index) read by get(i), keeps in
+// keys[] every entry above kth (n_gt of them) and the first need_eq entries
+// equal to kth in position order (the callers' positions follow key order, so
+// ties go to the lower key index).  Positions are read CH per thread at a
+// time, so their loads are in flight together.  Whole workgroup of
+// kSelectThreads; s_count and s_wave are LDS scratch.
+template <int CH, class Get>
+__device__ void collect_given(int64_t count, uint32_t kth, uint32_t need_eq, uint32_t n_gt, Get get,
+                              unsigned long long* keys, uint32_t* s_count, uint32_t* s_wave) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid == 0) s_count[0] = 0;
+  __syncthreads();
+  uint32_t eq_taken = 0;
+  for (int64_t base = 0; base < count; base += int64_t(CH) * kSelectThreads) {
+    uint2 e[CH];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int64_t i = base + int64_t(c) * kSelectThreads + tid;
+      e[c] = i < count ? get(i) : make_uint2(0u, 0u);
+    }
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int64_t i = base + int64_t(c) * kSelectThreads + tid;
+      const bool valid = i < count;
+      const bool gt = valid && e[c].x > kth;
+      const bool eq = valid && e[c].x == kth;
+      if (gt) {
+        const uint32_t slot = atomicAdd(&s_count[0], 1u);
+        keys[slot] = sort_key(e[c].x, e[c].y);
+      }
+      const uint64_t bal = __ballot(eq);
+      if (lane == 0) s_wave[wave] = static_cast<uint32_t>(__popcll(bal));
+      __syncthreads();
+      uint32_t before = 0, total = 0;
+      for (int wv = 0; wv < kSelectWaves; ++wv) {
+        const uint32_t cw = s_wave[wv];
+        before += wv < wave ? cw : 0u;
+        total += cw;
+      }
+      if (eq) {
+        const uint32_t rank = eq_taken + before + static_cast<uint32_t>(lanes_below(bal));
+        if (rank < need_eq) keys[n_gt + rank] = sort_key(e[c].x, e[c].y);
+      }
+      eq_taken += total;
+      __syncthreads();
+    }
+    if (s_count[0] == n_gt && eq_taken >= need_eq) break;   // uniform: everything kept is found
+  }
+  __syncthreads();
+}
+
+// Exact top-keff of `count` entries read by get(i) (in increasing i within
+// each of its select passes), ties to the lower position: the keff entries
+// go to keys[0, keff).
+template <class Get>
+__device__ void exact_collect(int64_t count, int keff, Get get, unsigned long long* keys, SelectLds& L,
+                              uint32_t* s_count, uint32_t* s_wave) {
+  if (keff <= 0) return;   // uniform
+  const uint2 sel = block_select_fn(count, static_cast<uint32_t>(keff), L, [&](int64_t i) { return get(i).x; });
+  collect_given<1>(count, sel.x, sel.y, static_cast<uint32_t>(keff) - sel.y, get, keys, s_count, s_wave);
+}
+
+// Sorts keys[0, kept) and writes the first k outputs of query q.
+__device__ void sort_write_any(unsigned long long* keys, unsigned kept, int k, int q, int32_t* __restrict__ out_idx,
+                               float* __restrict__ out_score) {
+  const unsigned span = max(kept, static_cast<unsigned>(k));
+  if (span <= kSelectThreads) {
+    sort_and_write<1>(keys, kept, k, q, out_idx, out_score);
+  } else if (span <= 2 * kSelectThreads) {
+    sort_and_write<2>(keys, kept, k, q, out_idx, out_score);
+  } else if (span <= 4 * kSelectThreads) {
+    sort_and_write<4>(keys, kept, k, q, out_idx, out_score);
+  } else if (span <= 8 * kSelectThreads) {
+    sort_and_write<8>(keys, kept, k, q, out_idx, out_score);
+  } else {
+    sort_and_write<16>(keys, kept, k, q, out_idx, out_score);
+  }
+}
+
+// A query's candidate list missed when it holds fewer than k keys or
+// overflowed.  Such a query is rescued by the rescue workgroups when its head
+// fits their slices and it is among the first kRescueSlots such queries (in
+// query order); otherwise workgroup 0 of its merge recomputes it alone.
+__device__ inline bool list_missed(uint32_t cnt, int k) {
+  return cnt < static_cast<uint32_t>(k) || cnt > static_cast<uint32_t>(kCandCap);
+}
+__device__ inline bool rescuable(const ScanArgs& a, int q) {
+  return a.rescue_wgs > 0 &&
+         head_length(a.lengths, q / a.group, a.n) <= int64_t(a.rescue_wgs) * kRescueSlice;
+}
+
+// Rescue slot of query q (-1: not rescued): counts the missed, rescuable
+// queries before it.  Whole workgroup; uniform result.
+__device__ int rescue_slot(const ScanArgs& a, int q, int k, uint32_t* s_wave) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (!list_missed(a.count[q], k) || !rescuable(a, q)) return -1;
+  uint32_t before = 0;
+  for (int base = 0; base < q; base += kSelectThreads) {   // uniform
+    const int i = base + tid;
+    const bool m = i < q && list_missed(a.count[i], k) && rescuable(a, i);
+    const uint64_t bal = __ballot(m);
+    if (lane == 0) s_wave[wave] = static_cast<uint32_t>(__popcll(bal));
+    __syncthreads();
+    for (int wv = 0; wv < kSelectWaves; ++wv) before += s_wave[wv];
+    __syncthreads();
+  }
+  return before < static_cast<uint32_t>(kRescueSlots) ? static_cast<int>(before) : -1;
+}
+
+// Scores of the slice keys s0 + tid + j * kSelectThreads (j < PT, those
+// below s1; 0 for the rest) for a plan, with the slice's plane words staged
+// in LDS (stage: `cap` words): a chunk of J slots at a time, all of the
+// chunk's loads issued before any is used, so the slice costs a few memory
+// round trips rather than one per plane.  Whole workgroup.
+template <int PT>
+__device__ void staged_scores(const uint32_t* head_planes, const QueryPlan& P, int64_t s0, int64_t s1,
+                              uint32_t* stage, int cap, uint32_t (&v)[PT]) {
+  const int tid = threadIdx.x;
+  const int np = static_cast<int>(P.np);
+  // J slots of 1024 keys span at most 32 J + 1 words per plane
+  const int J = max(1, min(PT, (cap / max(np, 1) - 1) / 32));
+  const int cw = 32 * J + 1;   // staged words per plane
+#pragma unroll
+  for (int j = 0; j < PT; ++j) v[j] = 0u;
+  for (int j0 = 0; j0 < PT; j0 += J) {   // uniform
+    const int64_t kb = s0 + int64_t(j0) * kSelectThreads;
+    if (kb >= s1) break;
+    const int64_t ke = min(s1, s0 + int64_t(j0 + J) * kSelectThreads);
+    const int64_t wb = kb >> 5;
+    const int nwc = static_cast<int>(((ke - 1) >> 5) - wb + 1);   // <= cw
+    const int total = np * nwc;
+    // stage: eight loads in flight per thread, then their stores
+    for (int e0 = 0; e0 < total; e0 += 8 * kSelectThreads) {
+      uint32_t x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int e = e0 + u * kSelectThreads + tid;
+        const int pp = e / nwc, w = e - pp * nwc;
+        x[u] = e < total ? head_planes[(P.rowoff[pp] >> 2) + wb + w] : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int e = e0 + u * kSelectThreads + tid;
+        const int pp = e / nwc, w = e - pp * nwc;
+        if (e < total) stage[pp * cw + w] = x[u];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < PT; ++j) {
+      if (j < j0 || j >= j0 + J) continue;   // uniform
+      const int64_t i = s0 + tid + int64_t(j) * kSelectThreads;
+      if (i < s1) {
+        const int wl = static_cast<int>((i >> 5) - wb);
+        const uint32_t sh = static_cast<uint32_t>(i & 31);
+        uint32_t t = 0;
+        for (int pp = 0; pp < np; ++pp)
+          t += ((stage[pp * cw + wl] >> sh) & 1u) ? static_cast<uint32_t>(P.V[pp]) : 0u;
+        v[j] = float_to_ordered(fmaf(static_cast<float>(static_cast<int32_t>(t)), P.sigma, P.C));
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// One rescue workgroup: slice r of every rescued query.  Each slice's exact
+// top-keff (keys in key order) goes to the query's rescue list, and its
+// entries' digits (plan_digit) to the query's shared histogram; the workgroup
+// that finishes the last slice of a query merges the lists and writes the
+// query's output.  Memory order: each list, count and histogram update is
+// released by an agent-scope fence before the slice counter's increment, and
+// the last workgroup acquires them with a fence after it.
+__device__ void rescue_role(const ScanArgs& a, int k, int r, int32_t* __restrict__ out_idx,
+                            float* __restrict__ out_score, unsigned long long* keys, SelectLds& L,
+                            uint32_t* s_count, uint32_t* s_wave, uint32_t* s_pref, int* s_list) {
+  constexpr int PT = kRescueSlice / kSelectThreads;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int R = a.rescue_wgs;
+  // the rescued queries: the first kRescueSlots missed, rescuable ones
+  int found = 0;
+  for (int base = 0; base < a.num_q && found < kRescueSlots; base += kSelectThreads) {   // uniform
+    const int i = base + tid;
+    const bool m = i < a.num_q && list_missed(a.count[i], k) && rescuable(a, i);
+    const uint64_t bal = __ballot(m);
+    if (lane == 0) s_wave[wave] = static_cast<uint32_t>(__popcll(bal));
+    __syncthreads();
+    uint32_t before = 0, total = 0;
+    for (int wv = 0; wv < kSelectWaves; ++wv) {
+      before += wv < wave ? s_wave[wv] : 0u;
+      total += s_wave[wv];
+    }
+    const uint32_t rank = static_cast<uint32_t>(found) + before + static_cast<uint32_t>(lanes_below(bal));
+    if (m && rank < static_cast<uint32_t>(kRescueSlots)) s_list[rank] = i;
+    found += static_cast<int>(total);
+    __syncthreads();
+  }
+  found = min(found, kRescueSlots);
+  QueryPlan& P = plan_in(keys);
+  uint32_t* lhist = &L.hist[0][0];   // 2048 bins, while no select runs
+  for (int slot = 0; slot < found; ++slot) {
+    const int f = s_list[slot];
+    load_plan(a, f, P);
+    const PlanDigit dg = plan_digit(P);
+    const int h = f / a.group;
+    const int64_t nh = head_length(a.lengths, h, a.n);
+    const int keff = static_cast<int>(min<int64_t>(k, nh));
+    const int64_t s0 = int64_t(r) * nh / R, s1 = int64_t(r + 1) * nh / R;   // at most kRescueSlice keys
+    const uint32_t* head_planes = a.planes + int64_t(h) * kD * kPlanes * a.ldw;
+    uint32_t v[PT];
+    staged_scores<PT>(head_planes, P, s0, s1, reinterpret_cast<uint32_t*>(keys), 2 * (kCandCap - kPlanSlots), v);
+    uint32_t pm = 0;
+#pragma unroll
+    for (int j = 0; j < PT; ++j) pm |= s0 + tid + j * kSelectThreads < s1 ? (1u << j) : 0u;
+    const int kk = static_cast<int>(min<int64_t>(keff, s1 - s0));
+    uint32_t kth_slice = 0u;
+    uint2* list = a.rescue + (size_t(slot) * R + r) * size_t(k);
+    uint32_t* ghist = a.rescue_hist + size_t(slot) * kBins;
+    if (kk > 0) {   // uniform
+      const uint2 sel = block_select_regs<PT>(v, pm, static_cast<uint32_t>(kk), L);
+      const uint32_t kth = sel.x, need_eq = sel.y;
+      kth_slice = kth;
+      for (int i = tid; i < kBins; i += kSelectThreads) lhist[i] = 0u;
+      __syncthreads();
+      // the slice's top-kk in key order: every entry above kth, and the
+      // first need_eq equal to it
+      uint32_t base = 0, eq_taken = 0;
+#pragma unroll
+      for (int j = 0; j < PT; ++j) {
+        const bool pres = (pm >> j) & 1u;
+        const bool gt = pres && v[j] > kth, eq = pres && v[j] == kth;
+        const uint64_t beq = __ballot(eq);
+        if (lane == 0) s_wave[wave] = static_cast<uint32_t>(__popcll(beq));
+        __syncthreads();
+        uint32_t eq_before = 0, eq_total = 0;
+        for (int wv = 0; wv < kSelectWaves; ++wv) {
+          eq_before += wv < wave ? s_wave[wv] : 0u;
+          eq_total += s_wave[wv];
+        }
+        const bool take = gt || (eq && eq_taken + eq_before + static_cast<uint32_t>(lanes_below(beq)) < need_eq);
+        __syncthreads();
+        const uint64_t btk = __ballot(take);
+        if (lane == 0) s_wave[wave] = static_cast<uint32_t>(__popcll(btk));
+        __syncthreads();
+        uint32_t tk_before = 0, tk_total = 0;
+        for (int wv = 0; wv < kSelectWaves; ++wv) {
+          tk_before += wv < wave ? s_wave[wv] : 0u;
+          tk_total += s_wave[wv];
+        }
+        if (take)
+          list[base + tk_before + static_cast<uint32_t>(lanes_below(btk))] =
+              make_uint2(v[j], static_cast<uint32_t>(s0 + tid + j * kSelectThreads));
+        hist_add(lhist, take, (v[j] >> dg.shift) & dg.mask);
+        base += tk_total;
+        eq_taken += eq_total;
+        __syncthreads();
+      }
+      for (int i = tid; i < kBins; i += kSelectThreads)
+        if (lhist[i]) atomicAdd(&ghist[i], lhist[i]);
+    }
+    if (tid == 0) a.rescue_cnt[slot * R + r] = make_uint2(static_cast<uint32_t>(kk), kth_slice);
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) s_count[1] = atomicAdd(&a.rescue_done[slot], 1u);
+    __syncthreads();
+    const uint32_t done_before = s_count[1];
+    __syncthreads();   // (s_count is written again below)
+    if (done_before != static_cast<uint32_t>(R - 1)) continue;   // uniform: not the last slice
+    __threadfence();
+    // The last slice: merge the R lists (in slice order, so positions follow
+    // key order).
+    if (tid == 0) {
+      uint32_t acc = 0, M = 0;
+      for (int i = 0; i < R; ++i) {
+        const uint2 c = a.rescue_cnt[slot * R + i];
+        s_pref[i] = acc;
+        acc += c.x;
+        if (c.x == static_cast<uint32_t>(keff)) M = max(M, c.y);
+      }
+      s_pref[R] = acc;
+      s_count[1] = M;
+    }
+    __syncthreads();
+    const uint32_t total = s_pref[R], M = s_count[1];
+    __syncthreads();
+    const uint2* lists = a.rescue + size_t(slot) * R * size_t(k);
+    // position -> entry: the slice from a per-thread cursor over the prefix
+    // counts (a thread's positions rise within a pass; a lower position
+    // starts a new pass)
+    int cur = 0;
+    int64_t last_i = -1;
+    auto entry = [&](int64_t i) -> uint2 {
+      if (i < last_i) cur = 0;
+      last_i = i;
+      while (s_pref[cur + 1] <= static_cast<uint32_t>(i)) ++cur;
+      const v2u32 e = __builtin_nontemporal_load(
+          reinterpret_cast<const v2u32*>(lists + size_t(cur) * k + (static_cast<uint32_t>(i) - s_pref[cur])));
+      return make_uint2(e.x, e.y);
+    };
+    constexpr int CH = 8;
+    if (keff > 0) {   // uniform
+      // The histogram of all list entries gives the bucket holding the
+      // keff-th largest; every entry from that bucket's lower edge up is
+      // collected, when they fit, and sorted.
+      DigitLds& D = *reinterpret_cast<DigitLds*>(keys + kFastKept);
+      for (int i = tid; i < kBins; i += kSelectThreads) {
+        const v2u32 hv = __builtin_nontemporal_load(reinterpret_cast<const v2u32*>(ghist) + i / 2);
+        D.hist[i] = (i & 1) ? hv.y : hv.x;
+      }
+      if (tid == 0) D.big = 0u;
+      __syncthreads();
+      digit_scan(D, static_cast<uint32_t>(keff) - 1u);
+      const uint32_t C = D.bstart + D.bcount;
+      const uint32_t low = dg.common | (D.bstar << dg.shift);
+      __syncthreads();
+      if (C <= static_cast<uint32_t>(kFastKept)) {   // uniform
+        if (tid == 0) s_count[0] = 0u;
+        __syncthreads();
+        for (int64_t b0 = 0; b0 < total; b0 += int64_t(CH) * kSelectThreads) {
+          uint2 e[CH];
+#pragma unroll
+          for (int c = 0; c < CH; ++c) {
+            const int64_t i = b0 + int64_t(c) * kSelectThreads + tid;
+            e[c] = i < total ? entry(i) : make_uint2(0u, 0u);
+          }
+#pragma unroll
+          for (int c = 0; c < CH; ++c) {
+            const int64_t i = b0 + int64_t(c) * kSelectThreads + tid;
+            if (i < total && e[c].x >= low) keys[atomicAdd(&s_count[0], 1u)] = sort_key(e[c].x, e[c].y);
+          }
+        }
+        __syncthreads();
+        sort_write_any(keys, C, k, f, out_idx, out_score);
+        __syncthreads();
+        continue;
+      }
+      if (dg.shift == 0u) {   // uniform
+        // each bucket is a single score, so the keff-th largest is `low`
+        // itself: every entry above it and the first ties in key order
+        collect_given<CH>(total, low, static_cast<uint32_t>(keff) - D.bstart, D.bstart, entry, keys, s_count,
+                          s_wave);
+        sort_write_any(keys, static_cast<unsigned>(keff), k, f, out_idx, out_score);
+        __syncthreads();
+        continue;
+      }
+    }
+    // Many entries share the bucket (ties): a slice that kept keff keys has
+    // keff keys at or above its own keff-th score, so the keff-th largest is
+    // at least the largest such score M.
+    uint32_t my_gt = 0, my_eq = 0;
+    for (int64_t b0 = 0; b0 < total; b0 += int64_t(CH) * kSelectThreads) {
+      uint2 e[CH];
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        const int64_t i = b0 + int64_t(c) * kSelectThreads + tid;
+        e[c] = i < total ? entry(i) : make_uint2(0u, 0u);
+      }
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        const bool valid = b0 + int64_t(c) * kSelectThreads + tid < total;
+        my_gt += (valid && e[c].x > M) ? 1u : 0u;
+        my_eq += (valid && e[c].x == M) ? 1u : 0u;
+      }
+    }
+    const uint32_t c_gt = block_sum(my_gt, s_wave), c_eq = block_sum(my_eq, s_wave);
+    if (c_gt + c_eq <= static_cast<uint32_t>(kFastKept)) {   // uniform
+      collect_given<CH>(total, M, c_eq, c_gt, entry, keys, s_count, s_wave);
+      sort_write_any(keys, c_gt + c_eq, k, f, out_idx, out_score);
+    } else if (c_gt < static_cast<uint32_t>(keff)) {
+      // M is then the keff-th largest: all entries above it and the first
+      // ties in key order
+      collect_given<CH>(total, M, static_cast<uint32_t>(keff) - c_gt, c_gt, entry, keys, s_count, s_wave);
+      sort_write_any(keys, static_cast<unsigned>(keff), k, f, out_idx, out_score);
+    } else {
+      exact_collect(total, keff, entry, keys, L, s_count, s_wave);
+      sort_write_any(keys, static_cast<unsigned>(keff), k, f, out_idx, out_score);
+    }
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(kSelectThreads) void scan_merge_kernel(ScanArgs a, int k, int parts,
                                                                     int32_t* __restrict__ out_idx,
                                                                     float* __restrict__ out_score) {
   constexpr int PT = kCandCap / kSelectThreads;
   __shared__ unsigned long long keys[kCandCap];     // sort buffer (score, ~index)
   __shared__ SelectLds L;
-  __shared__ QueryLds qs;
   __shared__ uint32_t s_count[2];
   __shared__ uint32_t s_wave[kSelectWaves];
   __shared__ uint32_t s_span[2];   // positions filled by this workgroup's scatter
-  const int q = blockIdx.x;
-  const int part = blockIdx.y;
-  const int parts = static_cast<int>(gridDim.y);
+  __shared__ uint32_t s_pref[kRescueMaxWgs + 1];
+  __shared__ int s_list[kRescueSlots];
+  const int bid = blockIdx.x;
+  if (bid >= a.num_q * parts) {   // uniform: a rescue workgroup
+    rescue_role(a, k, bid - a.num_q * parts, out_idx, out_score, keys, L, s_count, s_wave, s_pref, s_list);
+    return;
+  }
+  const int q = bid % a.num_q;
+  const int part = bid / a.num_q;
   const uint32_t p_lo = static_cast<uint32_t>(int64_t(k) * part / parts);
   const uint32_t p_hi = static_cast<uint32_t>(int64_t(k) * (part + 1) / parts);
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
   static_assert(PT * kSelectThreads == kCandCap, "one register per candidate slot");
   // The first kSpecSlots slots of the list load at once, before the count
   // arrives (the list is allocated to its capacity; slots past the count
@@ -1548,6 +2065,7 @@ __global__ __launch_bounds__(kSelectThreads) void scan_merge_kernel(ScanArgs a, 
   const uint32_t cnt = a.count[q];
   unsigned kept = 0;
   bool fast = false;   // uniform
+  if (list_missed(cnt, k) && rescue_slot(a, q, k, s_wave) >= 0) return;   // uniform: the rescue places it
 
   if (cnt >= static_cast<uint32_t>(k) && cnt <= static_cast<uint32_t>(kCandCap)) {
     if (cnt > static_cast<uint32_t>(kSpecSlots * kSelectThreads)) {   // uniform
@@ -1674,77 +2192,22 @@ __global__ __launch_bounds__(kSelectThreads) void scan_merge_kernel(ScanArgs a, 
     // them ahead of the count test instead of sinking them into the fast path)
 #pragma unroll
     for (int j = 0; j < kSpecSlots; ++j) asm volatile("" : : "v"(v[j]), "v"(id[j]));
-    // exact fallback: radix select over recomputed scores, of the head's nh
-    // keys; a head holding fewer than k keys returns all of them
+    // exact fallback, alone: every score recomputed (the main kernel's
+    // fixed-point arithmetic) in each select pass; a head holding fewer than
+    // k keys returns all of them
     const int h = q / a.group;
     const int64_t nh = head_length(a.lengths, h, a.n);
     const int keff = static_cast<int>(min<int64_t>(k, nh));
     const uint32_t* head_planes = a.planes + int64_t(h) * kD * kPlanes * a.ldw;
-    if (tid < kD) {
-      const float lo = a.lo[h * kD + tid], st = a.step[h * kD + tid];
-      const float qv = a.q[int64_t(q) * kD + tid];
-      const int bc = min(static_cast<int>(a.alloc[int64_t(q) * kD + tid]), kPlanes);
-      qs.b[tid] = static_cast<uint8_t>(bc);
-      for (int j = 0; j < kPlanes; ++j) qs.w[tid][j] = __fmul_rn(qv, st) * static_cast<float>(8 >> j);
-      const double v = wave_sum(static_cast<double>(qv) *
-                                (static_cast<double>(lo) + static_cast<double>(st) * pow2_3_minus(bc)));
-      if (lane == 0) qs.cpart[wave] = v;
-    }
-    __syncthreads();
-    if (tid == 0) qs.C = static_cast<float>(qs.cpart[0] + qs.cpart[1]);
-    __syncthreads();
-    const uint2 sel = keff > 0 ? block_select_fn(nh, static_cast<uint32_t>(keff), L, [&](int64_t i) {
-      return float_to_ordered(query_score(head_planes, a.ldw, qs, i));
-    }) : make_uint2(0xffffffffu, 0u);   // (uniform; nothing to select)
-    const uint32_t kth = sel.x;                                   // ordered score of the keff-th key
-    const uint32_t need_eq = sel.y;                               // ties at kth to take
-    const uint32_t n_gt = static_cast<uint32_t>(keff) - need_eq;  // keys strictly above it
-    if (tid == 0) s_count[0] = 0;
-    __syncthreads();
-    uint32_t eq_taken = 0;
-    for (int64_t base = 0; base < (keff > 0 ? nh : 0); base += blockDim.x) {
-      const int64_t i = base + tid;
-      const bool valid = i < nh;
-      const uint32_t v = valid ? float_to_ordered(query_score(head_planes, a.ldw, qs, i)) : 0u;
-      const bool gt = valid && v > kth;
-      const bool eq = valid && v == kth;
-      if (gt) {
-        const uint32_t slot = atomicAdd(&s_count[0], 1u);
-        keys[slot] = sort_key(v, static_cast<uint32_t>(i));
-      }
-      const uint64_t bal = __ballot(eq);
-      if (lane == 0) s_wave[wave] = static_cast<uint32_t>(__popcll(bal));
-      __syncthreads();
-      uint32_t before = 0, total = 0;
-      for (int wv = 0; wv < kSelectWaves; ++wv) {
-        const uint32_t c = s_wave[wv];
-        before += wv < wave ? c : 0u;
-        total += c;
-      }
-      if (eq) {
-        const uint32_t rank = eq_taken + before + static_cast<uint32_t>(lanes_below(bal));
-        if (rank < need_eq) keys[n_gt + rank] = sort_key(v, static_cast<uint32_t>(i));
-      }
-      eq_taken += total;
-      __syncthreads();
-    }
-    __syncthreads();
+    QueryPlan& P = plan_in(keys);
+    load_plan(a, q, P);
+    exact_collect(nh, keff, [&](int64_t i) { return make_uint2(plan_score(head_planes, P, i), static_cast<uint32_t>(i)); },
+                  keys, L, s_count, s_wave);
     kept = static_cast<unsigned>(keff);
   }
   // keys[0, kept) hold the kept keys (kept >= k unless the head holds fewer
   // than k): sort them and write the first k
-  const unsigned span = max(kept, static_cast<unsigned>(k));
-  if (span <= kSelectThreads) {
-    sort_and_write<1>(keys, kept, k, q, out_idx, out_score);
-  } else if (span <= 2 * kSelectThreads) {
-    sort_and_write<2>(keys, kept, k, q, out_idx, out_score);
-  } else if (span <= 4 * kSelectThreads) {
-    sort_and_write<4>(keys, kept, k, q, out_idx, out_score);
-  } else if (span <= 8 * kSelectThreads) {
-    sort_and_write<8>(keys, kept, k, q, out_idx, out_score);
-  } else {
-    sort_and_write<16>(keys, kept, k, q, out_idx, out_score);
-  }
+  sort_write_any(keys, kept, k, q, out_idx, out_score);
 }
 
 // Main-kernel launches may carry a start and a stop event: recorded by the
@@ -1802,6 +2265,12 @@ hipError_t launch_scan_topk(const uint32_t* planes, const float* lo, const float
   a.cand = ws.cand;
   a.tables = ws.tables;
   a.all_scores = all_scores;
+  a.num_q = num_q;
+  a.rescue = ws.rescue;
+  a.rescue_cnt = ws.rescue_cnt;
+  a.rescue_hist = ws.rescue_hist;
+  a.rescue_done = ws.rescue_done;
+  a.rescue_wgs = ws.rescue_wgs;
 
   const int full = group / kQueryChunk;
   const int rest = group % kQueryChunk;
@@ -1871,8 +2340,8 @@ hipError_t launch_scan_topk(const uint32_t* planes, const float* lo, const float
     if (e != hipSuccess) return e;
   }
   const int merge_parts = std::max(1, std::min(kMergeSplit, 256 / std::max(1, num_q)));
-  hipLaunchKernelGGL(scan_merge_kernel, dim3(num_q, merge_parts), dim3(kSelectThreads), 0, stream, a, k, out_idx,
-                     out_score);
+  hipLaunchKernelGGL(scan_merge_kernel, dim3(num_q * merge_parts + a.rescue_wgs), dim3(kSelectThreads), 0, stream,
+                     a, k, merge_parts, out_idx, out_score);
   return hipGetLastError();
 }
 

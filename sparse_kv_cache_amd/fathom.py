@@ -28,7 +28,7 @@ FATHOM_CONTROL_UNIFORM = 0
 FATHOM_CONTROL_TOP_CHANNELS = 1
 MAX_K = 4096
 NOALLOC_MAX_Q = 64
-NOALLOC_SCRATCH_BYTES = 12 << 20
+NOALLOC_SCRATCH_BYTES = 16 << 20
 
 EXPORTS = (
     "fathom_plane_ldw",

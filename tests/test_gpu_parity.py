@@ -799,3 +799,45 @@ def test_ragged_lengths_attention_skips_rows_past_length():
             continue
         ref = O.sparse_attention(k64[h], v64[h], q[i], ok, 128 ** -0.5)
         assert np.abs(out[i] - ref).max() <= 1e-4 * np.abs(v64[h][ok]).max()
+
+
+# ------------------------------------------------ missed candidate lists
+
+@pytest.mark.timeout(900)
+def test_qwen3_8b_1m_zero_queries_are_rescued(qwen_store):
+    """Three all-zero queries in the 1M-token step: every score ties, every
+    candidate list overflows.  The first two are rescued by the merge
+    launch's parallel slices, the third takes the single-workgroup path; all
+    three return keys 0 .. k-1 with score 0, and the other queries are
+    unaffected."""
+    S = qwen_store
+    w, G = S["w"], S["w"].group
+    say("qwen3_8b_1m zero queries")
+    q = S["q"].copy()
+    zero = (0, 9, 17)
+    q[list(zero)] = 0.0
+    alloc, idx, val = fa.allocate_scan_topk(S["planes"], S["lo"], S["step"], S["var"], S["store"], dev(q), G, 92,
+                                            w.k)
+    alloc, idx, val = host(alloc), host(idx), host(val)
+    assert np.array_equal(alloc, O.allocate_all(q, S["var_ref"], G, 92))
+    for i in zero:
+        assert np.array_equal(idx[i], np.arange(w.k)) and np.all(val[i] == 0.0), i
+    for i in (1, 8, 16, 31):
+        check_topk(idx[i], val[i], S["ref_scores"](i, alloc[i]), w.k, w.n)
+
+
+def test_undercounted_lists_are_rescued():
+    """Strong keys planted in the sampled blocks push theta above the k-th
+    score for queries 0, 1 and 2, so their lists hold fewer than k keys:
+    queries 0 and 1 are rescued in parallel slices, query 2 takes the
+    single-workgroup path; all match the oracle."""
+    say("undercounted lists")
+    n, G, B, k = 262144, 4, 92, 2048
+    keys, q = synth.make_inputs(61, 1, n, G)
+    top = np.abs(keys[0]).max(axis=0) + 1.0
+    # the sampled 1024-key blocks are 0, 32, 64, ... (8 blocks spread over 256)
+    for g, blk in ((0, 0), (1, 32), (2, 64)):
+        keys[0, blk * 1024:blk * 1024 + 200] = (np.sign(q[g]) * top)[None, :]
+    res, _ = check_full(keys, q, G, B, k)
+    for g, blk in ((0, 0), (1, 32), (2, 64)):
+        assert set(range(blk * 1024, blk * 1024 + 200)) <= set(res["idx"][g].tolist())
