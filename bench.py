@@ -404,7 +404,32 @@ def main():
                 rec["frac_of_pcie_copy"] = round(rec["pcie_gbs"] / ceilings["pcie_h2d_copy"]["gbs"], 3)
             host_resident[f"B{hb}_zero_copy"] = rec
             log(f"host-resident store, B={hb}, zero-copy: {h_ms * 1e3:.1f} us/step")
-        del pinned
+        # the union rows staged by the copy engines, head by head, overlapped
+        # with the scans (the call waits for the allocation on the host)
+        staging = fa.alloc_workspace(fa.staging_bytes(store), dev)
+        st_ws = fa.alloc_workspace(fa.workspace_bytes(fa.FATHOM_OP_SCAN, store, G, k), dev)
+        copy_stream = torch.cuda.Stream(device=dev)
+        for mname, smode in (("gather", fa.FATHOM_STAGE_GATHER), ("copy_engine", fa.FATHOM_STAGE_COPY_ENGINE)):
+            for hb in sorted(set(synth.WORKLOADS["host_resident"].budgets) | {budget}):
+                def staged_step(i):
+                    fa.allocate_scan_topk_staged(pinned, lo, step, var, store, qd, G, hb, k, staging=staging,
+                                                 workspace=st_ws, alloc=h_alloc, out_idx=out_idx, out_score=out_score,
+                                                 mode=smode, copy_stream=copy_stream)
+                staged_step(0)
+                s_ms = timed_loop(staged_step, args.host_steps, torch)
+                hb_bytes = union_bytes(h_alloc.cpu().numpy(), G, store.ldw)
+                rec = {
+                    "ms_per_step": round(s_ms, 4),
+                    "gkeys_per_s": round(H * n / (s_ms * 1e-3) / 1e9, 3),
+                    "union_bytes": hb_bytes,
+                    "pcie_gbs": round(hb_bytes / (s_ms * 1e-3) / 1e9, 1),
+                    "vs_zero_copy": round(host_resident[f"B{hb}_zero_copy"]["ms_per_step"] / s_ms, 3),
+                }
+                if ceilings:
+                    rec["frac_of_pcie_copy"] = round(rec["pcie_gbs"] / ceilings["pcie_h2d_copy"]["gbs"], 3)
+                host_resident[f"B{hb}_staged_{mname}"] = rec
+                log(f"host-resident store, B={hb}, staged ({mname}): {s_ms * 1e3:.1f} us/step")
+        del pinned, staging, st_ws
 
     # ---- attention over the rows the last step selected
     attention = None

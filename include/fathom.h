@@ -205,6 +205,40 @@ int fathom_allocate_scan_topk(const uint32_t* planes, const float* lo, const flo
                               int32_t budget_bits, int32_t k, uint8_t* alloc, int32_t* out_idx,
                               float* out_score, void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/* Staging modes of fathom_allocate_scan_topk_staged. */
+enum { FATHOM_STAGE_COPY_ENGINE = 0, FATHOM_STAGE_GATHER = 1 };
+
+/* The same decode step with the plane store in host memory, staged into HBM
+ * head by head ([Art] para 1 and limits paragraph; [Abs] s1, s6: the index
+ * lives in host memory, where avoiding transfers matters more than
+ * arithmetic).  planes_host: the store (layout as always) in pinned host
+ * memory (hipHostMalloc or torch pin_memory; not registered memory).
+ * staging: device memory for two head blocks, >= 2 * d * 4 * ldw * 4 bytes,
+ * 256-byte aligned.  workspace: >= fathom_workspace_bytes(FATHOM_OP_SCAN,
+ * store, group, k) (one head's queries at a time).
+ * The call launches the allocation of every query (alloc, as in
+ * fathom_allocate).  Then, per KV head h, only the head's union rows -- per
+ * channel c the contiguous rows j < u_c, u_c the deepest prefix any of the
+ * head's queries reads -- are copied from planes_host into staging slot
+ * h % 2 on copy_stream, while hip_stream scans head h - 1 from the other
+ * slot; events order each scan after its copy and each copy after the last
+ * scan (of this call or the previous one) that read its slot.
+ *   FATHOM_STAGE_COPY_ENGINE: hipMemcpyAsync per run of union rows (runs
+ *     closer than a copy's fixed cost are joined, rows between included);
+ *     the union is needed on the host, so the call BLOCKS the calling thread
+ *     until the allocation has been copied back.
+ *   FATHOM_STAGE_GATHER: a kernel on copy_stream reads the union rows over
+ *     PCIe in 16-byte loads (union computed on the device); no host wait.
+ * Results equal those of fathom_allocate_scan_topk on the same store.
+ * Outputs are valid once hip_stream has been synchronized; copy_stream must
+ * be a stream of the same device (the same stream works, without overlap).
+ * Concurrent staged calls share the library's events: serialize them. */
+int fathom_allocate_scan_topk_staged(const uint32_t* planes_host, const float* lo, const float* step,
+                                     const float* var, const fathom_store_desc* store, const float* q, int32_t num_q,
+                                     int32_t group, int32_t budget_bits, int32_t k, uint8_t* alloc, int32_t* out_idx,
+                                     float* out_score, uint32_t* staging, size_t staging_bytes, void* workspace,
+                                     size_t workspace_bytes, int32_t mode, void* hip_stream, void* copy_stream);
+
 /* For callers that cannot allocate memory (code under HIP graph capture,
  * tight serving loops, harnesses that forbid hipMalloc): the same call as
  * fathom_allocate_scan_topk, with the same results, but its scratch memory

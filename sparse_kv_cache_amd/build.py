@@ -18,7 +18,7 @@ OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfathom.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["pack.hip", "allocate.hip", "scan.hip", "attend.hip", "measure.hip", "fathom_api.hip"]
+SOURCES = ["pack.hip", "allocate.hip", "scan.hip", "attend.hip", "stage.hip", "measure.hip", "fathom_api.hip"]
 
 COMMON = [
     "--offload-arch=gfx950",

@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <algorithm>
 #include <cstring>
 #include <mutex>
 #include <vector>
@@ -118,6 +119,11 @@ ScanLayout scan_layout(int num_q, int64_t n, int k) {
 constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
 void* g_scratch_ptr[kMaxDevices] = {};   // device address of `scratch` per device
+
+// events of the staged host-resident call: (ready, freed) per staging slot,
+// and the allocation's
+std::mutex g_staged_mu;
+hipEvent_t g_staged_events[5] = {};
 
 // kernel timing record
 std::mutex g_timing_mu;
@@ -357,6 +363,137 @@ int fathom_allocate_scan_topk_noalloc(const uint32_t* planes, const float* lo, c
   return scan_impl("fathom_allocate_scan_topk_noalloc launch", planes, lo, step, store, q, nullptr, num_q, group,
                    k, out_idx, out_score, nullptr, ptr, FATHOM_NOALLOC_SCRATCH_BYTES, hip_stream, var, budget_bits,
                    alloc);
+}
+
+int fathom_allocate_scan_topk_staged(const uint32_t* planes_host, const float* lo, const float* step,
+                                     const float* var, const fathom_store_desc* store, const float* q, int32_t num_q,
+                                     int32_t group, int32_t budget_bits, int32_t k, uint8_t* alloc, int32_t* out_idx,
+                                     float* out_score, uint32_t* staging, size_t staging_bytes, void* workspace,
+                                     size_t workspace_bytes, int32_t mode, void* hip_stream, void* copy_stream) {
+  int st = check_store(store);
+  if (st != FATHOM_OK) return st;
+  if (!planes_host || !lo || !step || !var || !q || !alloc || !out_idx || !out_score || !staging)
+    return fail(FATHOM_ERR_INVALID_ARG, "pointers must be non-NULL");
+  if (mode != FATHOM_STAGE_COPY_ENGINE && mode != FATHOM_STAGE_GATHER)
+    return fail(FATHOM_ERR_INVALID_ARG, "unknown staging mode %d", mode);
+  if (num_q < 1 || group < 1) return fail(FATHOM_ERR_INVALID_ARG, "num_q and group must be >= 1");
+  if (static_cast<int64_t>(store->num_kv_heads) * group != num_q)
+    return fail(FATHOM_ERR_INVALID_ARG, "num_q = %d must equal num_kv_heads (%d) * group (%d)", num_q,
+                store->num_kv_heads, group);
+  if (budget_bits < 0 || budget_bits > kPlanes * kD)
+    return fail(FATHOM_ERR_INVALID_ARG, "budget_bits = %d outside [0, %d]", budget_bits, kPlanes * kD);
+  if (k < 1 || k > store->n) return fail(FATHOM_ERR_INVALID_ARG, "k = %d outside [1, n]", k);
+  if (k > FATHOM_MAX_K) return fail(FATHOM_ERR_UNSUPPORTED, "k = %d exceeds FATHOM_MAX_K (%d)", k, FATHOM_MAX_K);
+  if (!aligned(q, 8) || !aligned(var, 8) || !aligned(alloc, 2) || !aligned(planes_host, 16) ||
+      !aligned(staging, 256) || !aligned(lo, 4) || !aligned(step, 4) || !aligned(out_idx, 4) ||
+      !aligned(out_score, 4))
+    return fail(FATHOM_ERR_INVALID_ARG, "misaligned pointer (q, var 8; alloc 2; planes 16; staging 256 bytes)");
+  const int64_t head_words = int64_t(kD) * kPlanes * store->ldw;
+  if (staging_bytes < size_t(2 * head_words * 4))
+    return fail(FATHOM_ERR_WORKSPACE, "staging needs two head blocks: %lld bytes (got %zu)",
+                static_cast<long long>(2 * head_words * 4), staging_bytes);
+  const ScanLayout L = scan_layout(group, store->n, k);
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < L.total)
+    return fail(FATHOM_ERR_WORKSPACE, "staged scan needs a 256-byte aligned workspace of %zu bytes (got %zu)",
+                L.total, workspace_bytes);
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  hipStream_t cstream = static_cast<hipStream_t>(copy_stream);
+  const uint32_t* planes_dev = nullptr;   // device view of the pinned store (gather mode)
+  if (mode == FATHOM_STAGE_GATHER) {
+    void* dp = nullptr;
+    hipError_t e = hipHostGetDevicePointer(&dp, const_cast<uint32_t*>(planes_host), 0);
+    if (e != hipSuccess) return hip_fail(e, "hipHostGetDevicePointer (planes_host must be pinned host memory)");
+    planes_dev = static_cast<const uint32_t*>(dp);
+  }
+  // events (ready, freed) per staging slot and one for the allocation,
+  // created once
+  {
+    std::lock_guard<std::mutex> lock(g_staged_mu);
+    for (int i = 0; i < 5; ++i) {
+      if (g_staged_events[i]) continue;
+      hipError_t e = hipEventCreateWithFlags(&g_staged_events[i], hipEventDisableTiming);
+      if (e != hipSuccess) return hip_fail(e, "hipEventCreateWithFlags");
+    }
+  }
+  hipEvent_t* ready = &g_staged_events[0];
+  hipEvent_t* freed = &g_staged_events[2];
+  hipEvent_t ev_alloc = g_staged_events[4];
+  // 1. the allocation
+  hipError_t e = launch_allocate(q, num_q, group, var, budget_bits, alloc, stream);
+  if (e != hipSuccess) return hip_fail(e, "fathom_allocate_scan_topk_staged allocate launch");
+  std::vector<uint8_t> alloc_h;
+  if (mode == FATHOM_STAGE_COPY_ENGINE) {
+    // the copy commands need the union on the host: this thread waits
+    alloc_h.resize(size_t(num_q) * kD);
+    e = hipMemcpyAsync(alloc_h.data(), alloc, alloc_h.size(), hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(e, "allocation readback");
+  } else {
+    e = hipEventRecord(ev_alloc, stream);
+    if (e == hipSuccess) e = hipStreamWaitEvent(cstream, ev_alloc, 0);
+    if (e != hipSuccess) return hip_fail(e, "allocation event");
+  }
+  char* w = static_cast<char*>(workspace);
+  ScanWorkspace ws{reinterpret_cast<float*>(w + L.theta), reinterpret_cast<uint32_t*>(w + L.count),
+                   reinterpret_cast<float*>(w + L.sample), reinterpret_cast<uint2*>(w + L.cand),
+                   static_cast<void*>(w + L.tables), reinterpret_cast<uint2*>(w + L.rescue),
+                   reinterpret_cast<uint2*>(w + L.rescue_cnt), reinterpret_cast<uint32_t*>(w + L.rescue_hist),
+                   reinterpret_cast<uint32_t*>(w + L.rescue_done), L.rescue_wgs};
+  // copy-engine mode: a copy costs a fixed ~11 us besides its bytes (about
+  // 640 KB at the link's rate), so two runs are joined when the rows between
+  // them cost less than that
+  const int64_t join_rows = std::max<int64_t>(0, (int64_t(640) << 10) / (store->ldw * 4));
+  for (int h = 0; h < store->num_kv_heads; ++h) {
+    const int slot = h & 1;
+    uint32_t* dst_head = staging + slot * head_words;
+    // 2. wait until the scan that last read the slot (two heads back, or the
+    // previous call's) has finished
+    e = hipStreamWaitEvent(cstream, freed[slot], 0);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent (slot free)");
+    if (mode == FATHOM_STAGE_GATHER) {
+      e = launch_stage_union(planes_dev + int64_t(h) * head_words, dst_head, alloc + int64_t(h) * group * kD, group,
+                             store->ldw, cstream);
+      if (e != hipSuccess) return hip_fail(e, "stage_union launch");
+    } else {
+      // the head's union runs: rows j < u_c of channel c are contiguous, and
+      // so are consecutive channels while u_c = 4
+      const uint32_t* src_head = planes_host + int64_t(h) * head_words;
+      int64_t run_lo = -1, run_hi = -1;   // rows [run_lo, run_hi)
+      auto flush = [&]() -> hipError_t {
+        if (run_hi <= run_lo) return hipSuccess;
+        return hipMemcpyAsync(dst_head + run_lo * store->ldw, src_head + run_lo * store->ldw,
+                              size_t((run_hi - run_lo) * store->ldw * 4), hipMemcpyHostToDevice, cstream);
+      };
+      for (int c = 0; c < kD && e == hipSuccess; ++c) {
+        int u = 0;
+        for (int g = 0; g < group; ++g)
+          u = std::max<int>(u, std::min<int>(alloc_h[size_t(h * group + g) * kD + c], kPlanes));
+        if (u == 0) continue;
+        const int64_t lo_row = int64_t(c) * kPlanes;
+        if (run_hi >= 0 && lo_row - run_hi <= join_rows) {
+          run_hi = lo_row + u;   // joins the run (with the rows between)
+        } else {
+          e = flush();
+          run_lo = lo_row;
+          run_hi = lo_row + u;
+        }
+      }
+      if (e == hipSuccess) e = flush();
+      if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (union run)");
+    }
+    e = hipEventRecord(ready[slot], cstream);
+    if (e == hipSuccess) e = hipStreamWaitEvent(stream, ready[slot], 0);
+    if (e != hipSuccess) return hip_fail(e, "staging events");
+    // 3. the head's scan from the staged slot
+    e = launch_scan_topk(dst_head, lo + int64_t(h) * kD, step + int64_t(h) * kD, 1, store->n,
+                         store->lengths ? store->lengths + h : nullptr, store->ldw, q + int64_t(h) * group * kD,
+                         alloc + int64_t(h) * group * kD, group, group, k, out_idx + int64_t(h) * group * k,
+                         out_score + int64_t(h) * group * k, nullptr, ws, nullptr, stream);
+    if (e != hipSuccess) return hip_fail(e, "fathom_allocate_scan_topk_staged scan launch");
+    e = hipEventRecord(freed[slot], stream);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord (slot free)");
+  }
+  return ok();
 }
 
 int fathom_sparse_attention(const uint16_t* k_rows, const uint16_t* v_rows, int64_t stride_head,

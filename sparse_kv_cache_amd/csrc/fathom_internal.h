@@ -79,6 +79,12 @@ hipError_t launch_attend(const uint16_t* k_rows, const uint16_t* v_rows, int64_t
                          int64_t stride_token, int64_t n, const int32_t* lengths, const float* q, const int32_t* idx, int num_q,
                          int group, int k, float scale, float* part, float* out, hipStream_t stream);
 
+// Copies the union rows of one KV head (query group's allocation at alloc,
+// [group][kD]) from src_head (device view of pinned host memory) into
+// dst_head (HBM), same layout; other rows are left as they are.
+hipError_t launch_stage_union(const uint32_t* src_head, uint32_t* dst_head, const uint8_t* alloc, int group,
+                              int64_t ldw, hipStream_t stream);
+
 // Measurement aid: a streaming read of `bytes` (a multiple of 16) from src;
 // sink holds stream_read_blocks() words (written only on an improbable value).
 int stream_read_blocks();

@@ -26,6 +26,8 @@ FATHOM_OP_SCAN = 1
 FATHOM_OP_ATTEND = 2
 FATHOM_CONTROL_UNIFORM = 0
 FATHOM_CONTROL_TOP_CHANNELS = 1
+FATHOM_STAGE_COPY_ENGINE = 0
+FATHOM_STAGE_GATHER = 1
 MAX_K = 4096
 NOALLOC_MAX_Q = 64
 NOALLOC_SCRATCH_BYTES = 16 << 20
@@ -40,6 +42,7 @@ EXPORTS = (
     "fathom_scan_topk",
     "fathom_allocate_scan_topk",
     "fathom_allocate_scan_topk_noalloc",
+    "fathom_allocate_scan_topk_staged",
     "fathom_sparse_attention",
     "fathom_host_device_pointer",
     "fathom_status_string",
@@ -87,6 +90,8 @@ def _load():
         "fathom_scan_topk": (ctypes.c_int, [P, P, P, SD, P, P, i32, i32, i32, P, P, P, P, sz, P]),
         "fathom_allocate_scan_topk": (ctypes.c_int, [P, P, P, P, SD, P, i32, i32, i32, i32, P, P, P, P, sz, P]),
         "fathom_allocate_scan_topk_noalloc": (ctypes.c_int, [P, P, P, P, SD, P, i32, i32, i32, i32, P, P, P, P]),
+        "fathom_allocate_scan_topk_staged": (ctypes.c_int, [P, P, P, P, SD, P, i32, i32, i32, i32, P, P, P, P, sz, P,
+                                                            sz, i32, P, P]),
         "fathom_sparse_attention": (ctypes.c_int, [P, P, i64, i64, SD, P, P, i32, i32, i32, ctypes.c_float, P, P,
                                                    sz, P]),
         "fathom_host_device_pointer": (ctypes.c_int, [P, ctypes.POINTER(P)]),
@@ -268,6 +273,44 @@ def allocate_scan_topk_noalloc(planes: torch.Tensor, lo: torch.Tensor, step: tor
                                                Q, group, budget, k, _ptr(alloc), _ptr(out_idx), _ptr(out_score),
                                                _stream(stream))
     _check(st, "fathom_allocate_scan_topk_noalloc")
+    return alloc, out_idx, out_score
+
+
+def staging_bytes(store: StoreDesc) -> int:
+    """Device staging the host-resident staged call needs: two head blocks."""
+    return 2 * store.d * 4 * store.ldw * 4
+
+
+def allocate_scan_topk_staged(planes_host: torch.Tensor, lo: torch.Tensor, step: torch.Tensor, var: torch.Tensor,
+                              store: StoreDesc, q: torch.Tensor, group: int, budget: int, k: int, *,
+                              staging: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                              alloc: Optional[torch.Tensor] = None, out_idx: Optional[torch.Tensor] = None,
+                              out_score: Optional[torch.Tensor] = None, mode: int = FATHOM_STAGE_GATHER,
+                              copy_stream=None, stream=None):
+    """allocate_scan_topk() over a plane store in pinned host memory, its
+    union rows staged into HBM head by head (FATHOM_STAGE_GATHER: by a
+    kernel; FATHOM_STAGE_COPY_ENGINE: by hipMemcpyAsync, blocking until the
+    allocation reaches the host).  planes_host: pinned CPU tensor."""
+    assert planes_host.is_pinned()
+    Q, d = q.shape
+    dev = q.device
+    if alloc is None:
+        alloc = torch.empty((Q, d), dtype=torch.uint8, device=dev)
+    if out_idx is None:
+        out_idx = torch.empty((Q, k), dtype=torch.int32, device=dev)
+    if out_score is None:
+        out_score = torch.empty((Q, k), dtype=torch.float32, device=dev)
+    if staging is None:
+        staging = alloc_workspace(staging_bytes(store), dev)
+    if workspace is None:
+        workspace = alloc_workspace(workspace_bytes(FATHOM_OP_SCAN, store, group, k), dev)
+    if copy_stream is None:
+        copy_stream = torch.cuda.Stream(device=dev)
+    st = lib.fathom_allocate_scan_topk_staged(
+        _ptr(planes_host), _ptr(lo), _ptr(step), _ptr(var), ctypes.byref(store), _ptr(q), Q, group, budget, k,
+        _ptr(alloc), _ptr(out_idx), _ptr(out_score), _ptr(staging), staging.numel() * staging.element_size(),
+        _ptr(workspace), workspace.numel(), mode, _stream(stream), _stream(copy_stream))
+    _check(st, "fathom_allocate_scan_topk_staged")
     return alloc, out_idx, out_score
 
 

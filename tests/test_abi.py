@@ -208,3 +208,22 @@ def test_noalloc_rejects_on_host():
     s = SD(2, 128, 1000, 32)
     assert lib.fathom_allocate_scan_topk_noalloc(FAKE, FAKE, FAKE, None, ctypes.byref(s), FAKE, 8, 4, 92, 10, FAKE,
                                                  FAKE, FAKE, None) == fa.FATHOM_ERR_INVALID_ARG
+
+
+def test_staged_validation():
+    s = SD(2, 128, 1000, 32)
+
+    def call(num_q=8, group=4, budget=92, k=10, staging=FAKE, staging_bytes=1 << 30, ws_bytes=1 << 30, var=FAKE,
+             mode=0):
+        return lib.fathom_allocate_scan_topk_staged(FAKE, FAKE, FAKE, var, ctypes.byref(s), FAKE, num_q, group, budget,
+                                                    k, FAKE, FAKE, FAKE, staging, staging_bytes, FAKE, ws_bytes, mode,
+                                                    None, None)
+    assert call(num_q=6) == fa.FATHOM_ERR_INVALID_ARG
+    assert call(budget=600) == fa.FATHOM_ERR_INVALID_ARG
+    assert call(k=0) == fa.FATHOM_ERR_INVALID_ARG
+    assert call(var=None) == fa.FATHOM_ERR_INVALID_ARG
+    assert call(staging=ctypes.c_void_p(0x1010)) == fa.FATHOM_ERR_INVALID_ARG
+    assert call(staging_bytes=2 * 128 * 4 * 32 * 4 - 1) == fa.FATHOM_ERR_WORKSPACE
+    assert call(ws_bytes=100) == fa.FATHOM_ERR_WORKSPACE
+    assert call(mode=2) == fa.FATHOM_ERR_INVALID_ARG
+    assert fa.staging_bytes(s) == 2 * 128 * 4 * 32 * 4

@@ -633,6 +633,37 @@ def test_host_resident_full_size(qwen_store, qwen_pinned, budget):
     assert np.array_equal(host(d_val), val)
 
 
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("budget,mode", [(68, 1), (92, 1), (136, 1), (92, 0)])
+def test_host_resident_staged_full_size(qwen_store, qwen_pinned, budget, mode):
+    """The host-resident config through the copy-engine staging call: each
+    head's union rows copied from pinned host memory into a two-slot HBM
+    staging area while the previous head is scanned.  Allocations bit-exact
+    with the oracle's, the top-k set of one query per KV head against the
+    oracle's full scan, every returned score checked, and the whole result
+    identical to the HBM-resident fused call's."""
+    S = qwen_store
+    w, G, n = S["w"], S["w"].group, S["w"].n
+    say("host resident staged", budget, "gather" if mode else "copy engine")
+    pinned, _ = qwen_pinned
+    alloc, idx, val = fa.allocate_scan_topk_staged(pinned, S["lo"], S["step"], S["var"], S["store"], S["qd"], G,
+                                                   budget, w.k, mode=mode)
+    alloc, idx, val = host(alloc), host(idx), host(val)
+    alloc_ref = O.allocate_all(S["q"], S["var_ref"], G, budget)
+    assert np.array_equal(alloc, alloc_ref)
+    for i in range(w.num_q):
+        l, s_, _, codes = S["heads"][i // G]
+        ref_sel = O.scores_from_codes(codes[idx[i]], l, s_, S["q"][i], alloc_ref[i])
+        assert np.all(np.abs(val[i].astype(np.float64) - ref_sel) <= TOL * np.abs(ref_sel).max()), i
+    for h in range(w.num_kv_heads):
+        i = h * G + ((h + 1) % G)
+        check_topk(idx[i], val[i], S["ref_scores"](i, alloc_ref[i]), w.k, n)
+    d_alloc, d_idx, d_val = fa.allocate_scan_topk(S["planes"], S["lo"], S["step"], S["var"], S["store"], S["qd"], G,
+                                                  budget, w.k)
+    assert np.array_equal(host(d_idx), idx)
+    assert np.array_equal(host(d_val), val)
+
+
 @pytest.fixture(scope="module")
 def multi_store():
     """The many-session store at full size (128 KV heads = 16 sessions x 8
@@ -757,6 +788,15 @@ def test_ragged_lengths_pack_scan_append(lengths, n, G, B, k):
             if lengths[h]:
                 check_scores(sc[i, :lengths[h]], s_ref)
             assert np.all(np.isnan(sc[i, lengths[h]:])), "scores past the head's length are not written"
+    # the same ragged store from pinned host memory, staged head by head
+    pinned = torch.empty(planes.shape, dtype=planes.dtype, pin_memory=True)
+    pinned.copy_(planes)
+    torch.cuda.synchronize()
+    for mode in (fa.FATHOM_STAGE_GATHER, fa.FATHOM_STAGE_COPY_ENGINE):
+        s_alloc, s_idx, s_val = fa.allocate_scan_topk_staged(pinned, lo, step, var, store, qd, G, B, k, mode=mode)
+        assert np.array_equal(host(s_alloc), alloc)
+        assert np.array_equal(host(s_idx), idx) and np.array_equal(host(s_val), val)
+    del pinned
     # appends at each head's own length
     store2 = fa.append_keys(dev(new_keys), store, planes, lo, step)
     assert np.array_equal(host(ln), np.array(lengths, np.int32) + m_app)
