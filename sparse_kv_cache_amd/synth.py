@@ -120,3 +120,21 @@ def forced_tie_keys(seed: int, n: int, d: int = D_DEFAULT) -> np.ndarray:
     keys[:, 2] = keys[:, 1]                              # duplicated channel
     keys[:, 3] = np.where(rng.random(n) < 0.5, np.float32(-1.0), np.float32(1.0))
     return keys
+
+
+def plant_aligned_keys(seed: int, keys: np.ndarray, q: np.ndarray, per_query: int, logit: float) -> np.ndarray:
+    """Give attention a peak to find: for each query row g of q [G, d],
+    overwrite `per_query` random rows of one head's keys [n, d] with keys
+    along that query's direction, scaled so that q_g . k / sqrt(d) = logit,
+    plus N(0, 0.1) noise (in place).  Distinct rows per query; returns them,
+    int64 [G, per_query].  Only synthetic-input construction: the stand-in for
+    the peaked attention of a trained model."""
+    rng = np.random.default_rng([seed, 1 << 21])
+    n, d = keys.shape
+    rows = rng.choice(n, (q.shape[0], per_query), replace=False)
+    for g in range(q.shape[0]):
+        qg = q[g].astype(np.float64)
+        direction = qg * (logit * np.sqrt(d) / float(qg @ qg))
+        noise = 0.1 * rng.standard_normal((per_query, d))
+        keys[rows[g]] = (direction[None, :] + noise).astype(np.float32)
+    return rows

@@ -445,11 +445,15 @@ def test_sparse_attention_host_rows_match_device():
 
 def test_decode_step_attention_error_below_random_selection():
     """Whole decode step (pack, fused allocate + scan + top-k, attention over
-    the selected rows): its error against dense attention over all n keys is
-    below that of attending over k random keys, for every query."""
+    the selected rows) on keys with a peak to find: 32 keys per query along
+    its direction (logit 12, so dense attention puts most of its mass on
+    them).  The relative L2 error of the selected rows' attention against
+    dense attention over all n keys is small, and far below that of
+    attending over k random keys."""
     say("decode step attention error")
     n, H, group, k, B = 131072, 1, 4, 1024, 92
     keys, q = synth.make_inputs(41, H, n, H * group)
+    planted = synth.plant_aligned_keys(41, keys[0], q, 32, 12.0)
     vals = np.stack([synth.head_values(41, 0, n)])
     planes, lo, step, var = gpu_pack(keys)
     store = fa.store_desc(H, n, 128)
@@ -464,11 +468,12 @@ def test_decode_step_attention_error_below_random_selection():
         dense = O.attention(k64[0], v64[0], q[i], 128 ** -0.5)
         ref = O.sparse_attention(k64[0], v64[0], q[i], idx[i], 128 ** -0.5)
         assert np.abs(out[i] - ref).max() <= 1e-4 * np.abs(v64[0][idx[i]]).max()
+        assert set(planted[i].tolist()) <= set(idx[i].tolist()), "the planted keys are selected"
         err = O.attention_error(out[i], dense)
         err_rand = O.attention_error(O.sparse_attention(k64[0], v64[0], q[i], rng.choice(n, k, replace=False),
                                                         128 ** -0.5), dense)
         print(f"query {i}: attention error top-{k} {err:.4f}, random {err_rand:.4f}")
-        assert err < err_rand
+        assert err < 0.2 and err < 0.2 * err_rand
 
 
 def test_host_resident_store_matches_device():

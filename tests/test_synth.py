@@ -31,3 +31,15 @@ def test_workload_table():
     w = synth.WORKLOADS["qwen3_8b_1m"]
     assert (w.num_kv_heads, w.n, w.group, w.k, w.num_q) == (8, 1 << 20, 4, 2048, 32)
     assert synth.WORKLOADS["multi_session"].num_q == 512
+
+
+def test_planted_keys_have_the_requested_logit():
+    keys, q = synth.make_inputs(5, 1, 5000, 3)
+    k = keys[0].copy()
+    rows = synth.plant_aligned_keys(5, k, q, 16, 12.0)
+    assert rows.shape == (3, 16) and len(np.unique(rows)) == 48
+    for g in range(3):
+        logits = k[rows[g]].astype(np.float64) @ q[g].astype(np.float64) / np.sqrt(128)
+        assert np.all(np.abs(logits - 12.0) < 0.1 * np.linalg.norm(q[g]) / np.sqrt(128) * 5)
+    untouched = np.setdiff1d(np.arange(5000), rows.ravel())
+    assert np.array_equal(k[untouched], keys[0][untouched])
