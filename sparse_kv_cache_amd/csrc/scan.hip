@@ -390,10 +390,13 @@ __device__ void table_limbs(const UnionLds<GQ>& s, ChunkTable& T, double (&wsum)
 // Stores the finished table T for the main kernel.  (Issued at the end of
 // the sample kernel: a barrier or stage wait after a store waits for its
 // write to complete.)
-__device__ void store_table(const ScanArgs& a, const ChunkTable& T) {
+// Every sampled-block workgroup of a chunk builds the same table; workgroup
+// `part` of `parts` stores every parts-th piece of it.
+__device__ void store_table(const ScanArgs& a, const ChunkTable& T, int part, int parts) {
   uint4* dst = reinterpret_cast<uint4*>(static_cast<char*>(a.tables) + size_t(chunk_index(a)) * kChunkTableBytes);
   const uint4* src = reinterpret_cast<const uint4*>(&T);
-  for (int i = threadIdx.x; i < static_cast<int>(sizeof(ChunkTable) / 16); i += blockDim.x) dst[i] = src[i];
+  for (int i = part * blockDim.x + threadIdx.x; i < static_cast<int>(sizeof(ChunkTable) / 16); i += parts * blockDim.x)
+    dst[i] = src[i];
 }
 
 // ----------------------------------------------------------- block select
@@ -1401,12 +1404,11 @@ __global__ __launch_bounds__(kMainThreads) void scan_sample_kernel(ScanArgs a) {
       }
     }
   });
-  // workgroup 0 of the chunk stores its table and the allocations last
-  if (blockIdx.x == 0) {
-    store_table(a, T);
-    if (a.var && wave < GQ)
-      *reinterpret_cast<uint16_t*>(a.alloc_out + int64_t(q0 + wave) * kD + 2 * lane) = s_alloc[wave][lane];
-  }
+  // the chunk's workgroups store a share of its table each, and workgroup 0
+  // the allocations, last
+  store_table(a, T, blockIdx.x, gridDim.x);
+  if (blockIdx.x == 0 && a.var && wave < GQ)
+    *reinterpret_cast<uint16_t*>(a.alloc_out + int64_t(q0 + wave) * kD + 2 * lane) = s_alloc[wave][lane];
 }
 
 // ------------------------------------------------------------------- merge

@@ -22,7 +22,7 @@ namespace {
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
 constexpr int kStageThreads = 256;
-constexpr int kStageUnroll = 4;
+constexpr int kStageUnroll = 8;
 
 __global__ __launch_bounds__(kStageThreads) void stage_union_kernel(const uint32_t* __restrict__ src_head,
                                                                     uint32_t* __restrict__ dst_head,

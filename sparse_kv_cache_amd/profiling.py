@@ -4,6 +4,8 @@ repository, and computes the measured HBM traffic of the main scan kernel.
   python -m sparse_kv_cache_amd.profiling stats  <kernel_stats.csv> --command "..."
   python -m sparse_kv_cache_amd.profiling traffic --fetch <pmc.csv> --write <pmc.csv>
          --copy-mib M --budget B --out <file.json> --command "..."
+  python -m sparse_kv_cache_amd.profiling counters <pmc.csv> [<pmc.csv> ...] --title T
+         --command "..." [--command "..."]
 
 Traffic: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are read for the main
 scan kernel and for a plain elementwise kernel that reads and writes exactly
@@ -92,6 +94,62 @@ def traffic(fetch_csv: str, write_csv: str, copy_mib: int, budget: int) -> dict:
     }
 
 
+# rocprofv3's own definitions of the derived metrics reported (its counter
+# list prints them); the other rows are raw SQ counters, summed over the
+# GPU for one dispatch.
+DERIVED = {
+    "VALUBusy": "100*SQ_ACTIVE_INST_VALU/CU_NUM/GRBM_GUI_ACTIVE",
+    "VALUUtilization": "100*SQ_THREAD_CYCLES_VALU/(SQ_ACTIVE_INST_VALU*MAX_WAVE_SIZE)",
+    "LDSBankConflict": "100*SQ_LDS_BANK_CONFLICT/GRBM_GUI_ACTIVE/CU_NUM",
+}
+
+
+def counters_markdown(paths, title: str, commands) -> str:
+    """Per-kernel mean of every counter in the pmc CSVs (one row per
+    dispatch), plus ratios computed here with their formulas."""
+    vals = {}
+    for path in paths:
+        for r in csv.DictReader(open(path)):
+            name = _short(r["Kernel_Name"])
+            if not name.startswith("scan_"):
+                continue
+            vals.setdefault(name, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    out = [f"# {title}", "", f"Source digest of the scan kernels: `{source_digest()}`", "", "Commands:", ""]
+    for c in commands:
+        out += ["```", c, "```", ""]
+    for kernel in sorted(vals):
+        cs = vals[kernel]
+        mean = {c: sum(v) / len(v) for c, v in cs.items()}
+        out += [f"## {kernel}", "", "| counter | mean per dispatch | dispatches |", "|---|---:|---:|"]
+        for c in sorted(mean):
+            out.append(f"| {c} | {mean[c]:.6g} | {len(cs[c])} |")
+        derived = []
+        if "SQ_INSTS_VALU" in mean and mean.get("SQ_INSTS_MFMA"):
+            derived.append(("VALU instructions per MFMA", "SQ_INSTS_VALU / SQ_INSTS_MFMA",
+                            mean["SQ_INSTS_VALU"] / mean["SQ_INSTS_MFMA"]))
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in mean and mean.get("SQ_BUSY_CU_CYCLES"):
+            derived.append(("MFMA busy share of CU-busy cycles", "SQ_VALU_MFMA_BUSY_CYCLES / SQ_BUSY_CU_CYCLES",
+                            mean["SQ_VALU_MFMA_BUSY_CYCLES"] / mean["SQ_BUSY_CU_CYCLES"]))
+        if "SQ_LDS_BANK_CONFLICT" in mean and mean.get("SQ_INSTS_LDS"):
+            derived.append(("bank-conflict cycles per LDS instruction", "SQ_LDS_BANK_CONFLICT / SQ_INSTS_LDS",
+                            mean["SQ_LDS_BANK_CONFLICT"] / mean["SQ_INSTS_LDS"]))
+        if "SQ_LDS_BANK_CONFLICT" in mean and mean.get("SQ_LDS_IDX_ACTIVE"):
+            derived.append(("bank-conflict share of LDS-active cycles", "SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE",
+                            mean["SQ_LDS_BANK_CONFLICT"] / mean["SQ_LDS_IDX_ACTIVE"]))
+        if "SQ_WAIT_INST_ANY" in mean and mean.get("SQ_WAVE_CYCLES"):
+            derived.append(("waiting share of wave cycles", "SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES",
+                            mean["SQ_WAIT_INST_ANY"] / mean["SQ_WAVE_CYCLES"]))
+        if derived:
+            out += ["", "| ratio | formula | value |", "|---|---|---:|"]
+            out += [f"| {a} | `{b}` | {v:.4g} |" for a, b, v in derived]
+        present = [k for k in DERIVED if k in mean]
+        if present:
+            out += ["", "Derived metrics above are rocprofv3's: " +
+                    "; ".join(f"{k} = `{DERIVED[k]}`" for k in present) + "."]
+        out.append("")
+    return "\n".join(out) + "\n"
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -105,8 +163,14 @@ def main(argv=None) -> int:
     t.add_argument("--budget", type=int, required=True)
     t.add_argument("--out", required=True)
     t.add_argument("--command", action="append", default=[])
+    c = sub.add_parser("counters")
+    c.add_argument("csv", nargs="+")
+    c.add_argument("--title", required=True)
+    c.add_argument("--command", action="append", default=[])
     a = ap.parse_args(argv)
-    if a.cmd == "stats":
+    if a.cmd == "counters":
+        sys.stdout.write(counters_markdown(a.csv, a.title, a.command))
+    elif a.cmd == "stats":
         sys.stdout.write(stats_markdown(a.csv, a.command))
     else:
         rec = traffic(a.fetch, a.write, a.copy_mib, a.budget)
