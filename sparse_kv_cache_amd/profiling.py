@@ -6,6 +6,7 @@ repository, and computes the measured HBM traffic of the main scan kernel.
          --copy-mib M --budget B --out <file.json> --command "..."
   python -m sparse_kv_cache_amd.profiling counters <pmc.csv> [<pmc.csv> ...] --title T
          --command "..." [--command "..."]
+  python -m sparse_kv_cache_amd.profiling trace <kernel_trace.csv> --last N --title T --command "..."
 
 Traffic: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are read for the main
 scan kernel and for a plain elementwise kernel that reads and writes exactly
@@ -44,7 +45,8 @@ def _short(name: str) -> str:
 
 def stats_markdown(path: str, command: str) -> str:
     rows = list(csv.DictReader(open(path)))
-    out = ["# rocprofv3 kernel statistics", "", "Command:", "", "```", command, "```", "",
+    out = ["# rocprofv3 kernel statistics", "", f"Source digest of the scan kernels: `{source_digest()}`", "",
+           "Command:", "", "```", command, "```", "",
            "| kernel | calls | avg us | min us | max us | share % |",
            "|---|---:|---:|---:|---:|---:|"]
     for r in rows:
@@ -150,6 +152,24 @@ def counters_markdown(paths, title: str, commands) -> str:
     return "\n".join(out) + "\n"
 
 
+def trace_markdown(path: str, last: int, title: str, command: str) -> str:
+    """Mean, min and max duration of the last `last` dispatches of each
+    kernel in a kernel-trace CSV (the calls of the run's final phase)."""
+    rows = list(csv.DictReader(open(path)))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    by = {}
+    for r in rows:
+        by.setdefault(_short(r["Kernel_Name"]), []).append(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    out = [f"# {title}", "", f"Source digest of the scan kernels: `{source_digest()}`", "", "Command:", "", "```",
+           command, "```", "", f"Last {last} dispatches of each kernel (kernel trace):", "",
+           "| kernel | dispatches | mean us | min us | max us |", "|---|---:|---:|---:|---:|"]
+    for name in sorted(by, key=lambda n: -sum(by[n][-last:])):
+        d = by[name][-last:]
+        out.append(f"| {name} | {len(d)} | {sum(d) / len(d):.1f} | {min(d):.1f} | {max(d):.1f} |")
+    return "\n".join(out) + "\n"
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -167,8 +187,15 @@ def main(argv=None) -> int:
     c.add_argument("csv", nargs="+")
     c.add_argument("--title", required=True)
     c.add_argument("--command", action="append", default=[])
+    tr = sub.add_parser("trace")
+    tr.add_argument("csv")
+    tr.add_argument("--last", type=int, required=True)
+    tr.add_argument("--title", required=True)
+    tr.add_argument("--command", required=True)
     a = ap.parse_args(argv)
-    if a.cmd == "counters":
+    if a.cmd == "trace":
+        sys.stdout.write(trace_markdown(a.csv, a.last, a.title, a.command))
+    elif a.cmd == "counters":
         sys.stdout.write(counters_markdown(a.csv, a.title, a.command))
     elif a.cmd == "stats":
         sys.stdout.write(stats_markdown(a.csv, a.command))
