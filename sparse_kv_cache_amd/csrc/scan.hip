@@ -991,19 +991,18 @@ struct TileScanner {
   __device__ void run(Epi&& epi) {
     int step_i = 0, slot = 0;
     for (int ti = 0, tile = first_tile; ti < ntiles; ++ti, tile += tile_stride) {
-      // Issue priority falls over the last tiles of the run (3 until four
-      // remain, then one step per tile).  The workgroups sharing a CU start
-      // together; with equal priority the oldest wins arbitration and the
-      // youngest ends up scanning alone at the end, at a fraction of the
-      // CU's throughput.  Falling priority lets the ones behind catch up, so
-      // they finish close together.
+      // Issue priority falls over the last tiles of the run (2 until two
+      // remain, then one step per tile; 3 is the main kernel's threshold
+      // selection).  The workgroups sharing a CU start together; with equal
+      // priority the oldest wins arbitration and the youngest ends up
+      // scanning alone at the end, at a fraction of the CU's throughput.
+      // Falling priority lets the ones behind catch up, so they finish close
+      // together.
       {
-        const int level = min(3, max(0, ti - (ntiles - 4)));   // uniform
-        if (level == 0) {
-          __builtin_amdgcn_s_setprio(3);
-        } else if (level == 1) {
+        const int left = ntiles - 1 - ti;   // uniform
+        if (left >= 2) {
           __builtin_amdgcn_s_setprio(2);
-        } else if (level == 2) {
+        } else if (left == 1) {
           __builtin_amdgcn_s_setprio(1);
         } else {
           __builtin_amdgcn_s_setprio(0);
@@ -1034,15 +1033,7 @@ struct TileScanner {
   }
 };
 
-template <class Epi>
-__device__ void scan_tiles(const ScanArgs& a, const ChunkTable& T, uint32_t (&ring)[kMainStages][kStageDwords], int h,
-                           int first_tile, int tile_stride, int ntiles, Epi&& epi) {
-  TileScanner sc(a, T, ring, h, first_tile, tile_stride, ntiles);
-  sc.prologue();
-  sc.run(static_cast<Epi&&>(epi));
-}
-
-// Exact limb sums t of the 16 keys of a lane's column (see scan_tiles): key
+// Exact limb sums t of the 16 keys of a lane's column (see TileScanner): key
 // 8X + e comes out scaled by 2^e (-128 for e = 7).  Unscaling limb j is a
 // shift by 8j - e, exact (the sums are multiples of 2^e), and t = l0 + 2^8 l1
 // + 2^16 l2 + 2^24 l3 is exact in wrapping int32 arithmetic because
@@ -1131,6 +1122,10 @@ __global__ __launch_bounds__(kMainThreads, kMainWgPerCu * kMainWaves / 4) void s
   const int tile_end = min(min(a.tiles, head_tiles), tile_begin + a.tiles_per_wg);
   TileScanner scanner(a, T, ring, h, tile_begin, 1, tile_end - tile_begin);
   scanner.prologue();   // the first plane loads are in flight during the selection
+  // The selection runs above the scan's priority: a workgroup that starts
+  // it after its CU's other workgroups have begun scanning would otherwise
+  // wait behind their VALU work.
+  __builtin_amdgcn_s_setprio(3);
   if (a.top_lists) {   // uniform
     if (wave < GQ) {
       const float th = ordered_to_float(
@@ -2065,6 +2060,10 @@ __global__ __launch_bounds__(kSelectThreads) void scan_merge_kernel(ScanArgs a, 
     }
   }
   const uint32_t cnt = a.count[q];
+  // (loaded with the count and consumed here: left to its use under the
+  // branch below, the load would cost a round trip of its own)
+  const float theta_q = a.theta[q];
+  asm volatile("" : : "v"(theta_q));
   unsigned kept = 0;
   bool fast = false;   // uniform
   if (list_missed(cnt, k) && rescue_slot(a, q, k, s_wave) >= 0) return;   // uniform: the rescue places it
@@ -2087,7 +2086,7 @@ __global__ __launch_bounds__(kSelectThreads) void scan_merge_kernel(ScanArgs a, 
     // The scan's filter may also pass keys just below theta; only candidates
     // scoring >= theta count, and the list is complete for the top k exactly
     // when at least k of them do.
-    const uint32_t theta_o = float_to_ordered(a.theta[q]);
+    const uint32_t theta_o = float_to_ordered(theta_q);
     uint32_t pm = 0;
 #pragma unroll
     for (int j = 0; j < PT; ++j) {
