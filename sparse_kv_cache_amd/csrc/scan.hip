@@ -134,6 +134,8 @@ struct ScanArgs {
   int qoff;           // first query of chunk 0 within its head
   int tiles;          // kTileWords-word tiles per head
   int tiles_per_wg;   // tiles handled by one main workgroup
+  int main_wgs;       // main workgroups per (head, query chunk)
+  int interleave;     // main-kernel launch order: chunks interleaved (1) or one after another (0)
   float* theta;
   uint32_t* count;
   float* sample;
@@ -203,10 +205,11 @@ static_assert(sizeof(ChunkTable) % 16 == 0, "chunk tables are copied as uint4");
 // block of zero weights
 __host__ __device__ inline int nblocks_of(int U) { return U > 0 ? (U + kBlockPlanes - 1) / kBlockPlanes : 1; }
 
-__device__ inline int chunk_index(const ScanArgs& a) {
-  const int h = blockIdx.y / a.cph;
-  return h * a.chunks_per_head + a.qoff / kQueryChunk + static_cast<int>(blockIdx.y % a.cph);
+__device__ inline int chunk_index(const ScanArgs& a, int cy) {
+  const int h = cy / a.cph;
+  return h * a.chunks_per_head + a.qoff / kQueryChunk + cy % a.cph;
 }
+__device__ inline int chunk_index(const ScanArgs& a) { return chunk_index(a, static_cast<int>(blockIdx.y)); }
 
 __device__ inline int lanes_below(uint64_t mask) {
   const int lane = threadIdx.x & 63;
@@ -1080,8 +1083,21 @@ __global__ __launch_bounds__(kMainThreads, kMainWgPerCu * kMainWaves / 4) void s
   __shared__ uint32_t wbase_s[kMainWaves][4];
   __shared__ float theta_s[4];
   __shared__ uint32_t full_s[4];   // the query's global list has overflowed (seen by this workgroup)
-  const int h = blockIdx.y / a.cph;
-  const int q0 = h * a.group + a.qoff + (blockIdx.y % a.cph) * kQueryChunk;
+  // 1-D grid over the C (head, query chunk) pairs of the launch and their
+  // a.main_wgs workgroups each: chunk cy, its workgroup cx.  Interleaved
+  // (workgroup i scans chunk i % C) with one generation of resident
+  // workgroups: each chunk's workgroups then sit in every stretch of the
+  // launch order, and the CUs' workgroup slots, filled in that order, each
+  // hold one chunk (measured on the 1M-key step: main kernel 41.2 -> 40.0
+  // us).  One chunk after another with several generations: interleaved,
+  // the 128-head shape ran 3.5 us slower (each generation then reads the
+  // same narrow band of every head's plane rows).
+  const int nchunk = static_cast<int>(gridDim.x) / a.main_wgs;
+  const int bi = static_cast<int>(blockIdx.x);
+  const int cy = a.interleave ? bi % nchunk : bi / a.main_wgs;
+  const int cx = a.interleave ? bi / nchunk : bi % a.main_wgs;
+  const int h = cy / a.cph;
+  const int q0 = h * a.group + a.qoff + (cy % a.cph) * kQueryChunk;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int lane = threadIdx.x & 63;
   // With per-block lists, wavefront g selects theta of query q0 + g itself
@@ -1099,7 +1115,7 @@ __global__ __launch_bounds__(kMainThreads, kMainWgPerCu * kMainWaves / 4) void s
     // (read unconditionally, with the table, and used only without lists)
     const float theta_in = a.theta[q0 + min(static_cast<int>(threadIdx.x) & 3, GQ - 1)];
     const uint4* src = reinterpret_cast<const uint4*>(static_cast<const char*>(a.tables) +
-                                                      size_t(chunk_index(a)) * kChunkTableBytes);
+                                                      size_t(chunk_index(a, cy)) * kChunkTableBytes);
     uint4* dst = reinterpret_cast<uint4*>(&T);
     // all of a thread's loads issue before any store (a loop would wait for
     // each load in turn); indexes past the table copy its last piece again
@@ -1118,7 +1134,7 @@ __global__ __launch_bounds__(kMainThreads, kMainWgPerCu * kMainWaves / 4) void s
   __syncthreads();
   const int64_t nh = head_length(a.lengths, h, a.n);
   const int head_tiles = static_cast<int>(((nh + 31) / 32 + kTileWords - 1) / kTileWords);
-  const int tile_begin = blockIdx.x * a.tiles_per_wg;
+  const int tile_begin = cx * a.tiles_per_wg;
   const int tile_end = min(min(a.tiles, head_tiles), tile_begin + a.tiles_per_wg);
   TileScanner scanner(a, T, ring, h, tile_begin, 1, tile_end - tile_begin);
   scanner.prologue();   // the first plane loads are in flight during the selection
@@ -1293,7 +1309,7 @@ __global__ __launch_bounds__(kMainThreads, kMainWgPerCu * kMainWaves / 4) void s
       if (b0 + i < static_cast<uint32_t>(kCandCap)) a.cand[int64_t(q0 + g) * kCandCap + b0 + i] = cbuf[wave][g][i];
   }
   // the threshold of each query, for the merge
-  if (a.top_lists && blockIdx.x == 0 && static_cast<int>(threadIdx.x) < GQ) a.theta[q0 + threadIdx.x] = theta_s[threadIdx.x];
+  if (a.top_lists && cx == 0 && static_cast<int>(threadIdx.x) < GQ) a.theta[q0 + threadIdx.x] = theta_s[threadIdx.x];
 }
 
 // ------------------------------------------------------------------ sample
@@ -2219,8 +2235,7 @@ void launch_chunk_class(const ScanArgs& a, int H, int nsb, bool sample_phase, hi
   if (sample_phase) {
     hipLaunchKernelGGL(scan_sample_kernel<GQ>, dim3(nsb, H * a.cph), dim3(kMainThreads), 0, stream, a);
   } else {
-    const int wgs = (a.tiles + a.tiles_per_wg - 1) / a.tiles_per_wg;
-    hipExtLaunchKernelGGL(scan_main_kernel<GQ>, dim3(wgs, H * a.cph), dim3(kMainThreads), 0, stream,
+    hipExtLaunchKernelGGL(scan_main_kernel<GQ>, dim3(a.main_wgs * H * a.cph), dim3(kMainThreads), 0, stream,
                           ev_start, ev_stop, 0, a);
   }
 }
@@ -2314,6 +2329,8 @@ hipError_t launch_scan_topk(const uint32_t* planes, const float* lo, const float
   const int64_t target_wgs = int64_t(a.top_lists ? 1 : 4) * 256 * kMainWgPerCu;
   a.tiles_per_wg = static_cast<int>((total_tiles + target_wgs - 1) / target_wgs);
   if (a.tiles_per_wg < 1) a.tiles_per_wg = 1;
+  a.main_wgs = (a.tiles + a.tiles_per_wg - 1) / a.tiles_per_wg;
+  a.interleave = a.top_lists;
 
   // timing events: start on the first main launch, stop on the last
   hipEvent_t ev_start = timing ? timing->start : nullptr;
