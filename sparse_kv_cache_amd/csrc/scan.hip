@@ -281,27 +281,32 @@ __device__ inline double pow2_3_minus(int b) {
 // ahead so their latency overlaps other work.
 struct UnionInputs {
   float lo, st, q[4];
+  uint32_t b4;   // the channel's plane count for query g in byte g (set before build_union)
 };
 
 // Every thread loads (threads past kD re-read channel kD - 1 and ignore it):
 // loads under a branch would be waited for inside it.
 template <int GQ>
 __device__ inline UnionInputs load_union_inputs(const ScanArgs& a, int h, int q0) {
-  UnionInputs in{0.0f, 0.0f, {0.0f, 0.0f, 0.0f, 0.0f}};
+  UnionInputs in{0.0f, 0.0f, {0.0f, 0.0f, 0.0f, 0.0f}, 0u};
   const int t = min(static_cast<int>(threadIdx.x), kD - 1);
   in.lo = a.lo[h * kD + t];
   in.st = a.step[h * kD + t];
 #pragma unroll
   for (int g = 0; g < GQ; ++g) in.q[g] = a.q[int64_t(q0 + g) * kD + t];
+  if (!a.var) {   // uniform: a given allocation (with a.var the sample kernel computes it)
+#pragma unroll
+    for (int g = 0; g < GQ; ++g) in.b4 |= static_cast<uint32_t>(a.alloc[int64_t(q0 + g) * kD + t]) << (8 * g);
+  }
   return in;
 }
 
 // Builds the union plane list of a query chunk (queries q0 .. q0+GQ-1 on one
-// KV head, channel inputs in `in`, allocation of query q0 + g at
-// ab[g * kD ..]), the per-plane weights and the score offsets C_q.
-// Needs blockDim.x >= kD; ends with __syncthreads().
+// KV head, channel inputs and planes per query in `in`), the per-plane
+// weights and the score offsets C_q.  Needs blockDim.x >= kD; ends with
+// __syncthreads().
 template <int GQ>
-__device__ void build_union(const ScanArgs& a, const UnionInputs& in, const uint8_t* ab, UnionLds<GQ>& s) {
+__device__ void build_union(const ScanArgs& a, const UnionInputs& in, UnionLds<GQ>& s) {
   const int t = threadIdx.x;
   int u = 0, bq[4] = {0, 0, 0, 0};
   float qv[4] = {0.0f, 0.0f, 0.0f, 0.0f}, st = 0.0f;
@@ -311,7 +316,7 @@ __device__ void build_union(const ScanArgs& a, const UnionInputs& in, const uint
     double cp[GQ];
 #pragma unroll
     for (int g = 0; g < GQ; ++g) {
-      bq[g] = min(static_cast<int>(ab[g * kD + t]), kPlanes);
+      bq[g] = min(static_cast<int>((in.b4 >> (8 * g)) & 255u), kPlanes);
       qv[g] = in.q[g];
       u = max(u, bq[g]);
       cp[g] = static_cast<double>(qv[g]) *
@@ -1330,8 +1335,7 @@ __global__ __launch_bounds__(kMainThreads) void scan_sample_kernel(ScanArgs a) {
   const int q0 = h * a.group + a.qoff + (blockIdx.y % a.cph) * kQueryChunk;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int lane = threadIdx.x & 63;
-  const UnionInputs in = load_union_inputs<GQ>(a, h, q0);   // in flight during the allocation
-  const uint8_t* ab = a.alloc + int64_t(q0) * kD;
+  UnionInputs in = load_union_inputs<GQ>(a, h, q0);   // in flight during the allocation
   // the main kernel's candidate counts start at 0 (on the path without
   // per-block lists the threshold kernel resets them), and so do the merge's
   // rescue counters
@@ -1349,9 +1353,17 @@ __global__ __launch_bounds__(kMainThreads) void scan_sample_kernel(ScanArgs a) {
       s_alloc[wave][lane] = pair;
     }
     __syncthreads();
-    ab = reinterpret_cast<const uint8_t*>(&s_alloc[0][0]);
+    // (read here, from the LDS array itself: through a pointer that may also
+    // name global memory they would be flat loads, each waited for alone)
+    if (threadIdx.x < kD) {
+#pragma unroll
+      for (int g = 0; g < GQ; ++g) {
+        const uint16_t pair = s_alloc[g][threadIdx.x >> 1];
+        in.b4 |= static_cast<uint32_t>((pair >> (8 * (threadIdx.x & 1))) & 255u) << (8 * g);
+      }
+    }
   }
-  build_union<GQ>(a, in, ab, s);
+  build_union<GQ>(a, in, s);
   table_rows<GQ>(s, T);
   __syncthreads();
   const int col = lane & 15;
