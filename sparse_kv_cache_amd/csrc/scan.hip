@@ -58,6 +58,7 @@
 
 #include <algorithm>
 #include <climits>
+#include <cstddef>
 #include <type_traits>
 
 #include "allocate_wave.h"
@@ -107,7 +108,7 @@ constexpr int kStageDwords = 8 * kDmaDwords;
 #ifndef WAVE_CAND
 #define WAVE_CAND 32
 #endif
-constexpr int kWaveCand = WAVE_CAND;           // candidates per (wave, query) buffered in LDS
+constexpr int kWaveCand = WAVE_CAND;           // candidates per (wave, query) buffered in LDS, at least
 // Largest sample rank served by per-block group maxima: up to half the
 // lanes, so that the rank-th largest lane maximum usually leaves at most 64
 // candidates for the sort (nearer 64 the selection falls back to a search).
@@ -136,6 +137,8 @@ struct ScanArgs {
   int tiles_per_wg;   // tiles handled by one main workgroup
   int main_wgs;       // main workgroups per (head, query chunk)
   int interleave;     // main-kernel launch order: chunks interleaved (1) or one after another (0)
+  int ramp_step;      // scan issue priority: tiles per level of its fall (see TileScanner::run)
+  int ramp_top;       //   and its start (2, or 3 where no selection runs above it)
   float* theta;
   uint32_t* count;
   float* sample;
@@ -190,14 +193,23 @@ typedef unsigned int v2u32 __attribute__((ext_vector_type(2)));
 // What the main kernel needs of a (KV head, query chunk): the union rows, the
 // MFMA A operands (int8 limbs of the fixed-point plane weights), the scales
 // and the score offsets.  Built once per call by the sample kernel.
+// Per K block: its A operand and the offsets of its 64 union rows.  Blocks
+// sit one after another behind a small header, so the blocks a union uses
+// are a prefix of the table (the main kernel keeps its candidates in the
+// space of the unused ones).
+struct TableBlock {
+  uint4 A[4][16];                            // [K slice][row 4g + limb]: 16 int8 limbs
+  uint32_t rowoff[kBlockPlanes];             // byte offset of each union row in the head (0: padding)
+};
 struct ChunkTable {
-  uint32_t rowoff[kMaxUnion + kPadPlanes];   // byte offset of each union row in the head
-  uint4 A[kMaxBlocks][4][16];                // [block][K slice][row 4g + limb]: 16 int8 limbs
   float sigma[4];                            // fixed-point scale of each query's weights
   float C[4];                                // score offsets C_q
   int U;                                     // union planes
   int pad_[3];
+  TableBlock blk[kMaxBlocks];
 };
+constexpr int kTableHeadBytes = static_cast<int>(offsetof(ChunkTable, blk));
+static_assert(kTableHeadBytes % 16 == 0 && sizeof(TableBlock) % 16 == 0, "A operands stay 16-byte aligned");
 static_assert(sizeof(ChunkTable) <= kChunkTableBytes, "chunk table fits its workspace slot");
 static_assert(sizeof(ChunkTable) % 16 == 0, "chunk tables are copied as uint4");
 
@@ -384,7 +396,7 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 template <int GQ>
 __device__ void table_rows(const UnionLds<GQ>& s, ChunkTable& T) {
   const int U = s.U;
-  for (int i = threadIdx.x; i < kMaxUnion + kPadPlanes; i += blockDim.x) T.rowoff[i] = i < U ? s.rowoff[i] : 0u;
+  for (int i = threadIdx.x; i < kMaxUnion; i += blockDim.x) T.blk[i / kBlockPlanes].rowoff[i % kBlockPlanes] = i < U ? s.rowoff[i] : 0u;
   if (threadIdx.x < 4) T.C[threadIdx.x] = static_cast<int>(threadIdx.x) < GQ ? s.C[threadIdx.x] : 0.0f;
   if (threadIdx.x == 0) T.U = U;
 }
@@ -810,7 +822,7 @@ __device__ void build_limbs(const UnionLds<GQ>& s, ChunkTable& T, double (&wsum)
     const double ws = wsum[g];
     long long v = (ws > 0.0 && p < U) ? llrint(static_cast<double>(s.w[p][g]) * (0x1p30 / ws)) : 0ll;
     const int b = p / kBlockPlanes, G = (p % kBlockPlanes) / 16, byte = p % 16;
-    uint8_t* row = reinterpret_cast<uint8_t*>(&T.A[b][G][0]);
+    uint8_t* row = reinterpret_cast<uint8_t*>(&T.blk[b].A[G][0]);
 #pragma unroll
     for (int l = 0; l < 4; ++l) {
       const long long d = ((v + 128) & 255) - 128;   // balanced digit in [-128, 127]
@@ -964,7 +976,7 @@ struct TileScanner {
     ring_lane = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&ring[0][0])) +
                 static_cast<uint32_t>((col >> 1) * kDmaDwords + 2 * G * kTileWords + wave * kWaveWords) * 4u +
                 8u * static_cast<uint32_t>(col & 1);
-    a_lane = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&T.A[0][G][col]));
+    a_lane = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&T.blk[0].A[G][col]));
   }
 
   // Plane words are read once per call: the loads carry the non-temporal
@@ -978,7 +990,7 @@ struct TileScanner {
 #pragma unroll
       for (int j = 0; j < kDmaPerWave; ++j) {
         const int q = kDmaPerWave * wave + j;
-        const uint32_t vo = T.rowoff[it_b * kBlockPlanes + q + 8 * (lane >> 3)] + dma_lane_off + woff;
+        const uint32_t vo = T.blk[it_b].rowoff[q + 8 * (lane >> 3)] + dma_lane_off + woff;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, &ring[it_slot][q * kDmaDwords], 16, vo, 0, 0, kCpolNt);
       }
       ++issued;
@@ -999,18 +1011,23 @@ struct TileScanner {
   __device__ void run(Epi&& epi) {
     int step_i = 0, slot = 0;
     for (int ti = 0, tile = first_tile; ti < ntiles; ++ti, tile += tile_stride) {
-      // Issue priority falls over the last tiles of the run (2 until two
-      // remain, then one step per tile; 3 is the main kernel's threshold
-      // selection).  The workgroups sharing a CU start together; with equal
-      // priority the oldest wins arbitration and the youngest ends up
-      // scanning alone at the end, at a fraction of the CU's throughput.
-      // Falling priority lets the ones behind catch up, so they finish close
-      // together.
+      // Issue priority falls over the last tiles of the run, one level per
+      // a.ramp_step tiles, from a.ramp_top down to 0 for the last ones.  The
+      // workgroups sharing a CU start together; with equal priority the
+      // oldest wins arbitration and the youngest ends up scanning alone at
+      // the end, at a fraction of the CU's throughput.  Falling priority
+      // lets the ones behind catch up, so they finish close together.  Steps
+      // of 2 tiles: many sessions (two generations of 8-tile runs, from 3)
+      // 71.4-73.6 against 74.2-75.1 us with steps of 1 from 2; the 1M-key
+      // list path (from 2: its selection runs at 3) 39.5-40.3 against
+      // 39.9-40.8 us with steps of 1.
       {
         const int left = ntiles - 1 - ti;   // uniform
-        if (left >= 2) {
+        if (a.ramp_top == 3 && left >= 3 * a.ramp_step) {
+          __builtin_amdgcn_s_setprio(3);
+        } else if (left >= 2 * a.ramp_step) {
           __builtin_amdgcn_s_setprio(2);
-        } else if (left == 1) {
+        } else if (left >= a.ramp_step) {
           __builtin_amdgcn_s_setprio(1);
         } else {
           __builtin_amdgcn_s_setprio(0);
@@ -1027,7 +1044,7 @@ struct TileScanner {
         issue();   // into the slot every wave has finished reading
         uint32_t x[4 * kWaveX];
         const uint32_t addr = ring_lane + static_cast<uint32_t>(slot * kStageDwords) * 4u;
-        const uint32_t a_addr = a_lane + static_cast<uint32_t>(b * 4 * 16 * 16);
+        const uint32_t a_addr = a_lane + static_cast<uint32_t>(b * sizeof(TableBlock));
         v4i A;
         read_stage(addr, a_addr, x, A);
         ++step_i;
@@ -1072,18 +1089,22 @@ __device__ __forceinline__ int64_t column_key(int tile, int wave, int col, int X
   return (int64_t(tile) * kTileWords + wave * kWaveWords) * 32 + (col >> 3) * 64 + 8 * (col & 7) + 128 * X;
 }
 
-// kMainWgPerCu workgroups share a CU's 160 KB of LDS (the small arrays fit
-// in the 512 bytes left over)
-static_assert(sizeof(ChunkTable) + sizeof(uint32_t) * kMainStages * kStageDwords + sizeof(uint2) * kMainWaves * 4 * kWaveCand +
-                      512 <= 160 * 1024 / kMainWgPerCu,
+// kMainWgPerCu workgroups share a CU's 160 KB of LDS.  Beside its ring a
+// main workgroup holds the chunk table and its candidate buffers in one
+// arena (the small arrays fit in the 512 bytes left over): the buffers take
+// what the table's blocks past the union leave, so a small union leaves
+// room for more candidates per wave and query before they spill to the
+// global list (2.7 times kWaveCand with three blocks).
+constexpr int kMainArenaBytes =
+    (160 * 1024 / kMainWgPerCu - static_cast<int>(sizeof(uint32_t)) * kMainStages * kStageDwords - 512) / 16 * 16;
+static_assert(static_cast<int>(sizeof(ChunkTable) + sizeof(uint2) * kMainWaves * 4 * kWaveCand) <= kMainArenaBytes,
               "main-kernel LDS fits kMainWgPerCu workgroups per CU");
 
 // (the second launch bound is the minimum number of wavefronts per SIMD)
 template <int GQ>
 __global__ __launch_bounds__(kMainThreads, kMainWgPerCu * kMainWaves / 4) void scan_main_kernel(ScanArgs a) {
-  __shared__ ChunkTable T;
+  __shared__ __align__(16) uint32_t arena[kMainArenaBytes / 4];   // chunk table, then candidate buffers
   __shared__ uint32_t ring[kMainStages][kStageDwords];
-  __shared__ uint2 cbuf[kMainWaves][4][kWaveCand];   // candidates per (wave, query)
   __shared__ uint32_t wkept[kMainWaves][4];
   __shared__ uint32_t wbase_s[kMainWaves][4];
   __shared__ float theta_s[4];
@@ -1101,6 +1122,7 @@ __global__ __launch_bounds__(kMainThreads, kMainWgPerCu * kMainWaves / 4) void s
   const int bi = static_cast<int>(blockIdx.x);
   const int cy = a.interleave ? bi % nchunk : bi / a.main_wgs;
   const int cx = a.interleave ? bi / nchunk : bi % a.main_wgs;
+  ChunkTable& T = *reinterpret_cast<ChunkTable*>(arena);
   const int h = cy / a.cph;
   const int q0 = h * a.group + a.qoff + (cy % a.cph) * kQueryChunk;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
@@ -1137,6 +1159,10 @@ __global__ __launch_bounds__(kMainThreads, kMainWgPerCu * kMainWaves / 4) void s
     full_s[threadIdx.x & 3] = 0u;
   }
   __syncthreads();
+  // candidate buffers: cap entries per (wave, query) behind the union's blocks
+  const int cand_pairs = (kTableHeadBytes + nblocks_of(T.U) * static_cast<int>(sizeof(TableBlock))) / 8;   // uniform
+  const uint32_t cap = static_cast<uint32_t>((kMainArenaBytes / 8 - cand_pairs) / (kMainWaves * 4));
+  uint2* cbuf = reinterpret_cast<uint2*>(arena) + cand_pairs;   // [wave][query][cap]
   const int64_t nh = head_length(a.lengths, h, a.n);
   const int head_tiles = static_cast<int>(((nh + 31) / 32 + kTileWords - 1) / kTileWords);
   const int tile_begin = cx * a.tiles_per_wg;
@@ -1150,7 +1176,7 @@ __global__ __launch_bounds__(kMainThreads, kMainWgPerCu * kMainWaves / 4) void s
   if (a.top_lists) {   // uniform
     if (wave < GQ) {
       const float th = ordered_to_float(
-          wave_rth_largest<kLv>(lv, static_cast<uint32_t>(a.rsel), reinterpret_cast<uint32_t*>(&cbuf[wave][0][0])));
+          wave_rth_largest<kLv>(lv, static_cast<uint32_t>(a.rsel), reinterpret_cast<uint32_t*>(cbuf + wave * 4 * cap)));
       if (lane == 0) theta_s[wave] = th;   // (workgroup 0 stores it at the end)
     }
     lds_barrier();
@@ -1214,7 +1240,6 @@ __global__ __launch_bounds__(kMainThreads, kMainWgPerCu * kMainWaves / 4) void s
     wc2 += t2;
     wc3 += t3;
     const uint32_t slot0 = wave_off + incl - mine;
-    const uint32_t cap = static_cast<uint32_t>(kWaveCand);
     const uint32_t spill = slot0 + mine > cap ? slot0 + mine - max(slot0, cap) : 0u;
     uint32_t gpos = 0;
     if (__ballot(spill != 0) != 0) {   // uniform
@@ -1276,7 +1301,7 @@ __global__ __launch_bounds__(kMainThreads, kMainWgPerCu * kMainWaves / 4) void s
         const uint32_t key = static_cast<uint32_t>(((i & 8) ? key1 : key0) + (i & 7));
         const uint2 e = make_uint2(__float_as_uint(sc), key);
         if (slot_c < cap) {
-          cbuf[wave][G][slot_c] = e;
+          cbuf[(wave * 4 + G) * cap + slot_c] = e;
         } else {
           if (gpos < static_cast<uint32_t>(kCandCap)) a.cand[int64_t(q0 + G) * kCandCap + gpos] = e;
           ++gpos;
@@ -1288,10 +1313,10 @@ __global__ __launch_bounds__(kMainThreads, kMainWgPerCu * kMainWaves / 4) void s
   // flush: one global atomic per query reserves the buffered candidates'
   // slots, in wave order
   if (lane == 0) {
-    wkept[wave][0] = min(wc0, static_cast<uint32_t>(kWaveCand));
-    wkept[wave][1] = min(wc1, static_cast<uint32_t>(kWaveCand));
-    wkept[wave][2] = min(wc2, static_cast<uint32_t>(kWaveCand));
-    wkept[wave][3] = min(wc3, static_cast<uint32_t>(kWaveCand));
+    wkept[wave][0] = min(wc0, cap);
+    wkept[wave][1] = min(wc1, cap);
+    wkept[wave][2] = min(wc2, cap);
+    wkept[wave][3] = min(wc3, cap);
   }
   __syncthreads();
   if (threadIdx.x < GQ) {
@@ -1311,7 +1336,7 @@ __global__ __launch_bounds__(kMainThreads, kMainWgPerCu * kMainWaves / 4) void s
   for (int g = 0; g < GQ; ++g) {
     const uint32_t kept = wkept[wave][g], b0 = wbase_s[wave][g];
     for (uint32_t i = lane; i < kept; i += 64)
-      if (b0 + i < static_cast<uint32_t>(kCandCap)) a.cand[int64_t(q0 + g) * kCandCap + b0 + i] = cbuf[wave][g][i];
+      if (b0 + i < static_cast<uint32_t>(kCandCap)) a.cand[int64_t(q0 + g) * kCandCap + b0 + i] = cbuf[(wave * 4 + g) * cap + i];
   }
   // the threshold of each query, for the merge
   if (a.top_lists && cx == 0 && static_cast<int>(threadIdx.x) < GQ) a.theta[q0 + threadIdx.x] = theta_s[threadIdx.x];
@@ -1591,13 +1616,13 @@ __device__ void load_plan(const ScanArgs& a, int q, QueryPlan& P) {
   const int U = T.U;
   if (t < U) {
     const int b = t / kBlockPlanes, G = (t % kBlockPlanes) / 16, byte = t % 16;
-    const int8_t* row = reinterpret_cast<const int8_t*>(&T.A[b][G][0]);
+    const int8_t* row = reinterpret_cast<const int8_t*>(&T.blk[b].A[G][0]);
     uint32_t v = 0;
 #pragma unroll
     for (int l = 3; l >= 0; --l) v = (v << 8) + static_cast<uint32_t>(static_cast<int32_t>(row[(4 * g + l) * 16 + byte]));
     if (v != 0u) {
       const uint32_t slot = atomicAdd(&P.np, 1u);
-      P.rowoff[slot] = T.rowoff[t];
+      P.rowoff[slot] = T.blk[b].rowoff[t % kBlockPlanes];
       P.V[slot] = static_cast<int32_t>(v);
       // (wrapping sums of one sign, exact: they stay below 2^31 in magnitude)
       atomicAdd(static_cast<int32_t>(v) < 0 ? &P.tneg : &P.tpos, v);
@@ -2335,14 +2360,20 @@ hipError_t launch_scan_topk(const uint32_t* planes, const float* lo, const float
   // of one (head, query chunk).  With per-block lists every workgroup first
   // selects theta itself, so the tiles go to one generation of resident
   // workgroups (kMainWgPerCu per CU); with theta from the threshold kernel
-  // the start is cheap and four generations of shorter runs balance better
-  // (workgroups that finish early are replaced by new ones).
+  // the start is cheap and two generations of shorter runs balance better
+  // (workgroups that finish early are replaced by new ones).  Many sessions
+  // (128 heads of 128K keys, B = 68): 71.4-73.6 us with two generations
+  // against 80.5-82.0 with four, once the candidates of a run fit in LDS
+  // (with 32 per wave and query, runs of 8 tiles spilled to the global
+  // list about once per four tiles).
   const int64_t total_tiles = chunk_count * a.tiles;
-  const int64_t target_wgs = int64_t(a.top_lists ? 1 : 4) * 256 * kMainWgPerCu;
+  const int64_t target_wgs = int64_t(a.top_lists ? 1 : 2) * 256 * kMainWgPerCu;
   a.tiles_per_wg = static_cast<int>((total_tiles + target_wgs - 1) / target_wgs);
   if (a.tiles_per_wg < 1) a.tiles_per_wg = 1;
   a.main_wgs = (a.tiles + a.tiles_per_wg - 1) / a.tiles_per_wg;
   a.interleave = a.top_lists;
+  a.ramp_step = 2;
+  a.ramp_top = a.top_lists ? 2 : 3;
 
   // timing events: start on the first main launch, stop on the last
   hipEvent_t ev_start = timing ? timing->start : nullptr;
