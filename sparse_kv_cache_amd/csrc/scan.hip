@@ -217,6 +217,33 @@ static_assert(sizeof(ChunkTable) % 16 == 0, "chunk tables are copied as uint4");
 // block of zero weights
 __host__ __device__ inline int nblocks_of(int U) { return U > 0 ? (U + kBlockPlanes - 1) / kBlockPlanes : 1; }
 
+// A union of more than one K block whose last block holds at most 32 planes
+// scans that block with K = 32 MFMAs: half the B-operand masks and half the
+// MFMA work.  Its planes then sit in the first 8 rows of each 16-row slice
+// (union plane 64b + pl at slice pl / 8, byte pl % 8), where one transpose
+// read per key segment gathers them in the K = 32 operand order; the other
+// rows are padding.
+__host__ __device__ inline bool half_last_block(int U) {
+  return U > kBlockPlanes && U - kBlockPlanes * (nblocks_of(U) - 1) <= 32;
+}
+// The union plane at table position tp (block tp / 64, slice (tp % 64) / 16,
+// byte tp % 16), or -1 for padding.
+__host__ __device__ inline int union_plane_at(int tp, int U) {
+  const int b = tp / kBlockPlanes, bp = tp % kBlockPlanes;
+  int p = tp;
+  if (half_last_block(U) && b == nblocks_of(U) - 1) {
+    if ((bp & 15) >= 8) return -1;
+    p = b * kBlockPlanes + 8 * (bp >> 4) + (bp & 15);
+  }
+  return p < U ? p : -1;
+}
+// The table position of union plane p < U (inverse of union_plane_at).
+__host__ __device__ inline int table_pos_of(int p, int U) {
+  const int b = p / kBlockPlanes, pl = p % kBlockPlanes;
+  if (half_last_block(U) && b == nblocks_of(U) - 1) return b * kBlockPlanes + 16 * (pl >> 3) + (pl & 7);
+  return p;
+}
+
 __device__ inline int chunk_index(const ScanArgs& a, int cy) {
   const int h = cy / a.cph;
   return h * a.chunks_per_head + a.qoff / kQueryChunk + cy % a.cph;
@@ -396,7 +423,10 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 template <int GQ>
 __device__ void table_rows(const UnionLds<GQ>& s, ChunkTable& T) {
   const int U = s.U;
-  for (int i = threadIdx.x; i < kMaxUnion; i += blockDim.x) T.blk[i / kBlockPlanes].rowoff[i % kBlockPlanes] = i < U ? s.rowoff[i] : 0u;
+  for (int i = threadIdx.x; i < kMaxUnion; i += blockDim.x) {
+    const int p = union_plane_at(i, U);
+    T.blk[i / kBlockPlanes].rowoff[i % kBlockPlanes] = p >= 0 ? s.rowoff[p] : 0u;
+  }
   if (threadIdx.x < 4) T.C[threadIdx.x] = static_cast<int>(threadIdx.x) < GQ ? s.C[threadIdx.x] : 0.0f;
   if (threadIdx.x == 0) T.U = U;
 }
@@ -818,10 +848,11 @@ __device__ void build_limbs(const UnionLds<GQ>& s, ChunkTable& T, double (&wsum)
   }
   lds_barrier();
   for (int i = t; i < P * 4; i += blockDim.x) {
-    const int p = i >> 2, g = i & 3;
+    const int tp = i >> 2, g = i & 3;   // table position, query
+    const int p = union_plane_at(tp, U);
     const double ws = wsum[g];
-    long long v = (ws > 0.0 && p < U) ? llrint(static_cast<double>(s.w[p][g]) * (0x1p30 / ws)) : 0ll;
-    const int b = p / kBlockPlanes, G = (p % kBlockPlanes) / 16, byte = p % 16;
+    long long v = (ws > 0.0 && p >= 0) ? llrint(static_cast<double>(s.w[p][g]) * (0x1p30 / ws)) : 0ll;
+    const int b = tp / kBlockPlanes, G = (tp % kBlockPlanes) / 16, byte = tp % 16;
     uint8_t* row = reinterpret_cast<uint8_t*>(&T.blk[b].A[G][0]);
 #pragma unroll
     for (int l = 0; l < 4; ++l) {
@@ -921,6 +952,52 @@ __device__ __forceinline__ void mfma_block(const uint32_t (&t)[4 * kWaveX], v4i 
   }
 }
 
+// A half block (see half_last_block): the first transpose read of each key
+// segment (rows 16G .. 16G + 7, union planes 8G .. 8G + 7) and the first 8
+// bytes of the slice's A operand.
+__device__ __forceinline__ void read_stage_half(uint32_t addr, uint32_t a_addr, uint32_t (&t)[2 * kWaveX],
+                                                long& A) {
+  if constexpr (kWaveX == 2) {
+    v2u r0, r2;
+    asm volatile(
+        "ds_read_b64 %2, %4\n\t"
+        "ds_read_b64_tr_b8 %0, %3\n\t"
+        "ds_read_b64_tr_b8 %1, %3 offset:16\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r0), "=&v"(r2), "=&v"(A)
+        : "v"(addr), "v"(a_addr)
+        : "memory");
+    t[0] = r0.x;
+    t[1] = r0.y;
+    t[2] = r2.x;
+    t[3] = r2.y;
+  } else {
+    v2u r0;
+    asm volatile(
+        "ds_read_b64 %1, %3\n\t"
+        "ds_read_b64_tr_b8 %0, %2\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r0), "=&v"(A)
+        : "v"(addr), "v"(a_addr)
+        : "memory");
+    t[0] = r0.x;
+    t[1] = r0.y;
+  }
+}
+
+// A half block: K = 32 MFMAs, two masked dwords per key.
+template <bool FIRST>
+__device__ __forceinline__ void mfma_half(const uint32_t (&t)[2 * kWaveX], long A, v4i (&acc)[kWaveKeys]) {
+  const v4i zero = {0, 0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < kWaveKeys; ++i) {
+    const uint32_t m = 0x01010101u << (i & 7);
+    const int X = i >> 3;
+    const long bv = static_cast<long>((static_cast<uint64_t>(t[2 * X + 1] & m) << 32) | (t[2 * X] & m));
+    acc[i] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, bv, FIRST ? zero : acc[i], 0, 0, 0);
+  }
+}
+
 // Inclusive prefix sum over the 16 lanes of a DPP row.
 __device__ __forceinline__ uint32_t row_incl_sum(uint32_t v) {
   v += dpp_u32<kDppRowShr + 1>(0u, v);
@@ -944,6 +1021,7 @@ struct TileScanner {
   uint32_t (*ring)[kStageDwords];
   int first_tile, tile_stride, ntiles;
   int nblk, wave, lane, col, G, nsteps;
+  bool half;   // the last block is a half block (uniform)
   __amdgpu_buffer_rsrc_t rsrc;
   uint32_t dma_lane_off, ring_lane, a_lane;
   int it_tile, it_b = 0, it_slot = 0, issued = 0;   // next step to load (uniform)
@@ -952,6 +1030,7 @@ struct TileScanner {
                          int first_tile_, int tile_stride_, int ntiles_)
       : a(a_), T(T_), ring(ring_), first_tile(first_tile_), tile_stride(tile_stride_), ntiles(ntiles_) {
     nblk = nblocks_of(T.U);
+    half = half_last_block(T.U);
     wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
     lane = threadIdx.x & 63;
     col = lane & 15;
@@ -1034,25 +1113,40 @@ struct TileScanner {
         }
       }
       v4i acc[kWaveKeys];
-      auto step = [&](auto first, int b) {
-        // the last steps have fewer loads behind them: wait for all
+      // the stage of step b is ready to read at (LDS byte address) addr and
+      // its A operand at a_addr; the last steps have fewer loads behind them
+      // and wait for all
+      auto next_stage = [&](int b, uint32_t& addr, uint32_t& a_addr) {
         if (step_i + kMainStages - 2 < nsteps) {
           sync_stage<kDmaPerWave * (kMainStages - 2)>();
         } else {
           sync_stage<0>();
         }
         issue();   // into the slot every wave has finished reading
-        uint32_t x[4 * kWaveX];
-        const uint32_t addr = ring_lane + static_cast<uint32_t>(slot * kStageDwords) * 4u;
-        const uint32_t a_addr = a_lane + static_cast<uint32_t>(b * sizeof(TableBlock));
-        v4i A;
-        read_stage(addr, a_addr, x, A);
+        addr = ring_lane + static_cast<uint32_t>(slot * kStageDwords) * 4u;
+        a_addr = a_lane + static_cast<uint32_t>(b * sizeof(TableBlock));
         ++step_i;
         slot = slot + 1 == kMainStages ? 0 : slot + 1;
+      };
+      auto step = [&](auto first, int b) {
+        uint32_t addr, a_addr;
+        next_stage(b, addr, a_addr);
+        uint32_t x[4 * kWaveX];
+        v4i A;
+        read_stage(addr, a_addr, x, A);
         mfma_block<decltype(first)::value>(x, A, acc);
       };
+      const int nfull = half ? nblk - 1 : nblk;   // uniform
       step(std::true_type{}, 0);   // nblk >= 1: an empty union is one block of zero weights
-      for (int b = 1; b < nblk; ++b) step(std::false_type{}, b);
+      for (int b = 1; b < nfull; ++b) step(std::false_type{}, b);
+      if (half) {   // uniform: the last block, never the first
+        uint32_t addr, a_addr;
+        next_stage(nblk - 1, addr, a_addr);
+        uint32_t x[2 * kWaveX];
+        long A;
+        read_stage_half(addr, a_addr, x, A);
+        mfma_half<false>(x, A, acc);
+      }
       epi(tile, acc);
     }
   }
@@ -1615,14 +1709,15 @@ __device__ void load_plan(const ScanArgs& a, int q, QueryPlan& P) {
   __syncthreads();
   const int U = T.U;
   if (t < U) {
-    const int b = t / kBlockPlanes, G = (t % kBlockPlanes) / 16, byte = t % 16;
+    const int tp = table_pos_of(t, U);
+    const int b = tp / kBlockPlanes, G = (tp % kBlockPlanes) / 16, byte = tp % 16;
     const int8_t* row = reinterpret_cast<const int8_t*>(&T.blk[b].A[G][0]);
     uint32_t v = 0;
 #pragma unroll
     for (int l = 3; l >= 0; --l) v = (v << 8) + static_cast<uint32_t>(static_cast<int32_t>(row[(4 * g + l) * 16 + byte]));
     if (v != 0u) {
       const uint32_t slot = atomicAdd(&P.np, 1u);
-      P.rowoff[slot] = T.blk[b].rowoff[t % kBlockPlanes];
+      P.rowoff[slot] = T.blk[b].rowoff[tp % kBlockPlanes];
       P.V[slot] = static_cast<int32_t>(v);
       // (wrapping sums of one sign, exact: they stay below 2^31 in magnitude)
       atomicAdd(static_cast<int32_t>(v) < 0 ? &P.tneg : &P.tpos, v);
