@@ -138,7 +138,6 @@ struct ScanArgs {
   int main_wgs;       // main workgroups per (head, query chunk)
   int interleave;     // main-kernel launch order: chunks interleaved (1) or one after another (0)
   int ramp_step;      // scan issue priority: tiles per level of its fall (see TileScanner::run)
-  int ramp_top;       //   and its start (2, or 3 where no selection runs above it)
   float* theta;
   uint32_t* count;
   float* sample;
@@ -1091,18 +1090,18 @@ struct TileScanner {
     int step_i = 0, slot = 0;
     for (int ti = 0, tile = first_tile; ti < ntiles; ++ti, tile += tile_stride) {
       // Issue priority falls over the last tiles of the run, one level per
-      // a.ramp_step tiles, from a.ramp_top down to 0 for the last ones.  The
+      // a.ramp_step tiles, from 3 down to 0 for the last ones.  The
       // workgroups sharing a CU start together; with equal priority the
       // oldest wins arbitration and the youngest ends up scanning alone at
       // the end, at a fraction of the CU's throughput.  Falling priority
-      // lets the ones behind catch up, so they finish close together.  Steps
-      // of 2 tiles: many sessions (two generations of 8-tile runs, from 3)
-      // 71.4-73.6 against 74.2-75.1 us with steps of 1 from 2; the 1M-key
-      // list path (from 2: its selection runs at 3) 39.5-40.3 against
-      // 39.9-40.8 us with steps of 1.
+      // lets the ones behind catch up, so they finish close together.
+      // Steps of 2 tiles from 3: many sessions (two generations of 8-tile
+      // runs) 71.4-73.6 against 74.2-75.1 us with steps of 1 from 2; the
+      // 1M-key step 39.8-40.4 against 40.0-40.9 us with steps of 2 from 2
+      // and about 0.5 us more with steps of 1 from 2.
       {
         const int left = ntiles - 1 - ti;   // uniform
-        if (a.ramp_top == 3 && left >= 3 * a.ramp_step) {
+        if (left >= 3 * a.ramp_step) {
           __builtin_amdgcn_s_setprio(3);
         } else if (left >= 2 * a.ramp_step) {
           __builtin_amdgcn_s_setprio(2);
@@ -1263,9 +1262,10 @@ __global__ __launch_bounds__(kMainThreads, kMainWgPerCu * kMainWaves / 4) void s
   const int tile_end = min(min(a.tiles, head_tiles), tile_begin + a.tiles_per_wg);
   TileScanner scanner(a, T, ring, h, tile_begin, 1, tile_end - tile_begin);
   scanner.prologue();   // the first plane loads are in flight during the selection
-  // The selection runs above the scan's priority: a workgroup that starts
+  // The selection runs at the top issue priority: a workgroup that starts
   // it after its CU's other workgroups have begun scanning would otherwise
-  // wait behind their VALU work.
+  // wait behind their VALU work (which drops below it after their first
+  // tiles).
   __builtin_amdgcn_s_setprio(3);
   if (a.top_lists) {   // uniform
     if (wave < GQ) {
@@ -2468,7 +2468,6 @@ hipError_t launch_scan_topk(const uint32_t* planes, const float* lo, const float
   a.main_wgs = (a.tiles + a.tiles_per_wg - 1) / a.tiles_per_wg;
   a.interleave = a.top_lists;
   a.ramp_step = 2;
-  a.ramp_top = a.top_lists ? 2 : 3;
 
   // timing events: start on the first main launch, stop on the last
   hipEvent_t ev_start = timing ? timing->start : nullptr;
