@@ -1303,8 +1303,14 @@ __global__ __launch_bounds__(kMainThreads, kMainWgPerCu * kMainWaves / 4) void s
     const int64_t key0 = column_key(tile, wave, col, 0);
     const int64_t key1 = kWaveX == 2 ? column_key(tile, wave, col, 1) : key0;
     auto key_of = [&](int i) { return (i < 8 ? key0 : key1) + (i & 7); };
-    const int nv0 = qvalid ? static_cast<int>(max<int64_t>(0, min<int64_t>(8, nh - key0))) : 0;
-    const int nv1 = (kWaveX == 2 && qvalid) ? static_cast<int>(max<int64_t>(0, min<int64_t>(8, nh - key1))) : 0;
+    // keys of the lane that count: only the head's last tile holds keys past
+    // its end, so the others skip the range clamps
+    uint32_t vmask = qvalid ? (1u << kWaveKeys) - 1u : 0u;
+    if ((int64_t(tile) + 1) * kTileWords * 32 > nh) {   // uniform
+      const int nv0 = static_cast<int>(max<int64_t>(0, min<int64_t>(8, nh - key0)));
+      const int nv1 = kWaveX == 2 ? static_cast<int>(max<int64_t>(0, min<int64_t>(8, nh - key1))) : 0;
+      vmask &= ((1u << nv0) - 1u) | (((1u << nv1) - 1u) << 8);
+    }
     int tv[kWaveKeys];
     limb_sums(acc, tv);
     auto t_of = [&](int i) { return (i & 7) == 7 ? -tv[i] : tv[i]; };
@@ -1313,12 +1319,12 @@ __global__ __launch_bounds__(kMainThreads, kMainWgPerCu * kMainWaves / 4) void s
     if (a.all_scores) {
 #pragma unroll
       for (int i = 0; i < kWaveKeys; ++i)
-        if ((i & 7) < (i < 8 ? nv0 : nv1)) a.all_scores[int64_t(q0 + G) * a.n + key_of(i)] = score_of(i);
+        if ((vmask >> i) & 1u) a.all_scores[int64_t(q0 + G) * a.n + key_of(i)] = score_of(i);
     }
     uint32_t bits = 0;
 #pragma unroll
     for (int i = 0; i < kWaveKeys; ++i) bits |= t_of(i) >= theta_i ? (1u << i) : 0u;
-    bits &= ((1u << nv0) - 1u) | (((1u << nv1) - 1u) << 8);
+    bits &= vmask;
     if (__ballot(bits != 0) == 0) return;   // uniform
     // Candidates go to this wave's LDS buffer of their query: a DPP row holds
     // one query (lanes 16G..16G+15) and a row prefix sum orders its lanes.
