@@ -21,8 +21,9 @@
 //                            does.  When the sample rank of the threshold is
 //                            <= 32 it keeps only per-group maxima of the
 //                            block's scores, otherwise every sampled score;
-//   2. scan_threshold_kernel only when that rank is > 32: per query, a digit
-//                            select over the sampled scores gives theta;
+//   2. scan_threshold_kernel only when that rank is > 32 or the heads have
+//                            lengths of their own: per query, a digit select
+//                            over the sampled scores gives theta;
 //   3. scan_main_kernel      every key of every head, see below.  With the
 //                            group maxima, each workgroup selects theta
 //                            itself from them while its first plane loads
@@ -47,12 +48,15 @@
 //       the LDS transpose read (ds_read_b64_tr_b8) gives each lane, per byte,
 //       one plane of eight consecutive keys, and one AND per dword with
 //       0x01010101 << e keeps key e's bit of every plane, as bit * 2^e;
-// so one MFMA gives all 4 queries' 4 limb sums of 16 keys over 64 planes; the
-// epilogue unscales the limbs by shifts and recombines them into the exact
+// so one MFMA gives all 4 queries' 4 limb sums of 16 keys over 64 planes (a
+// union's last block of at most 32 planes takes v_mfma_i32_16x16x32_i8 on
+// half the rows instead); the epilogue unscales the limbs by shifts and
+// recombines them into the exact
 // integer t = sum_p V bit, and the score is fma(float(t), sum|W| 2^-30, C_q).
 // The tables (limbs, scale, offset C_q, union rows) are built once per chunk
 // by the sample kernel.  Keys whose t can reach theta are kept in LDS lists
-// per (wavefront, query) and flushed to the global candidate list at the end.
+// per (wavefront, query), in the LDS the union's table leaves free, and
+// flushed to the global candidate list at the end.
 
 #include <hip/hip_ext.h>
 
