@@ -154,6 +154,21 @@ def test_single_head_long(budget):
     check_full(keys, q, w.group, budget, w.k)
 
 
+@pytest.mark.parametrize("k", [10, 50])
+@pytest.mark.parametrize("budget", [1, 32, 33, 64, 65, 96, 97, 128, 129, 160, 161, 224, 225])
+def test_union_block_boundaries(budget, k):
+    # One query per KV head, so the union is exactly its allocation: U = B
+    # planes.  The budgets sit on both sides of each 32- and 64-plane
+    # boundary, where the last K block switches between a full block and a
+    # half block (at most 32 planes, scanned by K = 32 MFMAs once the union
+    # has more than one block).  k = 10 takes the per-block lists, k = 50
+    # the threshold kernel.  Every score is compared with the oracle's.
+    n, H = 5000, 2
+    say("union block boundaries", budget, k)
+    keys, q = synth.make_inputs(23 + budget, H, n, H)
+    check_full(keys, q, 1, budget, k)
+
+
 @pytest.mark.parametrize("n,H,group,budget,k,pad", [
     (1, 1, 1, 92, 1, 0),
     (33, 2, 2, 17, 33, 0),
